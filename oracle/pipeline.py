@@ -1,0 +1,253 @@
+"""Oracle pipeline: the method's steps composed in the paper's order.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Everything here works
+on host numpy arrays in the logical layouts:
+
+  q [B, Hq, N, D], k / v [B, Hkv, N, D] fp32 (bf16 inputs are widened exactly)
+  k codes [B, Hkv, N, D/2] u8 (element 2t in the low nibble), k scales
+  [B, Hkv, N, D/16] u8, v codes [B, Hkv, N, D] u8, delta_s [B, Hq, N] bf16 bits.
+
+Query head h reads KV head h // (Hq / Hkv) (contiguous GQA groups).
+Source: MpFA paper page ("MpFA: Hardware-Efficient Train-Free QK4V8
+FlashAttention Kernels on Blackwell GPUs"), §4-§5; where the page is silent
+the reading taken is stated in the docstring of the step that takes it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (KV_BLOCK, P_SCALE, amax, attn_state, bf16_to_f64, channel_mean, delta_s,
+               e4m3_table, fp8_quantize, fp8_scale, merge_states, nvfp4_dequantize,
+               nvfp4_global_scale, nvfp4_quantize)
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ------------------------------------------------------------ stage one --
+def quantize_k(k, q=None, q_mean=None, smooth=True):
+    """Stage one for K (MpFA §5.1 first stage, §6 "Online quantization").
+
+    smooth: K_c = fp32(K - Kbar) with Kbar the per-(b, kv-head) channel mean;
+    Qbar is the per-(b, q-head) mean of ``q`` when given, else ``q_mean``
+    (frozen means, as in decode); delta_s[b, h, j] = bf16(Qbar[b, h] . K_c[b, h//G, j]).
+    direct: K_c = K, no means and no delta_s.
+    Then NVFP4 with a global scale from the amax of the whole K_c tensor."""
+    k = np.asarray(k, dtype=F32)
+    B, Hkv, N, D = k.shape
+    out = {}
+    if smooth:
+        k_mean = channel_mean(k)
+        if q is not None:
+            q_mean = channel_mean(np.asarray(q, dtype=F32))
+        q_mean = np.asarray(q_mean, dtype=F32)
+        kc = (k - k_mean[:, :, None, :]).astype(F32)
+        Hq = q_mean.shape[1]
+        G = Hq // Hkv
+        ds = np.empty((B, Hq, N), dtype=np.uint16)
+        for b in range(B):
+            for h in range(Hq):
+                ds[b, h] = delta_s(q_mean[b, h], kc[b, h // G])
+        out.update(k_mean=k_mean, q_mean=q_mean, delta_s=ds)
+    else:
+        kc = k
+    g = nvfp4_global_scale(amax(kc))
+    codes, sf = nvfp4_quantize(kc, g)
+    out.update(k_fp4=codes, k_sf=sf, k_gscale=np.float32(g))
+    return out
+
+
+def quantize_v(v):
+    """FP8 E4M3 with one FP32 scale per tensor (MpFA §4.2; V is not centered)."""
+    v = np.asarray(v, dtype=F32)
+    s = fp8_scale(amax(v))
+    return {"v_fp8": fp8_quantize(v, s), "v_scale": np.float32(s)}
+
+
+def quantize_q(q, q_mean=None):
+    """NVFP4 of Q_c = fp32(Q - Qbar) (direct mode: Q_c = Q), global scale from the
+    amax of the whole Q_c tensor of the call.  Returns (codes, scales, g)."""
+    q = np.asarray(q, dtype=F32)
+    qc = q if q_mean is None else (q - np.asarray(q_mean, dtype=F32)[..., None, :]).astype(F32)
+    g = nvfp4_global_scale(amax(qc))
+    codes, sf = nvfp4_quantize(qc, g)
+    return codes, sf, np.float32(g)
+
+
+def _finalize(m, l, acc, s_v, scale, lse_offset, out_f64=False):
+    o = acc * float(s_v) / (P_SCALE * l[:, None])
+    if not out_f64:
+        o = o.astype(F32)
+    lse = scale * m + np.log(l)
+    if lse_offset is not None:
+        lse = lse + lse_offset
+    return o, lse
+
+
+def _prepare(q, k, v, scale, smooth, identity, q_mean=None):
+    """Shared preparation of dequantized operands for prefill and decode.
+
+    Returns dict with qt [B,Hq,Nq,D] f64, kt / vt [B,Hkv,N,D] f64, s_v,
+    delta [B,Hq,N] f64 or None, quant_p, k_mean (smooth) for the LSE offset."""
+    q = np.asarray(q, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    v = np.asarray(v, dtype=F32)
+    B, Hq = q.shape[:2]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    prep = {}
+    if identity:
+        if smooth:
+            k_mean = channel_mean(k)
+            if q_mean is None:
+                q_mean = channel_mean(q)
+            qm = np.asarray(q_mean, dtype=F64)
+            km = k_mean.astype(F64)
+            qt = q.astype(F64) - qm[:, :, None, :]
+            kt = k.astype(F64) - km[:, :, None, :]
+            delta = np.empty((B, Hq, k.shape[2]))
+            for b in range(B):
+                for h in range(Hq):
+                    delta[b, h] = kt[b, h // G] @ qm[b, h]
+            prep.update(k_mean=k_mean, delta=delta)
+        else:
+            qt, kt = q.astype(F64), k.astype(F64)
+            prep.update(delta=None)
+        prep.update(qt=qt, kt=kt, vt=v.astype(F64), s_v=1.0, quant_p=False)
+        return prep
+    if smooth:
+        kq = quantize_k(k, q=q if q_mean is None else None, q_mean=q_mean, smooth=True)
+        qcodes, qsf, gq = quantize_q(q, kq["q_mean"])
+        prep.update(k_mean=kq["k_mean"], delta=bf16_to_f64(kq["delta_s"]))
+    else:
+        kq = quantize_k(k, smooth=False)
+        qcodes, qsf, gq = quantize_q(q, None)
+        prep.update(delta=None)
+    vq = quantize_v(v)
+    table = e4m3_table()
+    prep.update(qt=nvfp4_dequantize(qcodes, qsf, gq),
+                kt=nvfp4_dequantize(kq["k_fp4"], kq["k_sf"], kq["k_gscale"]),
+                vt=table[vq["v_fp8"]], s_v=float(vq["v_scale"]), quant_p=True, kq=kq, vq=vq,
+                q_codes=qcodes, q_sf=qsf, q_gscale=gq)
+    return prep
+
+
+def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=None, out_f64=False):
+    """Causal (or full) prefill, MpFA §5.1 second stage, for the selected rows.
+
+    rows: None (every row) or an int array [R, 3] of (b, q-head, position).
+    Returns (O [R, D] fp32, LSE [R] f64, rows) -- O = acc * s_V / (448 l), LSE in
+    natural log with the smoothing row offset scale * (Q_i . Kbar) added back."""
+    q = np.asarray(q, dtype=F32)
+    B, Hq, N, D = q.shape
+    Hkv = np.asarray(k).shape[1]
+    G = Hq // Hkv
+    prep = _prepare(q, k, v, scale, smooth, identity)
+    if rows is None:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), D), dtype=F64 if out_f64 else F32)
+    LSE = np.empty(len(rows))
+    for b in range(B):
+        for h in range(Hq):
+            sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+            if len(sel) == 0:
+                continue
+            pos = rows[sel, 2]
+            qt = prep["qt"][b, h][pos]
+            row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
+            delta = None if prep["delta"] is None else prep["delta"][b, h]
+            m, l, acc = attn_state(qt, row_pos, prep["kt"][b, h // G], prep["vt"][b, h // G], delta,
+                                   0, N, scale, prep["quant_p"])
+            off = None
+            if smooth:
+                off = scale * (q[b, h][pos].astype(F64) @ prep["k_mean"][b, h // G].astype(F64))
+            o, lse = _finalize(m, l, acc, prep["s_v"], scale, off, out_f64)
+            O[sel] = o
+            LSE[sel] = lse
+    return O, LSE, rows
+
+
+def decode_partitions(n_kv: int, num_splits: int, block: int = KV_BLOCK):
+    """KV partitions of decode (MpFA §5.3: fixed chunks of whole 128-token blocks).
+
+    Reading: chunk = block * ceil(n_kv / (block * num_splits)); partition p covers
+    [p*chunk, min((p+1)*chunk, n_kv)) and may be empty."""
+    chunk = block * -(-n_kv // (block * num_splits))
+    return [(min(p * chunk, n_kv), min((p + 1) * chunk, n_kv)) for p in range(num_splits)]
+
+
+def decode(q, k, v, q_mean, num_splits, scale, smooth=True, identity=False, out_f64=False):
+    """Split-KV decode (MpFA §5.3): one query token per (batch, q-head), every key
+    visible, per-partition online-softmax states merged by log-sum-exp.
+
+    q [B, Hq, D] or [B, Hq, 1, D]; q_mean [B, Hq, D] frozen means (smooth mode).
+    Returns (O [B, Hq, D] fp32, LSE [B, Hq] f64)."""
+    q = np.asarray(q, dtype=F32)
+    if q.ndim == 3:
+        q = q[:, :, None, :]
+    B, Hq, _, D = q.shape
+    k = np.asarray(k, dtype=F32)
+    Hkv, N = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    prep = _prepare(q, k, v, scale, smooth, identity, q_mean=q_mean if smooth else None)
+    parts = decode_partitions(N, num_splits)
+    O = np.empty((B, Hq, D), dtype=F64 if out_f64 else F32)
+    LSE = np.empty((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            qt = prep["qt"][b, h, 0:1]
+            delta = None if prep["delta"] is None else prep["delta"][b, h]
+            ms, ls, accs = [], [], []
+            for (p0, p1) in parts:
+                if p1 <= p0:
+                    ms.append(-np.inf)
+                    ls.append(0.0)
+                    accs.append(np.zeros(D))
+                    continue
+                m, l, acc = attn_state(qt, np.array([-1]), prep["kt"][b, h // G],
+                                       prep["vt"][b, h // G], delta, p0, p1, scale, prep["quant_p"])
+                ms.append(m[0])
+                ls.append(l[0])
+                accs.append(acc[0])
+            m, l, acc = merge_states(np.array([ms]), np.array([ls]), np.array([accs]), scale)
+            off = None
+            if smooth:
+                off = np.array([scale * (q[b, h, 0].astype(F64) @ prep["k_mean"][b, h // G].astype(F64))])
+            o, lse = _finalize(m, l, acc, prep["s_v"], scale, off, out_f64)
+            O[b, h] = o[0]
+            LSE[b, h] = lse[0]
+    return O, LSE
+
+
+def exact_attention(q, k, v, scale, causal=True, rows=None):
+    """FP64 softmax(scale * Q K^T + mask) V and its natural-log LSE on the
+    unquantized inputs (report-only error reference)."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    B, Hq, Nq, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    if rows is None:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(Nq), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), D))
+    LSE = np.empty(len(rows))
+    for b in range(B):
+        for h in range(Hq):
+            sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+            if len(sel) == 0:
+                continue
+            pos = rows[sel, 2]
+            s = scale * (q[b, h][pos] @ k[b, h // G].T)
+            if causal:
+                s = np.where(np.arange(N)[None, :] <= pos[:, None], s, -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            e = np.exp(s - mx)
+            den = e.sum(axis=1, keepdims=True)
+            O[sel] = (e @ v[b, h // G]) / den
+            LSE[sel] = (mx + np.log(den))[:, 0]
+    return O, LSE
