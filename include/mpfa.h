@@ -1,0 +1,188 @@
+/*
+ * mpfa.h -- C ABI of the QK4PV8 attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method: "MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels
+ * on Blackwell GPUs" (paperpeel.com page).  Q.K^T is computed from NVFP4
+ * operands (E2M1 elements, one E4M3 scale per 16 head-dim elements, one FP32
+ * scale per tensor), P.V from FP8 E4M3 operands, with an FP32 online softmax
+ * (paper section 4.1).  With smoothing, Q and K are centred on their
+ * per-head sequence means and the score correction Delta_S = Qbar . K_c is
+ * added to the score accumulator as a rank-one matrix product before the
+ * mask and the running-max update (sections 3.2, 5.1, 5.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers.  The caller owns every buffer,
+ *   the workspace included.  The library never allocates, frees or
+ *   synchronises, keeps no state between calls and retains no pointer.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   The call returns once the kernels are enqueued; device-side faults
+ *   surface at the caller's next synchronisation.
+ * - Head dimension D must be 128 (the head size of the models the paper
+ *   measures, section 7.1).
+ * - Input dtypes: MPFA_F32 or MPFA_BF16, contiguous row-major [B, H, N, D].
+ * - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ * - Every pointer must be 16-byte aligned.
+ * - Non-finite inputs violate the precondition; results are then
+ *   unspecified.
+ * - Return value: MPFA_OK (0) or a negative MPFA_ERR_* code.  Arguments are
+ *   validated on the host before anything is enqueued; an invalid call
+ *   enqueues nothing.
+ *
+ * Quantized cache layouts (produced by the two quantizers, consumed by
+ * prefill and decode):
+ *   k_fp4    uint8 [B, Hkv, N, 64]   E2M1 codes, element 2t in the low
+ *                                     nibble of byte t (bit 3 = sign)
+ *   k_sf     uint8 [B, Hkv, N, 8]    E4M3 scale code of each 16-element block
+ *   k_gscale float [1]               per-tensor FP32 scale of the K codes
+ *   v_fp8    uint8 [B, Hkv, ceil(N/32), 128, 32]  E4M3 codes of V, stored in
+ *                                     tiles of 32 tokens, head-dim major
+ *                                     inside a tile: element (t, d) sits at
+ *                                     [t/32][d][t%32]; positions t >= N of
+ *                                     the last tile hold code 0
+ *   v_scale  float [1]               per-tensor FP32 scale of the V codes
+ *   delta_s  uint16 [B, Hq, N]       bf16 bits of Delta_S (smoothing only)
+ *   q_mean   float [B, Hq, 128], k_mean float [B, Hkv, 128]
+ *
+ * The value represented by a K code is e2m1(code) * e4m3(sf) * k_gscale and
+ * by a V code e4m3(code) * v_scale.
+ */
+#ifndef MPFA_H_
+#define MPFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input / output element types. */
+#define MPFA_F32 0
+#define MPFA_BF16 1
+
+/* Status codes. */
+#define MPFA_OK 0
+#define MPFA_ERR_INVALID (-1)     /* null / misaligned pointer, bad size, Hq % Hkv != 0 ... */
+#define MPFA_ERR_UNSUPPORTED (-2) /* D != 128, unknown dtype, GQA group above the limit */
+#define MPFA_ERR_WORKSPACE (-3)   /* ws_bytes smaller than mpfa_workspace_bytes() */
+#define MPFA_ERR_LAUNCH (-4)      /* the HIP runtime rejected a kernel launch */
+
+/* Operation selectors for mpfa_workspace_bytes(). */
+#define MPFA_OP_QUANTIZE_K 0
+#define MPFA_OP_QUANTIZE_V 1
+#define MPFA_OP_PREFILL 2
+#define MPFA_OP_DECODE 3
+
+/* Largest GQA group (Hq / Hkv) the decode kernel packs into one tile. */
+#define MPFA_DECODE_MAX_GROUP 8
+
+/*
+ * Bytes of device workspace the given operation needs for these sizes
+ * (multiple of 256).  Arguments not used by an operation are ignored
+ * (Hq for MPFA_OP_QUANTIZE_V, num_splits except for MPFA_OP_DECODE).  For
+ * MPFA_OP_QUANTIZE_K pass Hq = 0 when no query tensor will be given.
+ * Returns 0 for an unknown operation or a non-positive size.
+ */
+size_t mpfa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int num_splits);
+
+/* Static, human-readable name of a status code. */
+const char* mpfa_status_string(int status);
+
+/*
+ * mpfa_quantize_k_nvfp4 -- first stage for K (paper section 5.1, "first
+ * stage"; section 6, "Online quantization").
+ *
+ * Smoothing mode (k_mean and delta_s both non-NULL):
+ *   - k_mean[b, hk, :] <- channel mean of K over the N tokens;
+ *   - if q is non-NULL: q_mean[b, h, :] <- channel mean of Q [B, Hq, N, D]
+ *     (prefill); if q is NULL, q_mean is an INPUT holding means frozen
+ *     earlier in the request (decode);
+ *   - K_c = fp32(K - k_mean);
+ *   - delta_s[b, h, t] <- bf16(fp32(sum_d q_mean[b, h, d] * K_c[b, h/G, t, d]))
+ *     with the sum in FP64 over ascending d (the per-token compensation
+ *     vector computed "with one GEMV", section 5.1).
+ * Direct mode (q_mean, k_mean, delta_s all NULL; q ignored): K_c = K.
+ * Then NVFP4 of K_c: k_gscale <- amax(|K_c|) / 2688 (1 if the amax is 0),
+ * per 16-element block an E4M3 scale code of amax_block / (6 * k_gscale) and
+ * E2M1 codes of x / (scale * k_gscale), rounding to nearest, ties to the
+ * even code, saturating, sign kept.
+ *
+ * Means are exact up to one final rounding and independent of summation
+ * order: each channel is summed in 64-bit fixed point at 2^-30 of its
+ * largest magnitude.
+ *
+ * k, q: [B, Hkv, N, 128] and [B, Hq, N, 128] in k_dtype / q_dtype.
+ * Hq: number of query heads (needed in smoothing mode; Hq % Hkv == 0).
+ * ws: mpfa_workspace_bytes(MPFA_OP_QUANTIZE_K, B, q ? Hq : 0, Hkv, N, 128, 1).
+ */
+int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
+                          const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
+                          uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_quantize_v_fp8 -- FP8 E4M3 V cache (paper section 4.2: V is neither
+ * centred nor smoothed; section 6: one byte per V element).
+ *   v_scale <- amax(|V|) / 448 (1 if the amax is 0);
+ *   v_fp8   <- E4M3 codes of V / v_scale (round to nearest even, saturating),
+ *              in the tiled layout described above.
+ * v: [B, Hkv, N, 128] in v_dtype.
+ * ws: mpfa_workspace_bytes(MPFA_OP_QUANTIZE_V, ...).
+ */
+int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp8,
+                        float* v_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_prefill -- QK4PV8 attention over a whole sequence (paper section 5.1,
+ * "second stage"; sections 5.2, 4.1).
+ *
+ * Q is centred (smoothing: Q_c = fp32(Q - q_mean)) and quantized to NVFP4 on
+ * the fly with a per-call global scale amax(|Q_c|) / 2688.  Per row i and KV
+ * block of 128 keys (ascending, skipping blocks with no visible key):
+ *   S_ij = Q~_i . K~_j + Delta_S[j]      (compensation before mask and max)
+ *   m    = running max of S; p = 2^(lambda (S - m)), lambda = scale * log2(e)
+ *   l    = alpha l + sum p               (FP32, unquantized p)
+ *   acc  = alpha acc + e4m3(448 p) . V~  (FP8 P.V, the only in-loop rounding)
+ * out_i = acc * v_scale / (448 l); lse_i = scale * m + ln l, plus
+ * scale * (Q_i . k_mean) in smoothing mode (so it estimates the LSE of the
+ * uncentred scores).
+ *
+ * Smoothing iff delta_s != NULL (then q_mean and k_mean are required).
+ * causal != 0: key j is visible to row i iff j <= i; else every key.
+ * out: [B, Hq, N, 128] in out_dtype (MPFA_BF16, the paper's output, or
+ * MPFA_F32).  lse: [B, Hq, N] float, or NULL.
+ * ws: mpfa_workspace_bytes(MPFA_OP_PREFILL, ...).
+ */
+int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                 const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                 const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
+                 void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_decode -- one query token per (batch, query head) against N_kv cached
+ * keys (paper section 5.3): the KV history is cut into num_splits contiguous
+ * partitions of whole 128-key blocks (partition length
+ * 128 * ceil(N_kv / (128 * num_splits))); each partition runs the prefill
+ * block loop from its own start with every key visible, the GQA group's
+ * query heads packed into one tile, and the partial (m, l, acc) states are
+ * merged by log-sum-exp.
+ *
+ * q: [B, Hq, 1, 128].  q_mean: the frozen per-request means (smoothing).
+ * out: [B, Hq, 128]; lse: [B, Hq] or NULL.  Hq / Hkv <= MPFA_DECODE_MAX_GROUP.
+ * ws: mpfa_workspace_bytes(MPFA_OP_DECODE, B, Hq, Hkv, N_kv, 128, num_splits).
+ */
+int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPFA_H_ */

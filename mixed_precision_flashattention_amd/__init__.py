@@ -1,0 +1,265 @@
+"""Python binding of libmpfa.so, the QK4PV8 attention library for MI355X.
+
+Argument marshalling only: every step of the method runs in the HIP kernels
+behind the C ABI declared in ``include/mpfa.h``.  torch supplies device
+memory and the current stream.  The functions named like the C entry points
+take every buffer from the caller; the short-named helpers allocate the
+outputs and workspace with torch and call them.
+
+Importing does not load the library; the first call does, and raises if
+``libmpfa.so`` has not been built (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmpfa.so")
+
+MPFA_F32 = 0
+MPFA_BF16 = 1
+MPFA_OP_QUANTIZE_K = 0
+MPFA_OP_QUANTIZE_V = 1
+MPFA_OP_PREFILL = 2
+MPFA_OP_DECODE = 3
+MPFA_DECODE_MAX_GROUP = 8
+HEAD_DIM = 128
+V_TILE = 32  # tokens per head-dim-major V tile
+
+EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
+           "mpfa_quantize_v_fp8", "mpfa_prefill", "mpfa_decode")
+
+_lib = None
+
+
+class MpfaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status} ({status_string(status)})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmpfa.so (built by ``__graft_entry__.build()``) and declare signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.mpfa_workspace_bytes.restype = sz
+    L.mpfa_workspace_bytes.argtypes = [i32] * 7
+    L.mpfa_status_string.restype = ctypes.c_char_p
+    L.mpfa_status_string.argtypes = [i32]
+    L.mpfa_quantize_k_nvfp4.restype = i32
+    L.mpfa_quantize_k_nvfp4.argtypes = [P, i32, i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P,
+                                        P, sz, P]
+    L.mpfa_quantize_v_fp8.restype = i32
+    L.mpfa_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, sz, P]
+    L.mpfa_prefill.restype = i32
+    L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
+                               P, i32, P, P, sz, P]
+    L.mpfa_decode.restype = i32
+    L.mpfa_decode.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
+                              P, i32, P, P, sz, P]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().mpfa_status_string(int(status)).decode()
+
+
+def mpfa_workspace_bytes(op: int, B: int, Hq: int, Hkv: int, N: int, D: int = HEAD_DIM,
+                         num_splits: int = 1) -> int:
+    return int(load_library().mpfa_workspace_bytes(op, B, Hq, Hkv, N, D, num_splits))
+
+
+# ----------------------------------------------------------- marshalling --
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MPFA_F32
+    if t.dtype == torch.bfloat16:
+        return MPFA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 expected")
+
+
+def _check(*tensors):
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(fn: str, status: int):
+    if status != 0:
+        raise MpfaError(fn, status)
+
+
+def mpfa_quantize_k_nvfp4(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, Hq=None,
+                          stream=None):
+    """C-ABI call: k [B, Hkv, N, 128]; q [B, Hq, N, 128] or None (then q_mean is
+    an input); direct mode when k_mean, delta_s (and q_mean) are None."""
+    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws)
+    B, Hkv, N, D = k.shape
+    if Hq is None:
+        Hq = q.shape[1] if q is not None else (q_mean.shape[1] if q_mean is not None else 0)
+    st = load_library().mpfa_quantize_k_nvfp4(
+        _ptr(k), _dtype_code(k), B, Hkv, N, D, _ptr(q), _dtype_code(q) if q is not None else 0,
+        Hq, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf), _ptr(k_gscale), _ptr(delta_s),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_quantize_k_nvfp4", st)
+
+
+def mpfa_quantize_v_fp8(v, v_fp8, v_scale, ws, stream=None):
+    _check(v, v_fp8, v_scale, ws)
+    B, Hkv, N, D = v.shape
+    st = load_library().mpfa_quantize_v_fp8(_ptr(v), _dtype_code(v), B, Hkv, N, D, _ptr(v_fp8),
+                                            _ptr(v_scale), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream))
+    _raise("mpfa_quantize_v_fp8", st)
+
+
+def mpfa_prefill(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
+                 softmax_scale, causal, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse, ws)
+    B, Hq, N, D = q.shape
+    st = load_library().mpfa_prefill(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_prefill", st)
+
+
+def mpfa_decode(q, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
+                softmax_scale, num_splits, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse, ws)
+    B, Hq = q.shape[0], q.shape[1]
+    D = q.shape[-1]
+    st = load_library().mpfa_decode(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N_kv, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        float(softmax_scale), int(num_splits), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_decode", st)
+
+
+# ------------------------------------------------------ allocating helpers --
+def _workspace(op, B, Hq, Hkv, N, num_splits, device):
+    import torch
+    n = mpfa_workspace_bytes(op, B, Hq, Hkv, N, HEAD_DIM, num_splits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
+    """Allocate and fill the NVFP4 K cache.  Returns a dict with k_fp4, k_sf,
+    k_gscale and, in smoothing mode, k_mean, q_mean and delta_s."""
+    import torch
+    B, Hkv, N, D = k.shape
+    dev = k.device
+    out = {"k_fp4": torch.empty((B, Hkv, N, D // 2), dtype=torch.uint8, device=dev),
+           "k_sf": torch.empty((B, Hkv, N, D // 16), dtype=torch.uint8, device=dev),
+           "k_gscale": torch.empty(1, dtype=torch.float32, device=dev)}
+    if smooth:
+        if Hq is None:
+            Hq = q.shape[1] if q is not None else q_mean.shape[1]
+        if q is not None:
+            q_mean = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        out.update(k_mean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev),
+                   q_mean=q_mean,
+                   delta_s=torch.empty((B, Hq, N), dtype=torch.int16, device=dev))
+        ws = _workspace(MPFA_OP_QUANTIZE_K, B, Hq if q is not None else 0, Hkv, N, 1, dev)
+        mpfa_quantize_k_nvfp4(k, q, q_mean, out["k_mean"], out["k_fp4"], out["k_sf"],
+                              out["k_gscale"], out["delta_s"], ws, Hq=Hq, stream=stream)
+    else:
+        ws = _workspace(MPFA_OP_QUANTIZE_K, B, 0, Hkv, N, 1, dev)
+        mpfa_quantize_k_nvfp4(k, None, None, None, out["k_fp4"], out["k_sf"], out["k_gscale"],
+                              None, ws, Hq=0, stream=stream)
+    return out
+
+
+def quantize_v(v, stream=None):
+    """Allocate and fill the FP8 V cache (tiled layout, see mpfa.h)."""
+    import torch
+    B, Hkv, N, D = v.shape
+    n_tiles = (N + V_TILE - 1) // V_TILE
+    out = {"v_fp8": torch.empty((B, Hkv, n_tiles, D, V_TILE), dtype=torch.uint8, device=v.device),
+           "v_scale": torch.empty(1, dtype=torch.float32, device=v.device)}
+    ws = _workspace(MPFA_OP_QUANTIZE_V, B, 0, Hkv, N, 1, v.device)
+    mpfa_quantize_v_fp8(v, out["v_fp8"], out["v_scale"], ws, stream=stream)
+    return out
+
+
+def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False, ws=None,
+            out=None, lse=None, stream=None):
+    """QK4PV8 prefill from the caches returned by quantize_k / quantize_v.
+    Smoothing iff kq holds delta_s.  Returns (out, lse or None)."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = kq["k_fp4"].shape[1]
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(MPFA_OP_PREFILL, B, Hq, Hkv, N, 1, q.device)
+    smooth = kq.get("delta_s") is not None
+    mpfa_prefill(q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
+                 kq["k_fp4"], kq["k_sf"], kq["k_gscale"], vq["v_fp8"], vq["v_scale"],
+                 kq.get("delta_s") if smooth else None, softmax_scale, causal, out,
+                 lse if with_lse else None, ws, stream=stream)
+    return out, (lse if with_lse else None)
+
+
+def decode(q, kq, vq, softmax_scale, num_splits, out_dtype=None, with_lse=False, ws=None, out=None,
+           lse=None, stream=None):
+    """Split-KV decode; q [B, Hq, 1, 128].  Returns (out [B, Hq, 128], lse or None)."""
+    import torch
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv, N = kq["k_fp4"].shape[1], kq["k_fp4"].shape[2]
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(MPFA_OP_DECODE, B, Hq, Hkv, N, num_splits, q.device)
+    smooth = kq.get("delta_s") is not None
+    mpfa_decode(q, Hkv, N, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
+                kq["k_fp4"], kq["k_sf"], kq["k_gscale"], vq["v_fp8"], vq["v_scale"],
+                kq.get("delta_s") if smooth else None, softmax_scale, num_splits, out,
+                lse if with_lse else None, ws, stream=stream)
+    return out, (lse if with_lse else None)
+
+
+def v_tiles_to_rows(v_fp8_tiled, N: int):
+    """Host-side layout helper: tiled V codes [..., T, 128, 32] -> [..., N, 128]
+    (a pure permutation of bytes, used to compare caches element by element)."""
+    x = v_fp8_tiled
+    lead = x.shape[:-3]
+    T = x.shape[-3]
+    x = x.reshape(*lead, T, HEAD_DIM, V_TILE).swapaxes(-1, -2).reshape(*lead, T * V_TILE, HEAD_DIM)
+    return x[..., :N, :]

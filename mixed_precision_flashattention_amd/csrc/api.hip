@@ -1,0 +1,274 @@
+// C ABI of the library: argument validation, workspace layout and the
+// launch order of each entry point.  Everything runs on the caller's stream;
+// nothing is allocated, freed or synchronised here.
+#include "../../include/mpfa.h"
+#include "mpfa_internal.hpp"
+
+using namespace mpfa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool dtype_ok(int t) { return t == MPFA_F32 || t == MPFA_BF16; }
+
+// Workspace layouts (byte offsets from ws).
+struct QuantKWs {
+  size_t kmax, qmax, ksum, qsum, amax, total;
+};
+inline QuantKWs quant_k_layout(int B, int Hq, int Hkv) {
+  QuantKWs w;
+  const size_t nk = (size_t)B * Hkv * kD, nq = (size_t)B * Hq * kD;
+  w.kmax = 0;
+  w.qmax = align_up(w.kmax + nk * 4);
+  w.ksum = align_up(w.qmax + nq * 4);
+  w.qsum = align_up(w.ksum + nk * 8);
+  w.amax = align_up(w.qsum + nq * 8);
+  w.total = align_up(w.amax + 4);
+  return w;
+}
+
+struct DecodeWs {
+  size_t amax, m, l, acc, total;
+};
+inline DecodeWs decode_layout(int B, int Hq, int P) {
+  DecodeWs w;
+  const size_t ns = (size_t)B * Hq * P;
+  w.amax = 0;
+  w.m = align_up(4);
+  w.l = align_up(w.m + ns * 4);
+  w.acc = align_up(w.l + ns * 4);
+  w.total = align_up(w.acc + ns * kD * 4);
+  return w;
+}
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MPFA_OK : MPFA_ERR_LAUNCH;
+}
+
+// Sizes shared by every entry point.
+inline int check_sizes(int B, int Hkv, int N, int D) {
+  if (D != kD) return MPFA_ERR_UNSUPPORTED;
+  if (B < 1 || Hkv < 1 || N < 1) return MPFA_ERR_INVALID;
+  if ((int64_t)B * Hkv > 65535) return MPFA_ERR_INVALID;
+  if ((int64_t)N * kD > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+  return MPFA_OK;
+}
+
+inline int check_heads(int Hq, int Hkv, int B) {
+  if (Hq < 1 || Hq % Hkv != 0) return MPFA_ERR_INVALID;
+  if ((int64_t)B * Hq > 65535) return MPFA_ERR_INVALID;
+  return MPFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mpfa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int num_splits) {
+  if (B < 1 || Hkv < 1 || N < 1 || D < 1) return 0;
+  switch (op) {
+    case MPFA_OP_QUANTIZE_K:
+      return quant_k_layout(B, Hq > 0 ? Hq : 0, Hkv).total;
+    case MPFA_OP_QUANTIZE_V:
+    case MPFA_OP_PREFILL:
+      return kAlign;
+    case MPFA_OP_DECODE:
+      if (num_splits < 1 || Hq < 1) return 0;
+      return decode_layout(B, Hq, num_splits).total;
+    default:
+      return 0;
+  }
+}
+
+const char* mpfa_status_string(int status) {
+  switch (status) {
+    case MPFA_OK: return "ok";
+    case MPFA_ERR_INVALID: return "invalid argument";
+    case MPFA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MPFA_ERR_WORKSPACE: return "workspace too small";
+    case MPFA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
+                          const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
+                          uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
+                          void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if (!dtype_ok(k_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!k || !k_fp4 || !k_sf || !k_gscale || !ws) return MPFA_ERR_INVALID;
+  if (!aligned16(k) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(ws))
+    return MPFA_ERR_INVALID;
+  const bool smooth = k_mean != nullptr || delta_s != nullptr;
+  if (smooth) {
+    if (!k_mean || !delta_s || !q_mean) return MPFA_ERR_INVALID;
+    if ((st = check_heads(Hq, Hkv, B))) return st;
+    if (q) {
+      if (!dtype_ok(q_dtype)) return MPFA_ERR_UNSUPPORTED;
+      if (!aligned16(q)) return MPFA_ERR_INVALID;
+    }
+    if (!aligned16(q_mean) || !aligned16(k_mean) || !aligned16(delta_s)) return MPFA_ERR_INVALID;
+  }
+  const int Hq_ws = (smooth && q) ? Hq : 0;
+  const QuantKWs L = quant_k_layout(B, Hq_ws, Hkv);
+  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  uint32_t* amax = (uint32_t*)(w + L.amax);
+  const int kb = k_dtype == MPFA_BF16;
+  launch_fill_u32((uint32_t*)w, (int64_t)(L.total / 4), 0u, s);
+  const float* kc_mean = nullptr;
+  if (smooth) {
+    launch_channel_mean(k, kb, B * Hkv, N, (uint32_t*)(w + L.kmax),
+                        (unsigned long long*)(w + L.ksum), k_mean, s);
+    if (q)
+      launch_channel_mean(q, q_dtype == MPFA_BF16, B * Hq, N, (uint32_t*)(w + L.qmax),
+                          (unsigned long long*)(w + L.qsum), q_mean, s);
+    kc_mean = k_mean;
+  }
+  launch_centered_amax(k, kb, B * Hkv, N, kc_mean, amax, s);
+  launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf, s);
+  if (smooth) launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s);
+  return launch_status();
+}
+
+int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp8,
+                        float* v_scale, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if (!dtype_ok(v_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!v || !v_fp8 || !v_scale || !ws) return MPFA_ERR_INVALID;
+  if (!aligned16(v) || !aligned16(v_fp8) || !aligned16(ws)) return MPFA_ERR_INVALID;
+  if (ws_bytes < kAlign) return MPFA_ERR_WORKSPACE;
+  if ((N + 31) / 32 > 65535 * 64) return MPFA_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = (uint32_t*)ws;
+  const int vb = v_dtype == MPFA_BF16;
+  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_centered_amax(v, vb, B * Hkv, N, nullptr, amax, s);
+  launch_quantize_v_codes(v, vb, B * Hkv, N, amax, v_scale, v_fp8, s);
+  return launch_status();
+}
+
+int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                 const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                 const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
+                 void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if ((st = check_heads(Hq, Hkv, B))) return st;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out || !ws)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_fp8) ||
+      !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
+    return MPFA_ERR_INVALID;
+  if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
+                  !aligned16(delta_s)))
+    return MPFA_ERR_INVALID;
+  if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
+  if (ws_bytes < kAlign) return MPFA_ERR_WORKSPACE;
+  const int n_qtiles = (N + 127) / 128;
+  if ((int64_t)n_qtiles * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = (uint32_t*)ws;
+  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, delta_s ? q_mean : nullptr, amax, s);
+  PrefillParams p;
+  p.q = q;
+  p.q_bf16 = q_dtype == MPFA_BF16;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.G = Hq / Hkv;
+  p.q_mean = delta_s ? q_mean : nullptr;
+  p.k_mean = delta_s ? k_mean : nullptr;
+  p.k_fp4 = k_fp4;
+  p.k_sf = k_sf;
+  p.k_gscale = k_gscale;
+  p.v_fp8 = v_fp8;
+  p.v_scale = v_scale;
+  p.delta_s = delta_s;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.out = out;
+  p.out_bf16 = out_dtype == MPFA_BF16;
+  p.lse = lse;
+  p.q_amax = amax;
+  p.n_qtiles = n_qtiles;
+  launch_prefill(p, s);
+  return launch_status();
+}
+
+int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_sizes(B, Hkv, N_kv, D);
+  if (st) return st;
+  if ((st = check_heads(Hq, Hkv, B))) return st;
+  if (Hq / Hkv > MPFA_DECODE_MAX_GROUP) return MPFA_ERR_UNSUPPORTED;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (num_splits < 1) return MPFA_ERR_INVALID;
+  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out || !ws)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_fp8) ||
+      !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
+    return MPFA_ERR_INVALID;
+  if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
+                  !aligned16(delta_s)))
+    return MPFA_ERR_INVALID;
+  if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
+  if ((int64_t)B * Hkv * num_splits > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+  const DecodeWs L = decode_layout(B, Hq, num_splits);
+  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  uint32_t* amax = (uint32_t*)(w + L.amax);
+  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
+  DecodeParams p;
+  p.q = q;
+  p.q_bf16 = q_dtype == MPFA_BF16;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N_kv;
+  p.G = Hq / Hkv;
+  p.P = num_splits;
+  const int64_t per = ((int64_t)N_kv + (int64_t)kBlk * num_splits - 1) / ((int64_t)kBlk * num_splits);
+  p.chunk = (int)(per * kBlk);
+  p.q_mean = delta_s ? q_mean : nullptr;
+  p.k_mean = delta_s ? k_mean : nullptr;
+  p.k_fp4 = k_fp4;
+  p.k_sf = k_sf;
+  p.k_gscale = k_gscale;
+  p.v_fp8 = v_fp8;
+  p.v_scale = v_scale;
+  p.delta_s = delta_s;
+  p.scale = softmax_scale;
+  p.q_amax = amax;
+  p.ws_m = (float*)(w + L.m);
+  p.ws_l = (float*)(w + L.l);
+  p.ws_acc = (float*)(w + L.acc);
+  p.out = out;
+  p.out_bf16 = out_dtype == MPFA_BF16;
+  p.lse = lse;
+  launch_decode(p, s);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,278 @@
+// Split-KV QK4PV8 decode for gfx950 (paper "MpFA: ...", section 5.3
+// "Decode-Specific Optimizations").
+//
+// One wave per (batch, KV head, partition).  The G <= 8 query heads of the
+// GQA group are packed into the M dimension of the score MFMA (S = Q~ K~^T,
+// 32 x 32 x 16 f16; only rows 0..G-1 are real), so each lane holds one key
+// and the real rows sit in 4 accumulator registers of each lane half:
+// softmax work is spent on those registers only, never on the padded rows.
+// K codes go from HBM straight into registers and are expanded to exact
+// FP16 operands there; the rank-one compensation is one bf16 MFMA step with
+// the group's Delta_S rows as the B operand.  P is rounded to E4M3, turned
+// by LDS into the head-major B operand of a 16 x 16 x 128 FP8 MFMA whose A
+// operand (V^T) is read directly from the head-dim-major V tiles.  Each
+// partition leaves (m, l, acc) in the workspace; a second kernel merges the
+// partitions by log-sum-exp.
+#include "mpfa_internal.hpp"
+
+namespace mpfa {
+
+constexpr int kQStride = 272;  // LDS row of Q~ (f16)
+constexpr int kPStride = 144;  // LDS row of P^ (128 keys + 16 bytes)
+
+__global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
+  __shared__ __align__(16) uint8_t sq[8 * kQStride];
+  __shared__ __align__(16) uint8_t sp[8 * kPStride];
+  __shared__ float salpha[8];
+
+  const int N = p.N, G = p.G, P = p.P;
+  const int part = blockIdx.x % P;
+  const int bhk = blockIdx.x / P;
+  const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
+  const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)hk * G;  // first query head of the group
+  const int p0 = part * p.chunk;
+  const int p1 = min(p0 + p.chunk, N);
+  const bool smooth = p.delta_s != nullptr;
+
+  if (p0 >= p1) {  // empty partition: neutral state
+    if (lane < G) {
+      p.ws_m[(hq0 + lane) * P + part] = -INFINITY;
+      p.ws_l[(hq0 + lane) * P + part] = 0.0f;
+    }
+    for (int i = lane; i < G * kD; i += 64)
+      p.ws_acc[((hq0 + i / kD) * P + part) * kD + (i % kD)] = 0.0f;
+    return;
+  }
+
+  const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
+  const float gK = *p.k_gscale;
+  const float gg = gQ * gK;
+  const float lam = p.scale * kLog2e * gg;
+  const float cinv = 1.0f / gg;
+  const uint32_t c_hi = bf16_rne(cinv);
+  const uint32_t c_lo = bf16_rne(cinv - __uint_as_float(c_hi << 16));
+
+  {  // NVFP4 of the group's query rows: lane -> (row g = lane / 8, block lane % 8)
+    const int g = lane >> 3, blk = lane & 7;
+    uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (g < G) {
+      float x[16];
+      load16(p.q, (hq0 + g) * kD + blk * 16, p.q_bf16, x);
+      if (smooth) {
+        const float* mu = p.q_mean + (hq0 + g) * kD + blk * 16;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = x[j] - mu[j];
+      }
+      uint32_t c[16];
+      const uint32_t sc = nvfp4_block(x, gQ, c);
+      const float s = e4m3_value_pos(sc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f16x2 v2 = {(_Float16)(e2m1_value(c[2 * j]) * s),
+                          (_Float16)(e2m1_value(c[2 * j + 1]) * s)};
+        packed[j] = __builtin_bit_cast(uint32_t, v2);
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(sq + g * kQStride + blk * 32);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  }
+  __syncthreads();
+
+  // A operand (Q~): row col (real for col < G), head-dim slots 64h + 8kc .. +7.
+  i32x4 qa[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    qa[kc] = col < 8 ? *reinterpret_cast<const i32x4*>(sq + col * kQStride + (64 * h + 8 * kc) * 2)
+                     : i32x4{0, 0, 0, 0};
+  // A operand of the rank-one step: row g < G has 1/(gQ gK) (hi part in lane
+  // half 0, lo part in half 1) in slot g; the B operand holds Delta_S[g, key]
+  // in slot g of both halves, so the step adds Delta_S / (gQ gK) to row g.
+  i32x4 dA = {0, 0, 0, 0};
+  if (smooth && col < G) {
+    const int cv = (int)((h == 0 ? c_hi : c_lo) << (16 * (col & 1)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dA[i] = ((col >> 1) == i) ? cv : 0;
+  }
+
+  const int ntiles32 = (N + 31) / 32;
+  const int64_t kvh = (int64_t)b * p.Hkv + hk;
+  const uint8_t* kbase = p.k_fp4 + kvh * N * 64;
+  const uint8_t* sbase = p.k_sf + kvh * N * 8;
+  const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * (kD * 32);
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m_run[v] = -INFINITY;
+    l_run[v] = 0.0f;
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+
+  for (int k0 = p0; k0 < p1; k0 += kBlk) {
+    // ---- scores: 4 tiles of 32 keys, lane col = key -------------------
+    f32x16 s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = k0 + 32 * t + col;
+      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0;
+      uint32_t sc = 0;
+      i32x4 dB = {0, 0, 0, 0};
+      if (key < p1) {
+        const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)key * 64 + 32 * h);
+        c0 = src[0];
+        c1 = src[1];
+        sc = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)key * 8 + 4 * h);
+        if (smooth) {
+          uint32_t dv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < G) dv[g] = p.delta_s[(hq0 + g) * N + key];
+          dB = i32x4{(int)(dv[0] | (dv[1] << 16)), (int)(dv[2] | (dv[3] << 16)),
+                     (int)(dv[4] | (dv[5] << 16)), (int)(dv[6] | (dv[7] << 16))};
+        }
+      }
+      f32x16 acc = f32x16{};
+      if (smooth) acc = mfma32_bf16(dA, dB, acc);
+      const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        uint32_t e[4];
+        expand_fp4x8(w[kc], e4m3_scale_f16x2((sc >> (8 * (kc >> 1))) & 0xFFu), e);
+        acc = mfma32_f16(qa[kc], i32x4{(int)e[0], (int)e[1], (int)e[2], (int)e[3]}, acc);
+      }
+      s[t] = acc;
+    }
+
+    // ---- softmax on rows 4h + v (v < 4), keys across the 32 lanes ------
+    float alpha[4], nb[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (k0 + 32 * t + col >= p1) s[t][v] = -INFINITY;
+        mx = fmaxf(mx, s[t][v]);
+      }
+#pragma unroll
+      for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+      const float m_new = fmaxf(m_run[v], mx);
+      alpha[v] = fast_exp2(lam * (m_run[v] - m_new));
+      nb[v] = kLog2_448 - lam * m_new;
+      m_run[v] = m_new;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; t += 2) {
+        const float e0 = fast_exp2(fmaf(s[t][v], lam, nb[v]));
+        const float e1 = fast_exp2(fmaf(s[t + 1][v], lam, nb[v]));
+        lsum += e0 + e1;
+        const uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
+        uint8_t* prow = sp + (4 * h + v) * kPStride + col;
+        prow[32 * t] = (uint8_t)(wd & 0xFFu);
+        prow[32 * (t + 1)] = (uint8_t)((wd >> 8) & 0xFFu);
+      }
+      l_run[v] = fmaf(alpha[v], l_run[v], lsum);
+    }
+    if (col == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) salpha[4 * h + v] = alpha[v];
+    }
+    __syncthreads();
+
+    // ---- O^T += V^T P^T on FP8 16x16x128 -------------------------------
+    const int n = lane & 15, kg = lane >> 4;  // query column, 32-key group
+    const i32x8 pbv = n < 8 ? *reinterpret_cast<const i32x8*>(sp + n * kPStride + 32 * kg)
+                            : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    const float a_o = n < 8 ? salpha[n] : 1.0f;
+    const int tt = k0 / 32 + kg;
+    const bool v_ok = tt < ntiles32;
+    const uint8_t* vt = vbase + (int64_t)tt * (kD * 32);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      i32x8 va = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (v_ok) va = *reinterpret_cast<const i32x8*>(vt + (16 * dt + n) * 32);
+      o[dt] = mfma16_fp8(va, pbv, o[dt] * a_o);
+    }
+    __syncthreads();
+  }
+
+  // ---- partition state -------------------------------------------------
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float l = l_run[v];
+#pragma unroll
+    for (int o2 = 16; o2 > 0; o2 >>= 1) l += __shfl_xor(l, o2);
+    const int g = 4 * h + v;
+    if (col == 0 && g < G) {
+      p.ws_m[(hq0 + g) * P + part] = m_run[v];
+      p.ws_l[(hq0 + g) * P + part] = l;
+    }
+  }
+  const int n = lane & 15, kg = lane >> 4;
+  if (n < G) {
+    float* dst = p.ws_acc + ((hq0 + n) * P + part) * kD + 4 * kg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  }
+}
+
+// Log-sum-exp merge of the partitions (paper section 5.3): one block of 128
+// threads (one per channel) per (batch, query head).
+__global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
+  __shared__ float red[128];
+  const int bhq = blockIdx.x;
+  const int d = threadIdx.x;
+  const int P = p.P;
+  const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
+  const float gK = *p.k_gscale;
+  const float lam = p.scale * kLog2e * gQ * gK;
+  const float* wm = p.ws_m + (int64_t)bhq * P;
+  const float* wl = p.ws_l + (int64_t)bhq * P;
+  const float* wa = p.ws_acc + (int64_t)bhq * P * kD;
+  float m = -INFINITY;
+  for (int i = 0; i < P; ++i) m = fmaxf(m, wm[i]);
+  float l = 0.0f, acc = 0.0f;
+  for (int i = 0; i < P; ++i) {
+    const float mi = wm[i];
+    if (mi == -INFINITY) continue;
+    const float w = fast_exp2(lam * (mi - m));
+    l = fmaf(w, wl[i], l);
+    acc = fmaf(w, wa[(int64_t)i * kD + d], acc);
+  }
+  const float o = acc * (*p.v_scale / l);
+  if (p.out_bf16)
+    reinterpret_cast<uint16_t*>(p.out)[(int64_t)bhq * kD + d] = (uint16_t)bf16_rne(o);
+  else
+    reinterpret_cast<float*>(p.out)[(int64_t)bhq * kD + d] = o;
+  if (p.lse) {
+    float off = 0.0f;
+    if (p.delta_s) {
+      const int b = bhq / p.Hq, hk = (bhq % p.Hq) / p.G;
+      red[d] = load_elem(p.q, (int64_t)bhq * kD + d, p.q_bf16) *
+               p.k_mean[((int64_t)b * p.Hkv + hk) * kD + d];
+      __syncthreads();
+      for (int s = 64; s > 0; s >>= 1) {
+        if (d < s) red[d] += red[d + s];
+        __syncthreads();
+      }
+      off = p.scale * red[0];
+    }
+    if (d == 0) p.lse[bhq] = kLn2 * (lam * m + log2f(l)) - kLn2 * kLog2_448 + off;
+  }
+}
+
+void launch_decode(const DecodeParams& p, hipStream_t st) {
+  const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.P);
+  hipLaunchKernelGGL(k_decode_split, dim3(grid), dim3(64), 0, st, p);
+  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(p.B * p.Hq)), dim3(128), 0, st, p);
+}
+
+}  // namespace mpfa

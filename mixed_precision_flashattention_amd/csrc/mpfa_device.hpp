@@ -1,0 +1,205 @@
+// Device helpers of the QK4PV8 kernels for gfx950: number-format codecs,
+// FP4 -> FP16 operand expansion, MFMA wrappers and small wave utilities.
+//
+// Formats (paper "MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention
+// Kernels on Blackwell GPUs", section 4.1 and section 6 "Online
+// quantization"): NVFP4 = E2M1 elements with one E4M3 scale per 16 elements
+// plus an FP32 per-tensor scale; FP8 = OCP E4M3 ("FN": bias 7, largest
+// finite 448, no infinities).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpfa {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kBlk = 128;      // keys per online-softmax block
+constexpr float kNvfp4Range = 2688.0f;  // 6 * 448: largest E2M1 x E4M3 product
+constexpr float kE4M3Max = 448.0f;
+constexpr float kLog2_448 = 8.807354922057604f;  // log2(448)
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------- loading ----
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int is_bf16) {
+  if (is_bf16) {
+    uint32_t h = reinterpret_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(h << 16);
+  }
+  return reinterpret_cast<const float*>(p)[i];
+}
+
+// 16 consecutive elements (16-element aligned) of an fp32 or bf16 tensor.
+__device__ __forceinline__ void load16(const void* p, int64_t i, int is_bf16, float* x) {
+  if (is_bf16) {
+    const uint4* s = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    uint4 a = s[0], b = s[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 v = s[j];
+      x[4 * j] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- codecs --
+// E2M1 code of x: nearest of the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6},
+// ties to the even code, saturating at 6, sign bit (bit 3) copied from x so
+// that -0 and negatives rounding to zero keep their sign.  The comparisons
+// against the midpoints encode the tie rule directly (">" where the lower
+// code is even, ">=" where the upper one is).
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  const float a = fabsf(x);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// Value of an E2M1 code (4 bits).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float v = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+  return (c & 8u) ? -v : v;
+}
+
+// E4M3 code of a magnitude a >= 0 (finite): round to nearest, ties to the
+// even code, saturate at 448 (code 0x7E); never the NaN code.
+__device__ __forceinline__ uint32_t e4m3_encode_mag(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9; rint rounds half to even
+    return (uint32_t)__builtin_rintf(a * 512.0f);  // 8 -> code 0x08 = 2^-6
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits, half to even
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  return e4m3_encode_mag(fabsf(x)) | ((__float_as_uint(x) >> 24) & 0x80u);
+}
+
+// Value of a non-negative E4M3 code below 0x7F.
+__device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// bf16 bits of a finite fp32, round to nearest even.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// NVFP4 global scale from a tensor amax (the reading: amax / (6 * 448)).
+__device__ __forceinline__ float nvfp4_global_scale(float amax) {
+  return amax > 0.0f ? amax / kNvfp4Range : 1.0f;
+}
+
+// Quantize one 16-element block with global scale g: returns the E4M3 scale
+// code and writes the 16 E2M1 codes (one per entry, low 4 bits).
+__device__ __forceinline__ uint32_t nvfp4_block(const float* x, float g, uint32_t* codes) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ab = fmaxf(ab, fabsf(x[j]));
+  const float six_g = 6.0f * g;
+  const uint32_t sc = e4m3_encode_mag(ab / six_g);
+  const float s = e4m3_value_pos(sc);
+  const float sg = s * g;
+  const bool zero = (s == 0.0f) || (sg == 0.0f);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    codes[j] = zero ? ((__float_as_uint(x[j]) >> 28) & 8u) : e2m1_encode(x[j] / sg);
+  return sc;
+}
+
+// ------------------------------------------------ FP4 -> FP16 expansion --
+// Expand the 8 E2M1 codes of one 32-bit word (element 2t in the low nibble
+// of byte t) into 8 FP16 values code_value * s, packed two per word in
+// element order.  Every product of an E2M1 magnitude and an E4M3 scale has
+// at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
+// FP16 and the MFMA sees exactly the dequantized operand (up to the global
+// scale, which is applied in the exponent).
+//
+// FP16 bits of the E2M1 magnitudes have a zero low byte; the high byte is
+// looked up with v_perm_b32 (an 8-entry byte table), the sign bit moved in.
+__device__ __forceinline__ void expand_fp4x8(uint32_t w, f16x2 s2, uint32_t* out) {
+  const uint32_t lut_lo = 0x3E3C3800u;  // idx 0..3 -> 0x00 0x38 0x3C 0x3E
+  const uint32_t lut_hi = 0x46444240u;  // idx 4..7 -> 0x40 0x42 0x44 0x46
+  const uint32_t sel_e = w & 0x07070707u;
+  const uint32_t sel_o = (w >> 4) & 0x07070707u;
+  const uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_e) | ((w & 0x08080808u) << 4);
+  const uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_o) | (w & 0x80808080u);
+  const uint32_t p0 = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
+  const uint32_t p1 = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
+  const uint32_t p2 = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
+  const uint32_t p3 = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p0) * s2);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p1) * s2);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p2) * s2);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p3) * s2);
+}
+
+__device__ __forceinline__ f16x2 e4m3_scale_f16x2(uint32_t code) {
+  const _Float16 h = (_Float16)e4m3_value_pos(code & 0x7Fu);
+  return f16x2{h, h};
+}
+
+// ------------------------------------------------------------------ MFMA --
+__device__ __forceinline__ f32x16 mfma32_f16(const i32x4& a, const i32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const i32x4& a, const i32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// FP8 E4M3 x FP8 E4M3, 32x32x64, unit block scales (E8M0 127 = 1.0).
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// FP8 E4M3 x FP8 E4M3, 16x16x128, unit block scales.
+__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Two fp32 -> two E4M3 bytes into the low (HI = false) or high half of `old`
+// (hardware conversion, round to nearest even).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ atomics -----
+// Non-negative floats order like their bit patterns.
+__device__ __forceinline__ void atomic_max_nonneg(uint32_t* p, float v) {
+  atomicMax(p, __float_as_uint(v));
+}
+
+}  // namespace mpfa

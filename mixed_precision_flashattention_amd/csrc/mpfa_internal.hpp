@@ -1,0 +1,71 @@
+// Internal declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include "mpfa_device.hpp"
+
+namespace mpfa {
+
+struct PrefillParams {
+  const void* q;
+  int q_bf16;
+  int B, Hq, Hkv, N, G;
+  const float* q_mean;  // smoothing only
+  const float* k_mean;  // smoothing only (LSE offset)
+  const uint8_t* k_fp4;
+  const uint8_t* k_sf;
+  const float* k_gscale;
+  const uint8_t* v_fp8;
+  const float* v_scale;
+  const uint16_t* delta_s;  // NULL: direct mode
+  float scale;
+  int causal;
+  void* out;
+  int out_bf16;
+  float* lse;
+  const uint32_t* q_amax;  // amax of Q_c, computed by the pre-pass
+  int n_qtiles;
+};
+
+struct DecodeParams {
+  const void* q;
+  int q_bf16;
+  int B, Hq, Hkv, N, G, P, chunk;
+  const float* q_mean;
+  const float* k_mean;
+  const uint8_t* k_fp4;
+  const uint8_t* k_sf;
+  const float* k_gscale;
+  const uint8_t* v_fp8;
+  const float* v_scale;
+  const uint16_t* delta_s;
+  float scale;
+  const uint32_t* q_amax;
+  float* ws_m;    // [B*Hq, P]
+  float* ws_l;    // [B*Hq, P]
+  float* ws_acc;  // [B*Hq, P, 128]
+  void* out;
+  int out_bf16;
+  float* lse;
+};
+
+// quant.hip
+void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
+                         unsigned long long* sums, float* mean, hipStream_t st);
+void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
+                          uint32_t* out, hipStream_t st);
+void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
+                             const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
+                             hipStream_t st);
+void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
+                    const float* q_mean, uint16_t* delta, hipStream_t st);
+void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
+                             float* vscale, uint8_t* out, hipStream_t st);
+
+// prefill.hip
+void launch_prefill(const PrefillParams& p, hipStream_t st);
+
+// decode.hip
+void launch_decode(const DecodeParams& p, hipStream_t st);
+
+}  // namespace mpfa

@@ -1,0 +1,54 @@
+"""Helpers shared by the GPU parity tests (marshalling and comparison only)."""
+import numpy as np
+
+ATOL = 2e-3  # attention output tolerance (max-abs) against the oracle
+RTOL = 1e-2  # and relative part: |gpu - oracle| <= ATOL + RTOL * |oracle|
+LSE_ATOL = 2e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev(x, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t.to(dtype) if dtype is not None else t
+
+
+def host(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    if t.dtype == torch.int16:
+        return t.cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def assert_close(name, got, ref, atol=ATOL, rtol=RTOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite GPU values"
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    say(f"  {name}: max_abs={err.max():.3e} max_rel(|ref|>1e-3)="
+        f"{rel[np.abs(ref) > 1e-3].max() if (np.abs(ref) > 1e-3).any() else 0:.3e} "
+        f"violations={int(bad.sum())}/{bad.size}")
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())} elements out of tolerance; worst at {i}: "
+                             f"gpu={got[i]!r} oracle={ref[i]!r}")
+
+
+def assert_bytes_equal(name, got, ref):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    diff = got != ref
+    say(f"  {name}: {int(diff.sum())} mismatches of {diff.size}")
+    if diff.any():
+        i = np.argwhere(diff)[0]
+        raise AssertionError(f"{name}: {int(diff.sum())} mismatches; first at {tuple(i)}: "
+                             f"gpu={got[tuple(i)]!r} oracle={ref[tuple(i)]!r}")

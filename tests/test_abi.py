@@ -1,0 +1,153 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/mpfa.h declares, sizes workspaces, and rejects invalid arguments
+before launching anything (every call here fails validation, so no HIP
+work is ever enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpfa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpfa_\w+)\s*\(", text)))
+
+
+def header_define(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mixed_precision_flashattention_amd as mpfa
+    if not os.path.exists(mpfa.LIB_PATH):
+        from mixed_precision_flashattention_amd import _build
+        _build.build()
+    return mpfa.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    fns = header_functions()
+    for name in ("mpfa_quantize_k_nvfp4", "mpfa_quantize_v_fp8", "mpfa_prefill", "mpfa_decode",
+                 "mpfa_workspace_bytes", "mpfa_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import mixed_precision_flashattention_amd as mpfa
+    out = subprocess.run(["nm", "-D", "--defined-only", mpfa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(mpfa_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert set(mpfa.EXPORTS) == set(header_functions())
+
+
+def test_constants_match_header():
+    import mixed_precision_flashattention_amd as mpfa
+    for name in ("MPFA_F32", "MPFA_BF16", "MPFA_OP_QUANTIZE_K", "MPFA_OP_QUANTIZE_V",
+                 "MPFA_OP_PREFILL", "MPFA_OP_DECODE", "MPFA_DECODE_MAX_GROUP"):
+        assert getattr(mpfa, name) == header_define(name), name
+
+
+def test_status_strings(lib):
+    assert lib.mpfa_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert lib.mpfa_status_string(code) != b"unknown status"
+    assert lib.mpfa_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    ws = lib.mpfa_workspace_bytes
+    # decode: amax slot + m, l [B*Hq*P] + acc [B*Hq*P*128] floats, 256-aligned
+    B, Hq, Hkv, N, P = 16, 32, 8, 131072, 32
+    n = ws(3, B, Hq, Hkv, N, 128, P)
+    assert n % 256 == 0
+    assert n >= B * Hq * P * (2 + 128) * 4
+    assert n < B * Hq * P * (2 + 128) * 4 + 4 * 256
+    # quantize_k with a query tensor needs the query statistics too
+    assert ws(0, 1, 32, 8, 1024, 128, 1) > ws(0, 1, 0, 8, 1024, 128, 1)
+    assert ws(1, 1, 0, 8, 1024, 128, 1) == 256
+    assert ws(2, 1, 32, 8, 1024, 128, 1) == 256
+    assert ws(9, 1, 32, 8, 1024, 128, 1) == 0
+    assert ws(3, 1, 32, 8, 1024, 128, 0) == 0
+    assert ws(0, 0, 32, 8, 1024, 128, 1) == 0
+
+
+class _Fake:
+    """16-byte aligned host buffers standing in for device pointers: every call
+    below fails validation before anything would dereference them."""
+
+    def __init__(self):
+        self.buf = ctypes.create_string_buffer(4096 + 16)
+        base = ctypes.addressof(self.buf)
+        self.p = ctypes.c_void_p((base + 15) // 16 * 16)
+        self.mis = ctypes.c_void_p(self.p.value + 4)
+
+
+def _prefill(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, causal=1,
+             out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256, stream=None)
+    a.update(kw)
+    return lib.mpfa_prefill(*a.values())
+
+
+def _decode(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, splits=2,
+             out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.mpfa_decode(*a.values())
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP, WS = -1, -2, -3
+    assert _prefill(lib, f, D=64) == UNSUP
+    assert _prefill(lib, f, q_dtype=5) == UNSUP
+    assert _prefill(lib, f, out_dtype=2) == UNSUP
+    assert _prefill(lib, f, Hq=3) == INVALID  # Hq % Hkv != 0
+    assert _prefill(lib, f, N=0) == INVALID
+    assert _prefill(lib, f, B=0) == INVALID
+    assert _prefill(lib, f, q=None) == INVALID
+    assert _prefill(lib, f, k_fp4=f.mis) == INVALID
+    assert _prefill(lib, f, q_mean=None) == INVALID  # smoothing needs the means
+    assert _prefill(lib, f, scale=0.0) == INVALID
+    assert _prefill(lib, f, scale=float("nan")) == INVALID
+    assert _prefill(lib, f, ws_bytes=16) == WS
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP, WS = -1, -2, -3
+    assert _decode(lib, f, Hq=18) == UNSUP  # group of 9 query heads
+    assert _decode(lib, f, splits=0) == INVALID
+    assert _decode(lib, f, Hq=4, Hkv=3) == INVALID
+    assert _decode(lib, f, ws_bytes=256) == WS
+    assert _decode(lib, f, out=None) == INVALID
+    assert _decode(lib, f, D=256) == UNSUP
+
+
+def test_quantizers_reject_bad_arguments(lib):
+    f = _Fake()
+    qk = lib.mpfa_quantize_k_nvfp4
+    # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, ws_bytes, stream)
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -2
+    assert qk(f.mis, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 8, None) == -3
+    qv = lib.mpfa_quantize_v_fp8
+    assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, 256, None) == -2
+    assert qv(f.p, 1, 1, 2, 64, 128, None, f.p, f.p, 256, None) == -1
+    assert qv(f.p, 1, 1, 2, 64, 128, f.p, f.p, f.p, 8, None) == -3

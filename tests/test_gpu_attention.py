@@ -1,0 +1,115 @@
+"""GPU parity of QK4PV8 prefill and split-KV decode against the oracle, element
+by element: |gpu - oracle| <= 2e-3 + 1e-2 |oracle| on the FP32 output, LSE
+within 2e-3.  Sizes span several tiles and ragged tails."""
+import numpy as np
+import pytest
+
+from gpu_util import LSE_ATOL, assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mpfa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_precision_flashattention_amd as m
+    m.load_library()
+    return m
+
+
+def _run_prefill(mpfa, q, k, v, scale, causal, smooth, in_dtype, out_dtype, with_lse=True):
+    import torch
+    qd, kd, vd = dev(q, in_dtype), dev(k, in_dtype), dev(v, in_dtype)
+    if smooth:
+        kq = mpfa.quantize_k(kd, q=qd)
+    else:
+        kq = mpfa.quantize_k(kd, smooth=False)
+    vq = mpfa.quantize_v(vd)
+    out, lse = mpfa.prefill(qd, kq, vq, scale, causal=causal, out_dtype=out_dtype, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return host(out), (host(lse) if with_lse else None)
+
+
+def _check_prefill(mpfa, oracle_mod, cfg, causal=True, smooth=True, out_bf16=False):
+    import torch
+    in_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out_dtype = torch.bfloat16 if out_bf16 else torch.float32
+    q, k, v = (__import__("mixed_precision_flashattention_amd.synth", fromlist=["full"]).full(cfg, t)
+               for t in ("q", "k", "v"))
+    say(f"case: prefill B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} {cfg.dtype} causal={causal} "
+        f"smooth={smooth} out={'bf16' if out_bf16 else 'f32'}")
+    out, lse = _run_prefill(mpfa, q, k, v, cfg.scale, causal, smooth, in_dtype, out_dtype)
+    O, LSE, rows = oracle_mod.prefill_rows(q, k, v, cfg.scale, causal=causal, smooth=smooth)
+    # bf16 output adds one rounding (relative 2^-9) on top of the tolerance
+    extra = 2.0 ** -8 if out_bf16 else 0.0
+    assert_close("out", out.reshape(-1, 128), O, rtol=1e-2 + extra)
+    assert_close("lse", lse.reshape(-1), LSE, atol=LSE_ATOL, rtol=0.0)
+
+
+def test_prefill_small_config_full_smooth(mpfa, oracle_mod):
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("prefill_1k_2x1"))
+
+
+def test_prefill_small_config_full_direct(mpfa, oracle_mod):
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("prefill_1k_2x1"), smooth=False)
+
+
+@pytest.mark.parametrize("N", [1, 127, 129, 300])
+def test_prefill_gqa2_bf16_ragged(mpfa, oracle_mod, N):
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=2, Hq=4, Hkv=2, N=N),
+                   out_bf16=True)
+
+
+def test_prefill_gqa5_spikes(mpfa, oracle_mod):
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("qwen14b_prefill_32k", B=1, Hq=10, Hkv=2, N=520))
+
+
+@pytest.mark.parametrize("smooth", [True, False])
+def test_prefill_non_causal(mpfa, oracle_mod, smooth):
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=2, Hkv=1, N=333),
+                   causal=False, smooth=smooth)
+
+
+def _check_decode(mpfa, oracle_mod, cfg, smooth=True, with_lse=True):
+    import torch
+    from mixed_precision_flashattention_amd import synth
+    q, k, v = synth.full(cfg, "q"), synth.full(cfg, "k"), synth.full(cfg, "v")
+    qm = synth.q_mean(cfg)
+    say(f"case: decode B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} splits{cfg.num_splits} smooth={smooth}")
+    kd = dev(k, torch.bfloat16)
+    kq = mpfa.quantize_k(kd, q_mean=dev(qm)) if smooth else mpfa.quantize_k(kd, smooth=False)
+    vq = mpfa.quantize_v(dev(v, torch.bfloat16))
+    out, lse = mpfa.decode(dev(q, torch.bfloat16), kq, vq, cfg.scale, cfg.num_splits,
+                           out_dtype=torch.float32, with_lse=with_lse)
+    torch.cuda.synchronize()
+    O, LSE = oracle_mod.decode(q, k, v, qm if smooth else None, cfg.num_splits, cfg.scale, smooth=smooth)
+    assert_close("out", host(out).reshape(-1, 128), O.reshape(-1, 128))
+    if with_lse:
+        assert_close("lse", host(lse).reshape(-1), LSE.reshape(-1), atol=LSE_ATOL, rtol=0.0)
+
+
+@pytest.mark.parametrize("N,splits", [(1000, 3), (4096, 8), (1, 4), (300, 32), (129, 1)])
+def test_decode_gqa4(mpfa, oracle_mod, N, splits):
+    from mixed_precision_flashattention_amd import synth
+    _check_decode(mpfa, oracle_mod,
+                  synth.config("llama8b_decode_128k", B=2, Hq=8, Hkv=2, N=N, num_splits=splits))
+
+
+def test_decode_gqa5_direct(mpfa, oracle_mod):
+    from mixed_precision_flashattention_amd import synth
+    _check_decode(mpfa, oracle_mod,
+                  synth.config("llama8b_decode_128k", B=1, Hq=10, Hkv=2, N=2000, num_splits=5),
+                  smooth=False)
+
+
+def test_decode_gqa8(mpfa, oracle_mod):
+    from mixed_precision_flashattention_amd import synth
+    _check_decode(mpfa, oracle_mod,
+                  synth.config("llama8b_decode_128k", B=1, Hq=16, Hkv=2, N=777, num_splits=2))
