@@ -142,23 +142,18 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float* x, float g, uint32_
 // FP16 and the MFMA sees exactly the dequantized operand (up to the global
 // scale, which is applied in the exponent).
 //
-// FP16 bits of the E2M1 magnitudes have a zero low byte; the high byte is
-// looked up with v_perm_b32 (an 8-entry byte table), the sign bit moved in.
+// v_cvt_scalef32_pk_f16_fp4 decodes one byte (two codes, low nibble first)
+// and applies only the exponent of its scale operand, so it is used with
+// scale 1 and the E4M3 scale is applied by one packed FP16 multiply.
 __device__ __forceinline__ void expand_fp4x8(uint32_t w, f16x2 s2, uint32_t* out) {
-  const uint32_t lut_lo = 0x3E3C3800u;  // idx 0..3 -> 0x00 0x38 0x3C 0x3E
-  const uint32_t lut_hi = 0x46444240u;  // idx 4..7 -> 0x40 0x42 0x44 0x46
-  const uint32_t sel_e = w & 0x07070707u;
-  const uint32_t sel_o = (w >> 4) & 0x07070707u;
-  const uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_e) | ((w & 0x08080808u) << 4);
-  const uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_o) | (w & 0x80808080u);
-  const uint32_t p0 = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-  const uint32_t p1 = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-  const uint32_t p2 = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-  const uint32_t p3 = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p0) * s2);
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p1) * s2);
-  out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p2) * s2);
-  out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p3) * s2);
+  const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  out[0] = __builtin_bit_cast(uint32_t, a0 * s2);
+  out[1] = __builtin_bit_cast(uint32_t, a1 * s2);
+  out[2] = __builtin_bit_cast(uint32_t, a2 * s2);
+  out[3] = __builtin_bit_cast(uint32_t, a3 * s2);
 }
 
 __device__ __forceinline__ f16x2 e4m3_scale_f16x2(uint32_t code) {

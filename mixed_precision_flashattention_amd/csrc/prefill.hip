@@ -26,7 +26,7 @@ namespace mpfa {
 constexpr int kQTile = 128;
 constexpr int kKStride = 272;  // bytes per LDS row of K~ (128 f16 + 16 bytes of padding)
 
-__global__ __launch_bounds__(256) void k_prefill(PrefillParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(PrefillParams p) {
   __shared__ __align__(16) uint8_t smem_k[kQTile * kKStride];  // K~ block (Q~ in the prologue)
   __shared__ __align__(16) uint8_t smem_v[4 * kD * 32];        // 4 V tiles [d][32 tokens]
   __shared__ uint16_t smem_delta[kBlk];
@@ -130,43 +130,57 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
+  // Per-thread share of a block's loads: K codes of (key, head-dim half),
+  // 4 x 16 bytes of the V tiles, one Delta_S entry.  Block j+1 is fetched
+  // into registers while block j is computed.
+  const int ld_key = tid >> 1, ld_half = tid & 1;
+  uint4 kc0 = make_uint4(0, 0, 0, 0), kc1 = kc0;
+  uint32_t ksc = 0;
+  uint4 vv[4];
+  uint32_t dd = 0;
+  auto load_block = [&](int jb) {
+    const int kb0 = jb * kBlk;
+    const int gk = kb0 + ld_key;
+    kc0 = make_uint4(0, 0, 0, 0);
+    kc1 = kc0;
+    ksc = 0;
+    if (gk < N) {
+      const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)gk * 64 + 32 * ld_half);
+      kc0 = src[0];
+      kc1 = src[1];
+      ksc = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)gk * 8 + 4 * ld_half);
+    }
+    const int tt0 = kb0 / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int tt = idx >> 8;
+      vv[i] = make_uint4(0, 0, 0, 0);
+      if (tt0 + tt < ntiles32)
+        vv[i] = reinterpret_cast<const uint4*>(vbase + (int64_t)(tt0 + tt) * (kD * 32))[idx & 255];
+    }
+    if (smooth && tid < kBlk) dd = (kb0 + tid < N) ? dbase[kb0 + tid] : 0u;
+  };
+  load_block(0);
+
   for (int j = 0; j < nblk; ++j) {
     const int k0 = j * kBlk;
-    __syncthreads();
-    {  // K block: thread -> (key, half of the head dim), 32 code bytes + 4 scales
-      const int key = tid >> 1, hh = tid & 1;
-      const int gk = k0 + key;
-      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0;
-      uint32_t sc = 0;
-      if (gk < N) {
-        const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)gk * 64 + 32 * hh);
-        c0 = src[0];
-        c1 = src[1];
-        sc = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)gk * 8 + 4 * hh);
-      }
-      const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      uint8_t* dst = smem_k + key * kKStride + hh * 128;
+    __syncthreads();  // every wave is done with the previous block's LDS tiles
+    {
+      const uint32_t w[8] = {kc0.x, kc0.y, kc0.z, kc0.w, kc1.x, kc1.y, kc1.z, kc1.w};
+      uint8_t* dst = smem_k + ld_key * kKStride + ld_half * 128;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t e[4];
-        expand_fp4x8(w[i], e4m3_scale_f16x2((sc >> (8 * (i >> 1))) & 0xFFu), e);
+        expand_fp4x8(w[i], e4m3_scale_f16x2((ksc >> (8 * (i >> 1))) & 0xFFu), e);
         *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(e[0], e[1], e[2], e[3]);
       }
-    }
-    {  // V block: 4 consecutive 32-token tiles = 16 KB, a straight copy
-      const int tt0 = k0 / 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;
-        const int tt = idx >> 8;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (tt0 + tt < ntiles32)
-          val = reinterpret_cast<const uint4*>(vbase + (int64_t)(tt0 + tt) * (kD * 32))[idx & 255];
-        reinterpret_cast<uint4*>(smem_v)[idx] = val;
-      }
+      for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(smem_v)[tid + 256 * i] = vv[i];
+      if (smooth && tid < kBlk) smem_delta[tid] = (uint16_t)dd;
     }
-    if (smooth && tid < kBlk) smem_delta[tid] = (k0 + tid < N) ? dbase[k0 + tid] : (uint16_t)0;
     __syncthreads();
+    if (j + 1 < nblk) load_block(j + 1);
 
     // ---- scores S^T: 4 tiles of 32 keys x 32 queries --------------------
     f32x16 s[4];
@@ -229,9 +243,12 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillParams p) {
     l_run = fmaf(alpha, l_run, lsum);
 
     // ---- O^T = alpha O^T + V^T P^T on FP8 MFMA --------------------------
+    if (!__all(alpha == 1.0f)) {  // a row max moved somewhere in this wave
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      o[dt] *= alpha;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const i32x8 va = *reinterpret_cast<const i32x8*>(smem_v + (2 * c + h) * (kD * 32) +

@@ -159,3 +159,36 @@ def sample_rows(cfg: Config, n_random: int = 256) -> np.ndarray:
     for _ in range(n_random):
         rows.append((int(r.integers(cfg.B)), int(r.integers(cfg.Hq)), int(r.integers(cfg.N))))
     return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+def device_inputs(cfg: Config, device="cuda", seed: int | None = None):
+    """Q, K, V drawn directly on the device (for the throughput runs, whose
+    tensors are too large to draw on the host head by head): the same laws as
+    ``head`` -- N(0, 1), the same per-KV-head outlier channels and offsets as
+    ``k_outliers``, optional spikes -- from a seeded torch generator, rounded
+    to the configuration's dtype.  Decode also gets frozen query means.
+    Returns a dict of device tensors."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed * 1000003 + cfg.cid if seed is None else seed)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    nq = 1 if cfg.kind == "decode" else cfg.N
+    out = {}
+    for name, H, T in (("q", cfg.Hq, nq), ("k", cfg.Hkv, cfg.N), ("v", cfg.Hkv, cfg.N)):
+        x = torch.empty((cfg.B, H, T, cfg.D), dtype=tdt, device=device)
+        for b in range(cfg.B):  # one batch entry at a time bounds the fp32 scratch
+            xb = torch.randn((H, T, cfg.D), generator=g, device=device, dtype=torch.float32)
+            if name == "k" and cfg.n_outlier > 0:
+                for h in range(H):
+                    ch, off = k_outliers(cfg, h)
+                    xb[h][:, torch.from_numpy(ch).to(device)] += torch.from_numpy(off).to(device)
+            if cfg.spike_frac > 0:
+                mask = torch.rand(xb.shape, generator=g, device=device) < cfg.spike_frac
+                xb[mask] *= cfg.spike_mult
+            x[b].copy_(xb.to(tdt))
+            del xb
+        out[name] = x
+    if cfg.kind == "decode":
+        out["q_mean"] = torch.randn((cfg.B, cfg.Hq, cfg.D), generator=g, device=device,
+                                    dtype=torch.float32) / float(np.sqrt(cfg.N))
+    return out
