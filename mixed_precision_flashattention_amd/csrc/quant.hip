@@ -72,23 +72,26 @@ __global__ void k_mean_finalize(const uint32_t* __restrict__ absmax,
 }
 
 // max |fp32(x - mean[bh, d])| over a whole [BH, N, 128] tensor (mean may be
-// NULL).  Each thread takes 16-element groups; one atomic per wave.
-__global__ void k_centered_amax(const void* __restrict__ x, int is_bf16, int64_t n_groups,
-                                int N, const float* __restrict__ mean,
-                                uint32_t* __restrict__ out) {
+// NULL).  Grid (row chunks, BH): each thread takes 16-element groups of one
+// (batch, head) slice; one atomic per wave.
+constexpr int kAmaxGroups = 4096;  // 16-element groups per block (512 rows)
+
+__global__ void k_centered_amax(const void* __restrict__ x, int is_bf16, int N,
+                                const float* __restrict__ mean, uint32_t* __restrict__ out) {
+  const int64_t bh = blockIdx.y;
+  const int64_t n_groups = (int64_t)N * 8;
+  const int64_t g_begin = (int64_t)blockIdx.x * kAmaxGroups;
+  const int64_t g_end = min(n_groups, g_begin + kAmaxGroups);
+  const int d0 = (threadIdx.x & 7) * 16;  // blockDim is a multiple of 8
+  float mu[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mu[j] = mean ? mean[bh * kD + d0 + j] : 0.0f;
   float m = 0.0f;
-  for (int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; gi < n_groups;
-       gi += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t gi = g_begin + threadIdx.x; gi < g_end; gi += blockDim.x) {
     float v[16];
-    load16(x, gi * 16, is_bf16, v);
-    const int d0 = (int)(gi & 7) * 16;
-    if (mean) {
-      const float* mu = mean + (gi / 8 / N) * kD + d0;
+    load16(x, (bh * n_groups + gi) * 16, is_bf16, v);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = v[j] - mu[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j] - mu[j]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -210,9 +213,9 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
 
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
                           uint32_t* out, hipStream_t st) {
-  const int64_t n_groups = (int64_t)BH * N * (kD / 16);
-  hipLaunchKernelGGL(k_centered_amax, dim3(grid_for(n_groups, 256, 8192)), dim3(256), 0, st, x,
-                     is_bf16, n_groups, N, mean, out);
+  const int64_t n_groups = (int64_t)N * (kD / 16);
+  dim3 grid((unsigned)((n_groups + kAmaxGroups - 1) / kAmaxGroups), BH);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, mean, out);
 }
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
