@@ -19,7 +19,136 @@ namespace mpfa {
 
 constexpr int kQStride = 272;  // LDS row of Q~ (f16)
 constexpr int kPStride = 144;  // LDS row of P^ (128 keys + 16 bytes)
+constexpr int kVTileBytes = kD * 32;
 
+// Everything one 128-key block needs from HBM, per lane: the K codes of its
+// key in each of the 4 score tiles (32 bytes = its head-dim half), their 4
+// E4M3 scales, the group's Delta_S entries of those keys, and 8 x 32 bytes
+// of V^T operands.  Two of these are live: block j+1 is loaded while block
+// j is computed.
+struct DecodeBlockRegs {
+  uint4 k[4][2];
+  uint32_t sc[4];
+  uint32_t dl[4][8];
+  i32x8 v[8];
+};
+
+struct DecodeCtx {
+  const uint8_t* kbase;
+  const uint8_t* sbase;
+  const uint8_t* vbase;
+  const uint16_t* dbase;  // Delta_S row of the group's first query head
+  int N, G, ntiles32;
+};
+
+// Keys past the end are clamped to the last token (and masked later).
+template <bool SMOOTH>
+__device__ __forceinline__ void decode_load(DecodeBlockRegs& r, const DecodeCtx& c, int k0,
+                                            int lane) {
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int key = min(k0 + 32 * t + col, c.N - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(c.kbase + (int64_t)key * 64 + 32 * h);
+    r.k[t][0] = src[0];
+    r.k[t][1] = src[1];
+    r.sc[t] = *reinterpret_cast<const uint32_t*>(c.sbase + (int64_t)key * 8 + 4 * h);
+    if (SMOOTH) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        r.dl[t][g] = g < c.G ? c.dbase[(int64_t)g * c.N + key] : 0u;
+    }
+  }
+  const int n = lane & 15, kg = lane >> 4;
+  const int tt = min(k0 / 32 + kg, c.ntiles32 - 1);
+  const uint8_t* vt = c.vbase + (int64_t)tt * kVTileBytes;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) r.v[dt] = *reinterpret_cast<const i32x8*>(vt + (16 * dt + n) * 32);
+}
+
+struct DecodeState {
+  float m[4], l[4];
+  f32x4 o[8];
+};
+
+template <bool SMOOTH>
+__device__ __forceinline__ void decode_compute(const DecodeBlockRegs& r, DecodeState& st, int k0,
+                                               int p1, int lane, float lam, const i32x4* qa,
+                                               const i32x4& dA, uint8_t* sp, float* salpha) {
+  const int h = lane >> 5, col = lane & 31;
+  // ---- scores S = Q~ K~^T: 4 tiles of 32 keys, lane col = key ------------
+  f32x16 s[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t w[8] = {r.k[t][0].x, r.k[t][0].y, r.k[t][0].z, r.k[t][0].w,
+                           r.k[t][1].x, r.k[t][1].y, r.k[t][1].z, r.k[t][1].w};
+    uint32_t e[4];
+    expand_fp4x8(w[0], e4m3_scale_f16x2(r.sc[t] & 0xFFu), e);
+    const i32x4 kb0 = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
+    if (SMOOTH) {
+      const i32x4 dB = {(int)(r.dl[t][0] | (r.dl[t][1] << 16)), (int)(r.dl[t][2] | (r.dl[t][3] << 16)),
+                        (int)(r.dl[t][4] | (r.dl[t][5] << 16)), (int)(r.dl[t][6] | (r.dl[t][7] << 16))};
+      s[t] = mfma32_bf16(dA, dB, f32x16{});
+      s[t] = mfma32_f16(qa[0], kb0, s[t]);
+    } else {
+      s[t] = mfma32_f16(qa[0], kb0, f32x16{});
+    }
+#pragma unroll
+    for (int kc = 1; kc < 8; ++kc) {
+      expand_fp4x8(w[kc], e4m3_scale_f16x2((r.sc[t] >> (8 * (kc >> 1))) & 0xFFu), e);
+      s[t] = mfma32_f16(qa[kc], i32x4{(int)e[0], (int)e[1], (int)e[2], (int)e[3]}, s[t]);
+    }
+  }
+
+  // ---- softmax on rows 4h + v (v < 4), keys across the 32 lanes ----------
+  float alpha[4], nb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t][v] = (k0 + 32 * t + col < p1) ? s[t][v] : -INFINITY;
+      mx = fmaxf(mx, s[t][v]);
+    }
+#pragma unroll
+    for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    const float m_new = fmaxf(st.m[v], mx);
+    alpha[v] = fast_exp2(lam * (st.m[v] - m_new));
+    nb[v] = kLog2_448 - lam * m_new;
+    st.m[v] = m_new;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float lsum = 0.0f;
+    uint8_t* prow = sp + (4 * h + v) * kPStride + col;
+#pragma unroll
+    for (int t = 0; t < 4; t += 2) {
+      const float e0 = fast_exp2(fmaf(s[t][v], lam, nb[v]));
+      const float e1 = fast_exp2(fmaf(s[t + 1][v], lam, nb[v]));
+      lsum += e0 + e1;
+      const uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
+      prow[32 * t] = (uint8_t)(wd & 0xFFu);
+      prow[32 * (t + 1)] = (uint8_t)((wd >> 8) & 0xFFu);
+    }
+    st.l[v] = fmaf(alpha[v], st.l[v], lsum);
+  }
+  if (col == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) salpha[4 * h + v] = alpha[v];
+  }
+  __syncthreads();
+
+  // ---- O^T += V^T P^T on FP8 16x16x128 -----------------------------------
+  const int n = lane & 15, kg = lane >> 4;  // query column, 32-key group
+  const i32x8 pbv = n < 8 ? *reinterpret_cast<const i32x8*>(sp + n * kPStride + 32 * kg)
+                          : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const float a_o = n < 8 ? salpha[n] : 1.0f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma16_fp8(r.v[dt], pbv, st.o[dt] * a_o);
+  __syncthreads();
+}
+
+template <bool SMOOTH>
 __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   __shared__ __align__(16) uint8_t sq[8 * kQStride];
   __shared__ __align__(16) uint8_t sp[8 * kPStride];
@@ -33,7 +162,6 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)hk * G;  // first query head of the group
   const int p0 = part * p.chunk;
   const int p1 = min(p0 + p.chunk, N);
-  const bool smooth = p.delta_s != nullptr;
 
   if (p0 >= p1) {  // empty partition: neutral state
     if (lane < G) {
@@ -49,9 +177,6 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   const float gK = *p.k_gscale;
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;
-  const float cinv = 1.0f / gg;
-  const uint32_t c_hi = bf16_rne(cinv);
-  const uint32_t c_lo = bf16_rne(cinv - __uint_as_float(c_hi << 16));
 
   {  // NVFP4 of the group's query rows: lane -> (row g = lane / 8, block lane % 8)
     const int g = lane >> 3, blk = lane & 7;
@@ -59,7 +184,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
     if (g < G) {
       float x[16];
       load16(p.q, (hq0 + g) * kD + blk * 16, p.q_bf16, x);
-      if (smooth) {
+      if (SMOOTH) {
         const float* mu = p.q_mean + (hq0 + g) * kD + blk * 16;
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = x[j] - mu[j];
@@ -90,127 +215,55 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   // half 0, lo part in half 1) in slot g; the B operand holds Delta_S[g, key]
   // in slot g of both halves, so the step adds Delta_S / (gQ gK) to row g.
   i32x4 dA = {0, 0, 0, 0};
-  if (smooth && col < G) {
+  if (SMOOTH && col < G) {
+    const float cinv = 1.0f / gg;
+    const uint32_t c_hi = bf16_rne(cinv);
+    const uint32_t c_lo = bf16_rne(cinv - __uint_as_float(c_hi << 16));
     const int cv = (int)((h == 0 ? c_hi : c_lo) << (16 * (col & 1)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) dA[i] = ((col >> 1) == i) ? cv : 0;
   }
 
-  const int ntiles32 = (N + 31) / 32;
+  DecodeCtx c;
+  c.N = N;
+  c.G = G;
+  c.ntiles32 = (N + 31) / 32;
   const int64_t kvh = (int64_t)b * p.Hkv + hk;
-  const uint8_t* kbase = p.k_fp4 + kvh * N * 64;
-  const uint8_t* sbase = p.k_sf + kvh * N * 8;
-  const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * (kD * 32);
+  c.kbase = p.k_fp4 + kvh * N * 64;
+  c.sbase = p.k_sf + kvh * N * 8;
+  c.vbase = p.v_fp8 + kvh * c.ntiles32 * kVTileBytes;
+  c.dbase = SMOOTH ? p.delta_s + hq0 * N : nullptr;
 
-  float m_run[4], l_run[4];
+  DecodeState st;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    m_run[v] = -INFINITY;
-    l_run[v] = 0.0f;
+    st.m[v] = -INFINITY;
+    st.l[v] = 0.0f;
   }
-  f32x4 o[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{};
 
-  for (int k0 = p0; k0 < p1; k0 += kBlk) {
-    // ---- scores: 4 tiles of 32 keys, lane col = key -------------------
-    f32x16 s[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = k0 + 32 * t + col;
-      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0;
-      uint32_t sc = 0;
-      i32x4 dB = {0, 0, 0, 0};
-      if (key < p1) {
-        const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)key * 64 + 32 * h);
-        c0 = src[0];
-        c1 = src[1];
-        sc = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)key * 8 + 4 * h);
-        if (smooth) {
-          uint32_t dv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int g = 0; g < 8; ++g)
-            if (g < G) dv[g] = p.delta_s[(hq0 + g) * N + key];
-          dB = i32x4{(int)(dv[0] | (dv[1] << 16)), (int)(dv[2] | (dv[3] << 16)),
-                     (int)(dv[4] | (dv[5] << 16)), (int)(dv[6] | (dv[7] << 16))};
-        }
-      }
-      f32x16 acc = f32x16{};
-      if (smooth) acc = mfma32_bf16(dA, dB, acc);
-      const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        uint32_t e[4];
-        expand_fp4x8(w[kc], e4m3_scale_f16x2((sc >> (8 * (kc >> 1))) & 0xFFu), e);
-        acc = mfma32_f16(qa[kc], i32x4{(int)e[0], (int)e[1], (int)e[2], (int)e[3]}, acc);
-      }
-      s[t] = acc;
-    }
-
-    // ---- softmax on rows 4h + v (v < 4), keys across the 32 lanes ------
-    float alpha[4], nb[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (k0 + 32 * t + col >= p1) s[t][v] = -INFINITY;
-        mx = fmaxf(mx, s[t][v]);
-      }
-#pragma unroll
-      for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
-      const float m_new = fmaxf(m_run[v], mx);
-      alpha[v] = fast_exp2(lam * (m_run[v] - m_new));
-      nb[v] = kLog2_448 - lam * m_new;
-      m_run[v] = m_new;
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float lsum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 4; t += 2) {
-        const float e0 = fast_exp2(fmaf(s[t][v], lam, nb[v]));
-        const float e1 = fast_exp2(fmaf(s[t + 1][v], lam, nb[v]));
-        lsum += e0 + e1;
-        const uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
-        uint8_t* prow = sp + (4 * h + v) * kPStride + col;
-        prow[32 * t] = (uint8_t)(wd & 0xFFu);
-        prow[32 * (t + 1)] = (uint8_t)((wd >> 8) & 0xFFu);
-      }
-      l_run[v] = fmaf(alpha[v], l_run[v], lsum);
-    }
-    if (col == 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) salpha[4 * h + v] = alpha[v];
-    }
-    __syncthreads();
-
-    // ---- O^T += V^T P^T on FP8 16x16x128 -------------------------------
-    const int n = lane & 15, kg = lane >> 4;  // query column, 32-key group
-    const i32x8 pbv = n < 8 ? *reinterpret_cast<const i32x8*>(sp + n * kPStride + 32 * kg)
-                            : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    const float a_o = n < 8 ? salpha[n] : 1.0f;
-    const int tt = k0 / 32 + kg;
-    const bool v_ok = tt < ntiles32;
-    const uint8_t* vt = vbase + (int64_t)tt * (kD * 32);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      i32x8 va = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (v_ok) va = *reinterpret_cast<const i32x8*>(vt + (16 * dt + n) * 32);
-      o[dt] = mfma16_fp8(va, pbv, o[dt] * a_o);
-    }
-    __syncthreads();
+  // Two register stages: the loads of the next block are in flight while
+  // the current one is computed.
+  DecodeBlockRegs ra, rb;
+  decode_load<SMOOTH>(ra, c, p0, lane);
+  for (int k0 = p0; k0 < p1; k0 += 2 * kBlk) {
+    if (k0 + kBlk < p1) decode_load<SMOOTH>(rb, c, k0 + kBlk, lane);
+    decode_compute<SMOOTH>(ra, st, k0, p1, lane, lam, qa, dA, sp, salpha);
+    if (k0 + kBlk >= p1) break;
+    if (k0 + 2 * kBlk < p1) decode_load<SMOOTH>(ra, c, k0 + 2 * kBlk, lane);
+    decode_compute<SMOOTH>(rb, st, k0 + kBlk, p1, lane, lam, qa, dA, sp, salpha);
   }
 
   // ---- partition state -------------------------------------------------
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    float l = l_run[v];
+    float l = st.l[v];
 #pragma unroll
     for (int o2 = 16; o2 > 0; o2 >>= 1) l += __shfl_xor(l, o2);
     const int g = 4 * h + v;
     if (col == 0 && g < G) {
-      p.ws_m[(hq0 + g) * P + part] = m_run[v];
+      p.ws_m[(hq0 + g) * P + part] = st.m[v];
       p.ws_l[(hq0 + g) * P + part] = l;
     }
   }
@@ -220,7 +273,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<float4*>(dst + 16 * dt) =
-          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+          make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
   }
 }
 
@@ -271,7 +324,10 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
 
 void launch_decode(const DecodeParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.P);
-  hipLaunchKernelGGL(k_decode_split, dim3(grid), dim3(64), 0, st, p);
+  if (p.delta_s)
+    hipLaunchKernelGGL(k_decode_split<true>, dim3(grid), dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL(k_decode_split<false>, dim3(grid), dim3(64), 0, st, p);
   hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(p.B * p.Hq)), dim3(128), 0, st, p);
 }
 
