@@ -37,6 +37,38 @@ PEAK_MIXED = 1.0 / (0.5 / PEAK_FP4 + 0.5 / PEAK_FP8)  # half the FLOPs in each c
 PEAK_HBM = 8.0e12
 
 
+KERNEL_SOURCES = {
+    "prefill": ["csrc/prefill.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
+    "decode": ["csrc/decode.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
+    "quant": ["csrc/quant.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
+}
+
+
+def source_hash(kind):
+    """sha256 of the sources a kernel is built from (package-relative paths)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "mixed_precision_flashattention_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per call from profiles/traffic.json (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE, scaled by the copy-kernel factors), or None when the entry is
+    missing or was taken on kernel sources that have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f)["calls"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if entry.get("source_sha256") != source_hash(entry["kind"]):
+        return None
+    return int(entry["bytes_per_call"])
+
+
 def prefill_flops(B, Hq, N, causal=True):
     pairs = N * (N + 1) // 2 if causal else N * N
     return 4.0 * 128 * pairs * B * Hq
@@ -122,6 +154,99 @@ def accuracy_report(mpfa):
     return out
 
 
+def write_traffic(run_dir, args):
+    """profiles/traffic.json from six counter runs of `bench.py --only X`
+    (X in prefill, decode, copy; one FETCH_SIZE and one WRITE_SIZE pass each).
+    FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the
+    factor that maps the 1 GiB copy's reading to the 1 GiB it moved.  A call's
+    bytes are summed over its dispatches (fill, amax pre-pass, main kernel(s)),
+    averaged over the three calls."""
+    import collections
+    import csv
+
+    def load(op, counter):
+        path = os.path.join(run_dir, f"pmc_{op}_{counter}", "run_counter_collection.csv")
+        vals, names = collections.defaultdict(float), {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                i = int(r["Dispatch_Id"])
+                vals[i] += float(r["Counter_Value"])
+                names[i] = r["Kernel_Name"]
+        return vals, names
+
+    def short(name):
+        return name.split("(")[0].replace("void ", "").replace("mpfa::", "")
+
+    cf, cn = load("copy", "FETCH_SIZE")
+    cw, _ = load("copy", "WRITE_SIZE")
+    copies = [i for i, n in cn.items() if "copyBuffer" in n or "copy" in n.lower()][-3:]
+    fetch_kib = sum(cf[i] for i in copies) / len(copies)
+    write_kib = sum(cw[i] for i in copies) / len(copies)
+    moved_kib = (1 << 30) / 1024
+    F, W = moved_kib / fetch_kib, moved_kib / write_kib
+    out = {"calibration": {"copy_bytes": 1 << 30, "fetch_kib": round(fetch_kib, 1),
+                           "write_kib": round(write_kib, 1), "fetch_factor": round(F, 5),
+                           "write_factor": round(W, 5)},
+           "command": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv "
+                      "-d DIR/pmc_<op>_<counter> -o run -- python bench.py --only <op>; "
+                      "then python bench.py --write-traffic DIR",
+           "calls": {}}
+    for op, kind, main_kernel, offsets, name in (
+            ("prefill", "prefill", "k_prefill<true>", (-2, -1, 0),
+             f"mpfa_prefill {args.workload}"),
+            ("decode", "decode", "k_decode_split<true>", (-2, -1, 0, 1),
+             f"mpfa_decode {args.decode_workload}")):
+        fv, fn = load(op, "FETCH_SIZE")
+        wv, wn = load(op, "WRITE_SIZE")
+        parts = {}
+        for vals, names, key in ((fv, fn, "fetch_kib"), (wv, wn, "write_kib")):
+            mains = sorted(i for i, n in names.items() if main_kernel in n)
+            for o in offsets:
+                kname = short(names[mains[0] + o])
+                avg = sum(vals[i + o] for i in mains) / len(mains)
+                parts.setdefault(kname, {})[key] = round(avg, 1)
+        for p in parts.values():
+            p["bytes"] = int((p["fetch_kib"] * F + p["write_kib"] * W) * 1024)
+        out["calls"][name] = {"kind": kind, "source_sha256": source_hash(kind), "kernels": parts,
+                              "bytes_per_call": sum(p["bytes"] for p in parts.values())}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def profile_only(args, mpfa, synth, dev):
+    """Three calls of one operation for rocprofv3 counter passes: the prefill
+    call of the bench workload, the decode call of the decode workload, or a
+    1 GiB device-to-device copy (the calibration of FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    if args.only == "copy":
+        a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+    elif args.only == "prefill":
+        cfg = synth.config(args.workload)
+        x = synth.device_inputs(cfg, dev)
+        kq = mpfa.quantize_k(x["k"], q=x["q"])
+        vq = mpfa.quantize_v(x["v"])
+        out = torch.empty(x["q"].shape, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(256, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            mpfa.prefill(x["q"], kq, vq, cfg.scale, causal=True, out=out, ws=ws)
+    else:
+        cfg = synth.config(args.decode_workload)
+        x = synth.device_inputs(cfg, dev)
+        kq = mpfa.quantize_k(x["k"], q_mean=x["q_mean"])
+        vq = mpfa.quantize_v(x["v"])
+        del x["k"], x["v"]
+        out = torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            mpfa.decode(x["q"], kq, vq, cfg.scale, cfg.num_splits, out=out)
+    torch.cuda.synchronize()
+    log(f"[bench] --only {args.only}: 3 calls done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,7 +258,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="counter-collection mode: set up, run 3 calls of one operation, exit")
+    ap.add_argument("--write-traffic", metavar="DIR", default=None,
+                    help="build profiles/traffic.json from the rocprofv3 counter CSVs in DIR "
+                         "(pmc_{prefill,decode,copy}_{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -146,6 +279,9 @@ def main():
     mpfa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        profile_only(args, mpfa, synth, dev)
+        return
     cfg = synth.config(args.workload)
     B, Hq, Hkv, N, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.D
     log(f"[bench] {torch.cuda.get_device_name(0)} hip {torch.version.hip}; workload {cfg.name}")
@@ -225,7 +361,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "mpfa_prefill (Q amax pre-pass + k_prefill)",
                      "achieved": round(achieved, 2), "peak": round(PEAK_MIXED / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MIXED, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic("mpfa_prefill llama8b_prefill_16k"),
                      "flops_per_launch": flops, "ms_per_launch": round(ms_prefill, 4)},
         "prefill_ms": round(ms_prefill, 4), "prefill_direct_ms": round(ms_direct, 4),
         "stage_one_ms": round(ms_stage1, 4),
@@ -267,7 +403,8 @@ def main():
             "kv_len": dcfg.N, "num_splits": dcfg.num_splits, "ms": round(ms_dec, 4),
             "value": round(gbs, 1), "unit": "GB/s", "bytes_per_call": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4), "traffic": None},
+                         "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4),
+                         "traffic": measured_traffic("mpfa_decode llama8b_decode_128k")},
             "direct_ms": round(ms_dec_direct, 4), "direct_GBps": round(gbs_d, 1)}
         del dkq, dvq, dq, dout, dws, dx
         torch.cuda.empty_cache()
