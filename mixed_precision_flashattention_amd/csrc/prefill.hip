@@ -289,31 +289,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 
   // ---- epilogue -----------------------------------------------------------
+  // An MFMA reads its operands from all 64 lanes whatever the execution mask,
+  // while loads honour it; so nothing that feeds the accumulators may be moved
+  // into a branch on the row.  Every lane normalises, only the stores of rows
+  // past the end are skipped.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_row < N) {
-    const float inv = sV / l_tot;
-    const int64_t obase = ((int64_t)bh * N + my_row) * kD;
+  const float inv = sV / l_tot;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4; ++dt) o[dt] *= inv;
+  const bool row_ok = my_row < N;
+  const int64_t obase = ((int64_t)bh * N + min(my_row, N - 1)) * kD;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * h;
-        const float a0 = o[dt][4 * g] * inv, a1 = o[dt][4 * g + 1] * inv;
-        const float a2 = o[dt][4 * g + 2] * inv, a3 = o[dt][4 * g + 3] * inv;
-        if (p.out_bf16) {
-          uint2 w;
-          w.x = bf16_rne(a0) | (bf16_rne(a1) << 16);
-          w.y = bf16_rne(a2) | (bf16_rne(a3) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + d0) = w;
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + obase + d0) =
-              make_float4(a0, a1, a2, a3);
-        }
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * dt + 8 * g + 4 * h;
+      const float a0 = o[dt][4 * g], a1 = o[dt][4 * g + 1];
+      const float a2 = o[dt][4 * g + 2], a3 = o[dt][4 * g + 3];
+      if (p.out_bf16) {
+        uint2 w;
+        w.x = bf16_rne(a0) | (bf16_rne(a1) << 16);
+        w.y = bf16_rne(a2) | (bf16_rne(a3) << 16);
+        if (row_ok) *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + d0) = w;
+      } else if (row_ok) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + obase + d0) =
+            make_float4(a0, a1, a2, a3);
       }
-    if (p.lse && h == 0)
-      p.lse[(int64_t)bh * N + my_row] =
-          kLn2 * (lam * m_run + log2f(l_tot)) - kLn2 * kLog2_448 + lse_off;
-  }
+    }
+  if (p.lse && h == 0 && row_ok)
+    p.lse[(int64_t)bh * N + my_row] =
+        kLn2 * (lam * m_run + log2f(l_tot)) - kLn2 * kLog2_448 + lse_off;
 }
 
 #undef MPFA_PREFILL_LOAD
