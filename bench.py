@@ -109,7 +109,8 @@ def cpu_baseline(cfg, target_s=12.0):
     k = synth.head(cfg, "k", 0, 0)[None, None]
     v = synth.head(cfg, "v", 0, 0)[None, None]
     t0 = time.perf_counter()
-    prep = oracle.pipeline._prepare(q, k, v, cfg.scale, smooth=True, identity=False)
+    ops = oracle.Operands(q, k, v, cfg.scale, smooth=True, identity=False)
+    kt, vt, delta = ops.k(0, 0), ops.v(0, 0), ops.delta(0, 0)
     t_prep = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -118,8 +119,7 @@ def cpu_baseline(cfg, target_s=12.0):
     while spent < target_s and done_rows < cfg.N:
         rows = np.sort(rng.integers(0, cfg.N, batch)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.attn_state(prep["qt"][0, 0][rows], rows, prep["kt"][0, 0], prep["vt"][0, 0],
-                          prep["delta"][0, 0], 0, cfg.N, cfg.scale, True)
+        oracle.attn_state(ops.q(0, 0, rows), rows, kt, vt, delta, 0, cfg.N, cfg.scale, True)
         spent += time.perf_counter() - t0
         done_rows += len(rows)
         done_flops += 4.0 * 128 * float((rows + 1).sum())

@@ -121,27 +121,39 @@ double oracle_bf16_decode(uint16_t h) {
  *   mean = fp32( (double)S / (double)T * u )   (FP64 ops, round to nearest)
  * x is [T][D] row-major, one (batch, head) slice; out is [D].               */
 void oracle_channel_mean(const float* x, int64_t T, int D, float* out) {
+  /* Rows are walked in memory order; per channel this is the same max and
+   * the same exact integer sum as a walk down the column. */
+  double* M = (double*)calloc((size_t)D, sizeof(double));
+  double* u_inv = (double*)calloc((size_t)D, sizeof(double));
+  int* E = (int*)calloc((size_t)D, sizeof(int));
+  int64_t* S = (int64_t*)calloc((size_t)D, sizeof(int64_t));
+  int64_t t;
   int d;
-  for (d = 0; d < D; ++d) {
-    double M = 0.0;
-    int64_t t, S = 0;
-    int E;
-    for (t = 0; t < T; ++t) {
+  for (t = 0; t < T; ++t)
+    for (d = 0; d < D; ++d) {
       double a = fabs((double)x[t * D + d]);
-      if (a > M) M = a;
+      if (a > M[d]) M[d] = a;
     }
-    if (M == 0.0 || T == 0) { out[d] = 0.0f; continue; }
-    frexp(M, &E); /* M = f * 2^E with f in [0.5, 1) */
-    for (t = 0; t < T; ++t) {
-      double y = ldexp((double)x[t * D + d], 30 - E);
-      S += (int64_t)nearbyint(y); /* default rounding mode: half to even */
-    }
-    {
-      double mean = (double)S / (double)T;
-      mean = mean * ldexp(1.0, E - 30);
+  for (d = 0; d < D; ++d) {
+    if (M[d] > 0.0) frexp(M[d], &E[d]); /* M = f * 2^E with f in [0.5, 1) */
+    u_inv[d] = ldexp(1.0, 30 - E[d]);    /* 1/u, a power of two: x * u_inv is exact */
+  }
+  for (t = 0; t < T; ++t)
+    for (d = 0; d < D; ++d)
+      S[d] += (int64_t)nearbyint((double)x[t * D + d] * u_inv[d]); /* half to even */
+  for (d = 0; d < D; ++d) {
+    if (M[d] == 0.0 || T == 0) {
+      out[d] = 0.0f;
+    } else {
+      double mean = (double)S[d] / (double)T;
+      mean = mean * ldexp(1.0, E[d] - 30);
       out[d] = (float)mean;
     }
   }
+  free(M);
+  free(u_inv);
+  free(E);
+  free(S);
 }
 
 /* max |x| over n elements (exact). */

@@ -84,65 +84,90 @@ def _finalize(m, l, acc, s_v, scale, lse_offset, out_f64=False):
     return o, lse
 
 
-def _prepare(q, k, v, scale, smooth, identity, q_mean=None):
-    """Shared preparation of dequantized operands for prefill and decode.
+class Operands:
+    """The operands of the attention stage, FP64, one head at a time.
 
-    Returns dict with qt [B,Hq,Nq,D] f64, kt / vt [B,Hkv,N,D] f64, s_v,
-    delta [B,Hq,N] f64 or None, quant_p, k_mean (smooth) for the LSE offset."""
-    q = np.asarray(q, dtype=F32)
-    k = np.asarray(k, dtype=F32)
-    v = np.asarray(v, dtype=F32)
-    B, Hq = q.shape[:2]
-    Hkv = k.shape[1]
-    G = Hq // Hkv
-    prep = {}
-    if identity:
+    Quantized mode keeps the codes of the whole call (the global scales are
+    per-tensor, so they always see every head) and dequantizes a head when it
+    is asked for; identity mode widens the inputs.  Fields: s_v, quant_p,
+    k_mean (smooth) and the per-head accessors q(b, h, pos), k(b, hk),
+    v(b, hk), delta(b, h) (None in direct mode)."""
+
+    def __init__(self, q, k, v, scale, smooth, identity, q_mean=None):
+        q = np.asarray(q, dtype=F32)
+        k = np.asarray(k, dtype=F32)
+        v = np.asarray(v, dtype=F32)
+        B, Hq = q.shape[:2]
+        Hkv = k.shape[1]
+        self.G = Hq // Hkv
+        self.smooth = smooth
+        self.identity = identity
+        self._q, self._k, self._v = q, k, v
+        self.k_mean = None
+        self._delta = None
+        if identity:
+            if smooth:
+                self.k_mean = channel_mean(k)
+                if q_mean is None:
+                    q_mean = channel_mean(q)
+                self._qm = np.asarray(q_mean, dtype=F64)
+            self.s_v, self.quant_p = 1.0, False
+            return
         if smooth:
-            k_mean = channel_mean(k)
-            if q_mean is None:
-                q_mean = channel_mean(q)
-            qm = np.asarray(q_mean, dtype=F64)
-            km = k_mean.astype(F64)
-            qt = q.astype(F64) - qm[:, :, None, :]
-            kt = k.astype(F64) - km[:, :, None, :]
-            delta = np.empty((B, Hq, k.shape[2]))
-            for b in range(B):
-                for h in range(Hq):
-                    delta[b, h] = kt[b, h // G] @ qm[b, h]
-            prep.update(k_mean=k_mean, delta=delta)
+            kq = quantize_k(k, q=q if q_mean is None else None, q_mean=q_mean, smooth=True)
+            qcodes, qsf, gq = quantize_q(q, kq["q_mean"])
+            self.k_mean = kq["k_mean"]
+            self._delta = kq["delta_s"]
         else:
-            qt, kt = q.astype(F64), k.astype(F64)
-            prep.update(delta=None)
-        prep.update(qt=qt, kt=kt, vt=v.astype(F64), s_v=1.0, quant_p=False)
-        return prep
-    if smooth:
-        kq = quantize_k(k, q=q if q_mean is None else None, q_mean=q_mean, smooth=True)
-        qcodes, qsf, gq = quantize_q(q, kq["q_mean"])
-        prep.update(k_mean=kq["k_mean"], delta=bf16_to_f64(kq["delta_s"]))
-    else:
-        kq = quantize_k(k, smooth=False)
-        qcodes, qsf, gq = quantize_q(q, None)
-        prep.update(delta=None)
-    vq = quantize_v(v)
-    table = e4m3_table()
-    prep.update(qt=nvfp4_dequantize(qcodes, qsf, gq),
-                kt=nvfp4_dequantize(kq["k_fp4"], kq["k_sf"], kq["k_gscale"]),
-                vt=table[vq["v_fp8"]], s_v=float(vq["v_scale"]), quant_p=True, kq=kq, vq=vq,
-                q_codes=qcodes, q_sf=qsf, q_gscale=gq)
-    return prep
+            kq = quantize_k(k, smooth=False)
+            qcodes, qsf, gq = quantize_q(q, None)
+        vq = quantize_v(v)
+        self.kq, self.vq = kq, vq
+        self.q_codes, self.q_sf, self.q_gscale = qcodes, qsf, gq
+        self.s_v = float(vq["v_scale"])
+        self.quant_p = True
+        self._table = e4m3_table()
+
+    def q(self, b, h, pos):
+        if self.identity:
+            x = self._q[b, h][pos].astype(F64)
+            return x - self._qm[b, h][None, :] if self.smooth else x
+        return nvfp4_dequantize(self.q_codes[b, h][pos], self.q_sf[b, h][pos], self.q_gscale)
+
+    def k(self, b, hk):
+        if self.identity:
+            x = self._k[b, hk].astype(F64)
+            return x - self.k_mean[b, hk].astype(F64)[None, :] if self.smooth else x
+        return nvfp4_dequantize(self.kq["k_fp4"][b, hk], self.kq["k_sf"][b, hk], self.kq["k_gscale"])
+
+    def v(self, b, hk):
+        if self.identity:
+            return self._v[b, hk].astype(F64)
+        return self._table[self.vq["v_fp8"][b, hk]]
+
+    def delta(self, b, h):
+        """Compensation vector of (b, q-head h): the stored bf16 values, or in
+        identity mode the FP64 product of the centered keys with Qbar."""
+        if not self.smooth:
+            return None
+        if self.identity:
+            return self.k(b, h // self.G) @ self._qm[b, h]
+        return bf16_to_f64(self._delta[b, h])
 
 
-def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=None, out_f64=False):
+def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=None, out_f64=False,
+                 ops=None):
     """Causal (or full) prefill, MpFA §5.1 second stage, for the selected rows.
 
     rows: None (every row) or an int array [R, 3] of (b, q-head, position).
+    ops: an Operands already built from the same q, k, v and mode (else built here).
     Returns (O [R, D] fp32, LSE [R] f64, rows) -- O = acc * s_V / (448 l), LSE in
     natural log with the smoothing row offset scale * (Q_i . Kbar) added back."""
     q = np.asarray(q, dtype=F32)
     B, Hq, N, D = q.shape
-    Hkv = np.asarray(k).shape[1]
-    G = Hq // Hkv
-    prep = _prepare(q, k, v, scale, smooth, identity)
+    if ops is None:
+        ops = Operands(q, k, v, scale, smooth, identity)
+    G = ops.G
     if rows is None:
         bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
         rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
@@ -150,22 +175,24 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
     O = np.empty((len(rows), D), dtype=F64 if out_f64 else F32)
     LSE = np.empty(len(rows))
     for b in range(B):
-        for h in range(Hq):
-            sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
-            if len(sel) == 0:
-                continue
-            pos = rows[sel, 2]
-            qt = prep["qt"][b, h][pos]
-            row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
-            delta = None if prep["delta"] is None else prep["delta"][b, h]
-            m, l, acc = attn_state(qt, row_pos, prep["kt"][b, h // G], prep["vt"][b, h // G], delta,
-                                   0, N, scale, prep["quant_p"])
-            off = None
-            if smooth:
-                off = scale * (q[b, h][pos].astype(F64) @ prep["k_mean"][b, h // G].astype(F64))
-            o, lse = _finalize(m, l, acc, prep["s_v"], scale, off, out_f64)
-            O[sel] = o
-            LSE[sel] = lse
+        for hk in range(q.shape[1] // G):
+            kt = vt = None
+            for h in range(hk * G, (hk + 1) * G):
+                sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+                if len(sel) == 0:
+                    continue
+                if kt is None:
+                    kt, vt = ops.k(b, hk), ops.v(b, hk)
+                pos = rows[sel, 2]
+                row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
+                m, l, acc = attn_state(ops.q(b, h, pos), row_pos, kt, vt, ops.delta(b, h), 0, N, scale,
+                                       ops.quant_p)
+                off = None
+                if smooth:
+                    off = scale * (q[b, h][pos].astype(F64) @ ops.k_mean[b, hk].astype(F64))
+                o, lse = _finalize(m, l, acc, ops.s_v, scale, off, out_f64)
+                O[sel] = o
+                LSE[sel] = lse
     return O, LSE, rows
 
 
@@ -178,46 +205,57 @@ def decode_partitions(n_kv: int, num_splits: int, block: int = KV_BLOCK):
     return [(min(p * chunk, n_kv), min((p + 1) * chunk, n_kv)) for p in range(num_splits)]
 
 
-def decode(q, k, v, q_mean, num_splits, scale, smooth=True, identity=False, out_f64=False):
+def decode(q, k, v, q_mean, num_splits, scale, smooth=True, identity=False, out_f64=False, heads=None,
+           ops=None):
     """Split-KV decode (MpFA §5.3): one query token per (batch, q-head), every key
     visible, per-partition online-softmax states merged by log-sum-exp.
 
     q [B, Hq, D] or [B, Hq, 1, D]; q_mean [B, Hq, D] frozen means (smooth mode).
-    Returns (O [B, Hq, D] fp32, LSE [B, Hq] f64)."""
+    heads: None (every (b, q-head)) or a list of (b, q-head) pairs.
+    ops: an Operands already built from the same inputs and mode (else built here).
+    Returns (O, LSE): [B, Hq, D] fp32 and [B, Hq] f64, or [len(heads), D] and
+    [len(heads)] for a head list."""
     q = np.asarray(q, dtype=F32)
     if q.ndim == 3:
         q = q[:, :, None, :]
     B, Hq, _, D = q.shape
-    k = np.asarray(k, dtype=F32)
-    Hkv, N = k.shape[1], k.shape[2]
-    G = Hq // Hkv
-    prep = _prepare(q, k, v, scale, smooth, identity, q_mean=q_mean if smooth else None)
+    N = np.asarray(k).shape[2]
+    if ops is None:
+        ops = Operands(q, k, v, scale, smooth, identity, q_mean=q_mean if smooth else None)
+    G = ops.G
     parts = decode_partitions(N, num_splits)
-    O = np.empty((B, Hq, D), dtype=F64 if out_f64 else F32)
-    LSE = np.empty((B, Hq))
-    for b in range(B):
-        for h in range(Hq):
-            qt = prep["qt"][b, h, 0:1]
-            delta = None if prep["delta"] is None else prep["delta"][b, h]
-            ms, ls, accs = [], [], []
-            for (p0, p1) in parts:
-                if p1 <= p0:
-                    ms.append(-np.inf)
-                    ls.append(0.0)
-                    accs.append(np.zeros(D))
-                    continue
-                m, l, acc = attn_state(qt, np.array([-1]), prep["kt"][b, h // G],
-                                       prep["vt"][b, h // G], delta, p0, p1, scale, prep["quant_p"])
-                ms.append(m[0])
-                ls.append(l[0])
-                accs.append(acc[0])
-            m, l, acc = merge_states(np.array([ms]), np.array([ls]), np.array([accs]), scale)
-            off = None
-            if smooth:
-                off = np.array([scale * (q[b, h, 0].astype(F64) @ prep["k_mean"][b, h // G].astype(F64))])
-            o, lse = _finalize(m, l, acc, prep["s_v"], scale, off, out_f64)
-            O[b, h] = o[0]
-            LSE[b, h] = lse[0]
+    sel = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else [tuple(x) for x in heads]
+    O = np.empty((len(sel), D), dtype=F64 if out_f64 else F32)
+    LSE = np.empty(len(sel))
+    cache = {}
+    for i, (b, h) in enumerate(sel):
+        hk = h // G
+        if (b, hk) not in cache:
+            cache.clear()
+            cache[(b, hk)] = (ops.k(b, hk), ops.v(b, hk))
+        kt, vt = cache[(b, hk)]
+        qt = ops.q(b, h, np.array([0]))
+        delta = ops.delta(b, h)
+        ms, ls, accs = [], [], []
+        for (p0, p1) in parts:
+            if p1 <= p0:
+                ms.append(-np.inf)
+                ls.append(0.0)
+                accs.append(np.zeros(D))
+                continue
+            m, l, acc = attn_state(qt, np.array([-1]), kt, vt, delta, p0, p1, scale, ops.quant_p)
+            ms.append(m[0])
+            ls.append(l[0])
+            accs.append(acc[0])
+        m, l, acc = merge_states(np.array([ms]), np.array([ls]), np.array([accs]), scale)
+        off = None
+        if smooth:
+            off = np.array([scale * (q[b, h, 0].astype(F64) @ ops.k_mean[b, hk].astype(F64))])
+        o, lse = _finalize(m, l, acc, ops.s_v, scale, off, out_f64)
+        O[i] = o[0]
+        LSE[i] = lse[0]
+    if heads is None:
+        return O.reshape(B, Hq, D), LSE.reshape(B, Hq)
     return O, LSE
 
 

@@ -32,20 +32,26 @@ def _run_prefill(mpfa, q, k, v, scale, causal, smooth, in_dtype, out_dtype, with
     return host(out), (host(lse) if with_lse else None)
 
 
-def _check_prefill(mpfa, oracle_mod, cfg, causal=True, smooth=True, out_bf16=False):
+def _check_prefill(mpfa, oracle_mod, cfg, causal=True, smooth=True, out_bf16=False, edit=None):
+    """Prefill of the configuration's inputs (``edit`` may replace q, k, v)
+    against the oracle, every row."""
     import torch
+    from mixed_precision_flashattention_amd import synth
     in_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     out_dtype = torch.bfloat16 if out_bf16 else torch.float32
-    q, k, v = (__import__("mixed_precision_flashattention_amd.synth", fromlist=["full"]).full(cfg, t)
-               for t in ("q", "k", "v"))
+    q, k, v = (synth.full(cfg, t) for t in ("q", "k", "v"))
+    if edit is not None:
+        q, k, v = edit(q, k, v)
     say(f"case: prefill B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} {cfg.dtype} causal={causal} "
-        f"smooth={smooth} out={'bf16' if out_bf16 else 'f32'}")
+        f"smooth={smooth} out={'bf16' if out_bf16 else 'f32'}"
+        f"{' edited inputs' if edit is not None else ''}")
     out, lse = _run_prefill(mpfa, q, k, v, cfg.scale, causal, smooth, in_dtype, out_dtype)
     O, LSE, rows = oracle_mod.prefill_rows(q, k, v, cfg.scale, causal=causal, smooth=smooth)
     # bf16 output adds one rounding (relative 2^-9) on top of the tolerance
     extra = 2.0 ** -8 if out_bf16 else 0.0
     assert_close("out", out.reshape(-1, 128), O, rtol=1e-2 + extra)
     assert_close("lse", lse.reshape(-1), LSE, atol=LSE_ATOL, rtol=0.0)
+    return out, O
 
 
 def test_prefill_small_config_full_smooth(mpfa, oracle_mod):
@@ -77,12 +83,17 @@ def test_prefill_non_causal(mpfa, oracle_mod, smooth):
                    causal=False, smooth=smooth)
 
 
-def _check_decode(mpfa, oracle_mod, cfg, smooth=True, with_lse=True):
+def _check_decode(mpfa, oracle_mod, cfg, smooth=True, with_lse=True, edit=None):
+    """Split-KV decode of the configuration's inputs (``edit`` may replace
+    q, k, v) against the oracle, every (batch, head)."""
     import torch
     from mixed_precision_flashattention_amd import synth
     q, k, v = synth.full(cfg, "q"), synth.full(cfg, "k"), synth.full(cfg, "v")
+    if edit is not None:
+        q, k, v = edit(q, k, v)
     qm = synth.q_mean(cfg)
-    say(f"case: decode B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} splits{cfg.num_splits} smooth={smooth}")
+    say(f"case: decode B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} splits{cfg.num_splits} smooth={smooth}"
+        f"{' edited inputs' if edit is not None else ''}")
     kd = dev(k, torch.bfloat16)
     kq = mpfa.quantize_k(kd, q_mean=dev(qm)) if smooth else mpfa.quantize_k(kd, smooth=False)
     vq = mpfa.quantize_v(dev(v, torch.bfloat16))
@@ -93,6 +104,7 @@ def _check_decode(mpfa, oracle_mod, cfg, smooth=True, with_lse=True):
     assert_close("out", host(out).reshape(-1, 128), O.reshape(-1, 128))
     if with_lse:
         assert_close("lse", host(lse).reshape(-1), LSE.reshape(-1), atol=LSE_ATOL, rtol=0.0)
+    return host(out), O
 
 
 @pytest.mark.parametrize("N,splits", [(1000, 3), (4096, 8), (1, 4), (300, 32), (129, 1)])
@@ -113,3 +125,40 @@ def test_decode_gqa8(mpfa, oracle_mod):
     from mixed_precision_flashattention_amd import synth
     _check_decode(mpfa, oracle_mod,
                   synth.config("llama8b_decode_128k", B=1, Hq=16, Hkv=2, N=777, num_splits=2))
+
+
+# ---- degenerate inputs: a global amax or a centered tensor that is exactly 0 --
+def _zero_k(q, k, v):
+    return q, np.zeros_like(k), v
+
+
+def _same_key(q, k, v):
+    """Every token of a KV head carries the same key: centered K is (nearly) 0."""
+    return q, np.ascontiguousarray(np.broadcast_to(k[:, :, :1, :], k.shape)), v
+
+
+def _zero_v(q, k, v):
+    return q, k, np.zeros_like(v)
+
+
+def _zero_q(q, k, v):
+    return np.zeros_like(q), k, v
+
+
+@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q], ids=lambda f: f.__name__)
+@pytest.mark.parametrize("smooth", [True, False])
+def test_prefill_degenerate_inputs(mpfa, oracle_mod, edit, smooth):
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("llama8b_prefill_16k", B=1, Hq=4, Hkv=2, N=200)
+    out, O = _check_prefill(mpfa, oracle_mod, cfg, smooth=smooth, edit=edit)
+    if edit is _zero_v:
+        assert not np.any(out), "zero V must give a zero output"
+
+
+@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q], ids=lambda f: f.__name__)
+def test_decode_degenerate_inputs(mpfa, oracle_mod, edit):
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("llama8b_decode_128k", B=2, Hq=8, Hkv=2, N=700, num_splits=4)
+    out, O = _check_decode(mpfa, oracle_mod, cfg, edit=edit)
+    if edit is _zero_v:
+        assert not np.any(out), "zero V must give a zero output"
