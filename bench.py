@@ -231,7 +231,8 @@ def profile_only(args, mpfa, synth, dev):
         kq = mpfa.quantize_k(x["k"], q=x["q"])
         vq = mpfa.quantize_v(x["v"])
         out = torch.empty(x["q"].shape, dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(256, dtype=torch.uint8, device=dev)
+        ws = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, cfg.B, cfg.Hq, cfg.Hkv, cfg.N),
+                         dtype=torch.uint8, device=dev)
         for _ in range(3):
             mpfa.prefill(x["q"], kq, vq, cfg.scale, causal=True, out=out, ws=ws)
     else:
@@ -301,7 +302,8 @@ def main():
     ws_k = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_QUANTIZE_K, B, Hq, Hkv, N),
                        dtype=torch.uint8, device=dev)
     ws_v = torch.empty(256, dtype=torch.uint8, device=dev)
-    ws_p = torch.empty(256, dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, B, Hq, Hkv, N),
+                       dtype=torch.uint8, device=dev)
 
     def stage1():
         mpfa.mpfa_quantize_k_nvfp4(k, q, kq["q_mean"], kq["k_mean"], kq["k_fp4"], kq["k_sf"],

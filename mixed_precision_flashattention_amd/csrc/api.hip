@@ -44,6 +44,19 @@ inline DecodeWs decode_layout(int B, int Hq, int P) {
   return w;
 }
 
+// Prefill: the Q amax word, then K~ (the K cache expanded to FP16,
+// [B, Hkv, N, 128] halves).
+struct PrefillWs {
+  size_t amax, k_f16, total;
+};
+inline PrefillWs prefill_layout(int B, int Hkv, int N) {
+  PrefillWs w;
+  w.amax = 0;
+  w.k_f16 = kAlign;
+  w.total = align_up(w.k_f16 + (size_t)B * Hkv * N * kD * 2);
+  return w;
+}
+
 inline int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MPFA_OK : MPFA_ERR_LAUNCH;
@@ -74,8 +87,9 @@ size_t mpfa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int nu
     case MPFA_OP_QUANTIZE_K:
       return quant_k_layout(B, Hq > 0 ? Hq : 0, Hkv).total;
     case MPFA_OP_QUANTIZE_V:
-    case MPFA_OP_PREFILL:
       return kAlign;
+    case MPFA_OP_PREFILL:
+      return prefill_layout(B, Hkv, N).total;
     case MPFA_OP_DECODE:
       if (num_splits < 1 || Hq < 1) return 0;
       return decode_layout(B, Hq, num_splits).total;
@@ -175,14 +189,17 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
                   !aligned16(delta_s)))
     return MPFA_ERR_INVALID;
   if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
-  if (ws_bytes < kAlign) return MPFA_ERR_WORKSPACE;
+  const PrefillWs L = prefill_layout(B, Hkv, N);
+  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
   const int n_qtiles = (N + 127) / 128;
   if ((int64_t)n_qtiles * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
 
   hipStream_t s = (hipStream_t)stream;
-  uint32_t* amax = (uint32_t*)ws;
+  uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
+  uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
   launch_fill_u32(amax, kAlign / 4, 0u, s);
   launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, delta_s ? q_mean : nullptr, amax, s);
+  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv * N, k_f16, s);
   PrefillParams p;
   p.q = q;
   p.q_bf16 = q_dtype == MPFA_BF16;
@@ -193,8 +210,7 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.G = Hq / Hkv;
   p.q_mean = delta_s ? q_mean : nullptr;
   p.k_mean = delta_s ? k_mean : nullptr;
-  p.k_fp4 = k_fp4;
-  p.k_sf = k_sf;
+  p.k_f16 = k_f16;
   p.k_gscale = k_gscale;
   p.v_fp8 = v_fp8;
   p.v_scale = v_scale;

@@ -11,8 +11,7 @@ struct PrefillParams {
   int B, Hq, Hkv, N, G;
   const float* q_mean;  // smoothing only
   const float* k_mean;  // smoothing only (LSE offset)
-  const uint8_t* k_fp4;
-  const uint8_t* k_sf;
+  const uint8_t* k_f16;  // K~ expanded to FP16 by the pre-pass, [B, Hkv, N, 128]
   const float* k_gscale;
   const uint8_t* v_fp8;
   const float* v_scale;
@@ -63,6 +62,8 @@ void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const ui
                              float* vscale, uint8_t* out, hipStream_t st);
 
 // prefill.hip
+void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, uint8_t* k_f16,
+                     hipStream_t st);
 void launch_prefill(const PrefillParams& p, hipStream_t st);
 
 // decode.hip

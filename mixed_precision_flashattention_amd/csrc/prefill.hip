@@ -1,13 +1,18 @@
 // Causal / full QK4PV8 prefill for gfx950 (paper "MpFA: ...", section 5.1
 // "second stage", section 5.2 "MMA Compensation", section 4.1).
 //
+// A pre-pass expands the NVFP4 K cache once per call into exact FP16
+// operands K~ = E2M1 code value x E4M3 block scale (at most 6 significant
+// bits, range [2^-10, 2688]: exact in FP16; the per-tensor global scale stays
+// out and is folded into the exp2 constant).
+//
 // Work unit: one (batch, query head, 128-row query tile); 4 waves of 32 rows;
-// two workgroups share a CU (<= 256 VGPRs per wave), so one workgroup's
+// two workgroups share a CU (<= 256 registers per wave), so one workgroup's
 // softmax overlaps the other's matrix products.  Per 128-key block:
-//   * the workgroup expands the NVFP4 K block into exact FP16 operands
-//     (code value x E4M3 block scale) in LDS and copies the FP8 V tiles and
-//     the block's Delta_S into LDS; the global loads of block j+1 are issued
-//     before block j is computed;
+//   * K~ rows, the FP8 V tiles and Delta_S reach LDS by direct global->LDS
+//     loads (no registers, no VALU); V is double-buffered and loaded one
+//     block ahead, K~ is loaded as soon as every wave has finished its score
+//     products of the previous block;
 //   * each wave computes S^T (keys x its 32 queries) on MFMA: with
 //     smoothing, a first bf16 step writes Delta_S * (1 / (gQ gK)) into the
 //     accumulator (the rank-one term of section 5.2 -- no element-wise add on
@@ -28,32 +33,103 @@
 namespace mpfa {
 
 constexpr int kQTile = 128;
-constexpr int kQStride = 272;  // bytes per LDS row of the prologue's Q~ (128 f16 + padding)
+constexpr int kRowBytes = 256;  // one K~ or Q~ row in LDS: 128 f16
 // K~ in LDS: 256-byte rows whose 16 chunks of 16 bytes are permuted by key:
 // chunk c of key k sits at c ^ kswz(k).  A 16-lane pass of an operand read
 // touches keys {0-3, 32-35, 4-7, 36-39} + base of one chunk column, and
 // kswz gives those keys 16 distinct chunk slots, so no two lanes of a pass
-// share a bank; the expansion writes (keys 0-7, both halves) spread too.
+// share a bank.
 __device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+// Q~ staging rows use chunk c ^ (row & 15): the operand read (16 rows, one
+// chunk column) and the quantizer's writes (8 rows x 8 chunk pairs) are both
+// spread over all 16 chunk slots.
+__device__ __forceinline__ int qswz(int r) { return r & 15; }
 // V in LDS: [4 tiles][2 halves][128 channels][16 bytes]: each lane's two
 // 16-byte reads are then contiguous across lanes (no bank conflicts).
 constexpr int kVTileBytes = kD * 32;
+constexpr int kVBlockBytes = 4 * kVTileBytes;
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_addr + 16 i (lds_addr wave-uniform).  Written as inline assembly so the
+// compiler's wait-count pass does not treat every later LDS read as
+// dependent on it; the kernel waits for these loads itself before the
+// barrier that publishes a block.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// This wave's share (8 KB: rows 32 w .. 32 w + 31) of K~ block k0.  Rows past
+// the end repeat the last key; those keys are masked out of the block.
+__device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0, uint32_t smem_k,
+                                              int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int piece = 8 * wave + i;  // 1 KB = rows 4 piece .. 4 piece + 3
+    const int r = 4 * piece + (lane >> 4);
+    const int chunk = (lane & 15) ^ kswz(r);  // the chunk that belongs in slot lane & 15
+    const int key = min(k0 + r, N - 1);
+    lds_load16(ktil + (int64_t)key * kRowBytes + 16 * chunk, smem_k + piece * 1024);
+  }
+}
+
+// This wave's share (4 KB) of V block k0: pieces (tile, half, 64 channels).
+__device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32, int k0,
+                                              uint32_t dst, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int piece = 4 * wave + i;
+    const int t = piece >> 2, half = (piece >> 1) & 1, ch0 = 64 * (piece & 1);
+    const int tt = min(k0 / 32 + t, ntiles32 - 1);
+    lds_load16(vbase + (int64_t)tt * kVTileBytes + (ch0 + lane) * 32 + half * 16,
+               dst + t * kVTileBytes + half * (kD * 16) + ch0 * 16);
+  }
+}
+
+// Workgroup -> (query tile, batch, query head).  Workgroups are dealt to the
+// 8 XCDs round-robin; when the KV heads split evenly, XCD x takes KV heads
+// x, x + 8, ... with all their query heads and tiles, so one L2 serves each
+// KV head, and inside an XCD the heaviest (last) query tiles go first
+// (longest-processing-time order, paper section 5.1).  Otherwise the order
+// is the plain LPT one over all heads.
+__device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, int& tile, int& b,
+                                             int& hq) {
+  const int nkv = p.B * p.Hkv;
+  if ((nkv & 7) == 0) {
+    const int x = wid & 7, slot = wid >> 3;
+    const int per_tile = (nkv >> 3) * p.G;
+    tile = p.n_qtiles - 1 - slot / per_tile;
+    const int r = slot % per_tile;
+    const int g = x + 8 * (r / p.G);
+    b = g / p.Hkv;
+    hq = (g % p.Hkv) * p.G + r % p.G;
+  } else {
+    const int nbh = p.B * p.Hq;
+    tile = p.n_qtiles - 1 - wid / nbh;
+    const int bh = wid % nbh;
+    b = bh / p.Hq;
+    hq = bh % p.Hq;
+  }
+}
 
 template <bool SMOOTH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
-  __shared__ __align__(16) uint8_t smem_k[kQTile * kQStride];  // K~ block (Q~ in the prologue)
-  __shared__ __align__(16) uint8_t smem_v[4 * kVTileBytes];    // V block
+  __shared__ __align__(16) uint8_t smem_k[kQTile * kRowBytes];  // K~ block (Q~ in the prologue)
+  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];     // V blocks j and j + 1
   __shared__ uint16_t smem_delta[kBlk];
 
   const int N = p.N;
-  const int nbh = p.B * p.Hq;
-  const int wid = blockIdx.x;
-  const int tile = p.n_qtiles - 1 - wid / nbh;  // heaviest (last) query tiles first
-  const int bh = wid % nbh;
-  const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / p.G;
+  int tile, b, hq;
+  prefill_unit(p, blockIdx.x, tile, b, hq);
+  const int bh = b * p.Hq + hq, hk = hq / p.G;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int row0 = tile * kQTile;
 
@@ -64,7 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float lam = p.scale * kLog2e * gg;  // exp2 constant per unit of the MFMA score
 
   // ---- prologue: NVFP4 of the query tile, expanded to FP16 in LDS --------
-  float* lse_part = reinterpret_cast<float*>(smem_v);  // [128 rows][8 blocks]
+  float* lse_part = reinterpret_cast<float*>(smem_v[1]);  // [128 rows][8 blocks]
   for (int u = tid; u < kQTile * 8; u += 256) {
     const int r = u >> 3, blk = u & 7;
     const int qrow = row0 + r;
@@ -93,9 +169,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         packed[j] = __builtin_bit_cast(uint32_t, v2);
       }
     }
-    uint4* dst = reinterpret_cast<uint4*>(smem_k + r * kQStride + blk * 32);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    uint4* dst = reinterpret_cast<uint4*>(smem_k + r * kRowBytes);
+    dst[(2 * blk) ^ qswz(r)] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[(2 * blk + 1) ^ qswz(r)] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
     lse_part[r * 8 + blk] = part;
   }
   __syncthreads();
@@ -106,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   i32x4 qf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = *reinterpret_cast<const i32x4*>(smem_k + qr * kQStride + (64 * h + 8 * kc) * 2);
+    qf[kc] = *reinterpret_cast<const i32x4*>(smem_k + qr * kRowBytes + 16 * ((8 * h + kc) ^ qswz(qr)));
   float lse_off = 0.0f;
   if (SMOOTH && p.lse) {
 #pragma unroll
@@ -131,10 +207,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nblk = p.causal ? min(tile + 1, nblk_all) : nblk_all;
   const int ntiles32 = (N + 31) / 32;
   const int64_t kvh = (int64_t)b * p.Hkv + hk;
-  const uint8_t* kbase = p.k_fp4 + kvh * N * 64;
-  const uint8_t* sbase = p.k_sf + kvh * N * 8;
+  const uint8_t* ktil = p.k_f16 + kvh * N * kRowBytes;
   const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * kVTileBytes;
   const uint16_t* dbase = SMOOTH ? p.delta_s + (int64_t)bh * N : nullptr;
+  const uint32_t lds_k = lds_addr(smem_k);
+  const uint32_t lds_v0 = lds_addr(smem_v[0]), lds_v1 = lds_addr(smem_v[1]);
 
   // A-row rho of score tile t holds key 64*(t/2) + 32*hp + 16*(t%2) + vp of
   // the block (hp, vp from rho below); the MFMA output register v of lane
@@ -146,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int t = 0; t < 4; ++t) {
     koff[t] = 64 * (t >> 1) + 32 * hp + 16 * (t & 1) + vp;
     ksw[t] = kswz(koff[t]);
-    krow[t] = smem_k + koff[t] * 256;
+    krow[t] = smem_k + koff[t] * kRowBytes;
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -154,57 +231,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  // Per-thread share of a block's loads: K codes of (key, head-dim half),
-  // 16 bytes of each of the 4 V tiles, one Delta_S entry.  Indices past the end
-  // are clamped to the last token: those keys are masked out of the block,
-  // so the (finite) values read there never reach the result.
-  const int ld_key = tid >> 1, ld_half = tid & 1;
-  // V: thread tid moves 16-byte unit (channel tid % 128, half tid / 128) of
-  // each tile, global unit 2 * channel + half, so its LDS stores are
-  // contiguous across lanes.
-  const int vsrc = 2 * (tid & 127) + (tid >> 7);
-  uint4 kc0, kc1, vv0, vv1, vv2, vv3;
-  uint32_t ksc, dd = 0;
-#define MPFA_PREFILL_LOAD(JB)                                                                 \
-  do {                                                                                        \
-    const int kb0 = (JB) * kBlk;                                                              \
-    const int gk = min(kb0 + ld_key, N - 1);                                                  \
-    const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)gk * 64 + 32 * ld_half); \
-    kc0 = src[0];                                                                             \
-    kc1 = src[1];                                                                             \
-    ksc = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)gk * 8 + 4 * ld_half);          \
-    const int tt0 = kb0 / 32;                                                                 \
-    vv0 = reinterpret_cast<const uint4*>(vbase + (int64_t)min(tt0 + 0, ntiles32 - 1) * kVTileBytes)[vsrc]; \
-    vv1 = reinterpret_cast<const uint4*>(vbase + (int64_t)min(tt0 + 1, ntiles32 - 1) * kVTileBytes)[vsrc]; \
-    vv2 = reinterpret_cast<const uint4*>(vbase + (int64_t)min(tt0 + 2, ntiles32 - 1) * kVTileBytes)[vsrc]; \
-    vv3 = reinterpret_cast<const uint4*>(vbase + (int64_t)min(tt0 + 3, ntiles32 - 1) * kVTileBytes)[vsrc]; \
-    if (SMOOTH && tid < kBlk) dd = dbase[min(kb0 + tid, N - 1)];                              \
-  } while (0)
-  MPFA_PREFILL_LOAD(0);
+  __syncthreads();  // Q~ and the LSE parts are consumed: LDS is free for the blocks
+  issue_v_block(vbase, ntiles32, 0, lds_v0, wave, lane);
+  issue_k_block(ktil, N, 0, lds_k, wave, lane);
+  uint32_t dd = 0;
+  if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 
   for (int j = 0; j < nblk; ++j) {
     const int k0 = j * kBlk;
-    __syncthreads();  // every wave is done with the previous block's LDS tiles
-    {
-      const uint32_t w[8] = {kc0.x, kc0.y, kc0.z, kc0.w, kc1.x, kc1.y, kc1.z, kc1.w};
-      uint8_t* dst = smem_k + ld_key * 256;
-      const int sw = kswz(ld_key);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t e[4];
-        expand_fp4x8(w[i], e4m3_scale_f16x2((ksc >> (8 * (i >> 1))) & 0xFFu), e);
-        *reinterpret_cast<uint4*>(dst + 16 * ((8 * ld_half + i) ^ sw)) =
-            make_uint4(e[0], e[1], e[2], e[3]);
-      }
-      const int voff = tid * 16;  // = half * 2048 + channel * 16
-      *reinterpret_cast<uint4*>(smem_v + 0 * kVTileBytes + voff) = vv0;
-      *reinterpret_cast<uint4*>(smem_v + 1 * kVTileBytes + voff) = vv1;
-      *reinterpret_cast<uint4*>(smem_v + 2 * kVTileBytes + voff) = vv2;
-      *reinterpret_cast<uint4*>(smem_v + 3 * kVTileBytes + voff) = vv3;
-      if (SMOOTH && tid < kBlk) smem_delta[tid] = (uint16_t)dd;
+    wait_direct_loads();  // this wave's part of block j has landed
+    if (SMOOTH && tid < kBlk) smem_delta[tid] = (uint16_t)dd;
+    __syncthreads();  // block j is visible to every wave; V buffer (j+1)&1 is free
+    if (j + 1 < nblk) {
+      issue_v_block(vbase, ntiles32, k0 + kBlk, (j & 1) ? lds_v0 : lds_v1, wave, lane);
+      if (SMOOTH && tid < kBlk) dd = dbase[min(k0 + kBlk + tid, N - 1)];
     }
-    __syncthreads();
-    if (j + 1 < nblk) MPFA_PREFILL_LOAD(j + 1);
 
     // ---- scores S^T: 4 tiles of 32 keys x 32 queries --------------------
     f32x16 s[4];
@@ -227,6 +268,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int t = 0; t < 4; ++t)
         s[t] = mfma32_f16(
             *reinterpret_cast<const i32x4*>(krow[t] + 16 * ((8 * h + kc) ^ ksw[t])), qf[kc], s[t]);
+
+    __syncthreads();  // every wave is done with K~ and Delta_S of block j
+    if (j + 1 < nblk) issue_k_block(ktil, N, k0 + kBlk, lds_k, wave, lane);
 
     // ---- mask (diagonal or ragged block only) and online softmax --------
     const bool need_mask = (p.causal && k0 + kBlk > row0) || (k0 + kBlk > N);
@@ -275,9 +319,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
+    const uint8_t* vblk = smem_v[j & 1];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint8_t* vt = smem_v + (2 * c + h) * kVTileBytes + col * 16;
+      const uint8_t* vt = vblk + (2 * c + h) * kVTileBytes + col * 16;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const i32x4 lo = *reinterpret_cast<const i32x4*>(vt + dt * 512);
@@ -321,7 +366,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         kLn2 * (lam * m_run + log2f(l_tot)) - kLn2 * kLog2_448 + lse_off;
 }
 
-#undef MPFA_PREFILL_LOAD
+// K~ = E2M1 code value x E4M3 block scale in FP16, row-major [rows][128]:
+// one thread per 16-element block (8 code bytes, one scale byte -> 32 bytes).
+__global__ __launch_bounds__(256) void k_expand_k(const uint2* __restrict__ codes,
+                                                  const uint8_t* __restrict__ sf,
+                                                  int64_t n_blocks, uint4* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n_blocks) return;
+  const uint2 w = codes[g];
+  const f16x2 s2 = e4m3_scale_f16x2(sf[g]);
+  uint32_t e[8];
+  expand_fp4x8(w.x, s2, e);
+  expand_fp4x8(w.y, s2, e + 4);
+  out[2 * g] = make_uint4(e[0], e[1], e[2], e[3]);
+  out[2 * g + 1] = make_uint4(e[4], e[5], e[6], e[7]);
+}
+
+void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, uint8_t* k_f16,
+                     hipStream_t st) {
+  const int64_t n_blocks = rows * (kD / 16);
+  hipLaunchKernelGGL(k_expand_k, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint2*>(k_fp4), k_sf, n_blocks,
+                     reinterpret_cast<uint4*>(k_f16));
+}
 
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.n_qtiles * p.B * p.Hq);
