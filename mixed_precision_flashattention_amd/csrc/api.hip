@@ -191,8 +191,8 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
   const PrefillWs L = prefill_layout(B, Hkv, N);
   if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
-  const int n_qtiles = (N + 127) / 128;
-  if ((int64_t)n_qtiles * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+  const int n_units = (N + 255) / 256;
+  if ((int64_t)n_units * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
@@ -221,7 +221,7 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.out_bf16 = out_dtype == MPFA_BF16;
   p.lse = lse;
   p.q_amax = amax;
-  p.n_qtiles = n_qtiles;
+  p.n_units = n_units;
   launch_prefill(p, s);
   return launch_status();
 }

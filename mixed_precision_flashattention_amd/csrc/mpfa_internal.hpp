@@ -22,7 +22,7 @@ struct PrefillParams {
   int out_bf16;
   float* lse;
   const uint32_t* q_amax;  // amax of Q_c, computed by the pre-pass
-  int n_qtiles;
+  int n_units;             // 256-row query units per (batch, head)
 };
 
 struct DecodeParams {

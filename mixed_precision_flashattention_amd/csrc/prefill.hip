@@ -32,7 +32,7 @@
 
 namespace mpfa {
 
-constexpr int kQTile = 128;
+constexpr int kUnitRows = 256;  // query rows per workgroup (two groups of 128)
 constexpr int kRowBytes = 256;  // one K~ or Q~ row in LDS: 128 f16
 // K~ in LDS: 256-byte rows whose 16 chunks of 16 bytes are permuted by key:
 // chunk c of key k sits at c ^ kswz(k).  A 16-lane pass of an operand read
@@ -63,26 +63,26 @@ __device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_addr) {
 __device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// This wave's share (8 KB: rows 32 w .. 32 w + 31) of K~ block k0.  Rows past
-// the end repeat the last key; those keys are masked out of the block.
-__device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0, uint32_t smem_k,
+// This wave's share (4 KB of 32) of K~ block k0.  Rows past the end repeat
+// the last key; those keys are masked out of the block.
+__device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0, uint32_t dst,
                                               int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int piece = 8 * wave + i;  // 1 KB = rows 4 piece .. 4 piece + 3
+  for (int i = 0; i < 4; ++i) {
+    const int piece = 4 * wave + i;  // 1 KB = rows 4 piece .. 4 piece + 3
     const int r = 4 * piece + (lane >> 4);
     const int chunk = (lane & 15) ^ kswz(r);  // the chunk that belongs in slot lane & 15
     const int key = min(k0 + r, N - 1);
-    lds_load16(ktil + (int64_t)key * kRowBytes + 16 * chunk, smem_k + piece * 1024);
+    lds_load16(ktil + (int64_t)key * kRowBytes + 16 * chunk, dst + piece * 1024);
   }
 }
 
-// This wave's share (4 KB) of V block k0: pieces (tile, half, 64 channels).
+// This wave's share (2 KB of 16) of V block k0: pieces (tile, half, 64 channels).
 __device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32, int k0,
                                               uint32_t dst, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int piece = 4 * wave + i;
+  for (int i = 0; i < 2; ++i) {
+    const int piece = 2 * wave + i;
     const int t = piece >> 2, half = (piece >> 1) & 1, ch0 = 64 * (piece & 1);
     const int tt = min(k0 / 32 + t, ntiles32 - 1);
     lds_load16(vbase + (int64_t)tt * kVTileBytes + (ch0 + lane) * 32 + half * 16,
@@ -90,48 +90,179 @@ __device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32
   }
 }
 
-// Workgroup -> (query tile, batch, query head).  Workgroups are dealt to the
-// 8 XCDs round-robin; when the KV heads split evenly, XCD x takes KV heads
-// x, x + 8, ... with all their query heads and tiles, so one L2 serves each
-// KV head, and inside an XCD the heaviest (last) query tiles go first
+// Workgroup -> (256-row query unit, batch, query head).  Workgroups are dealt
+// to the 8 XCDs round-robin; when the KV heads split evenly, XCD x takes KV
+// heads x, x + 8, ... with all their query heads and units, so one L2 serves
+// each KV head, and inside an XCD the heaviest (last) units go first
 // (longest-processing-time order, paper section 5.1).  Otherwise the order
 // is the plain LPT one over all heads.
-__device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, int& tile, int& b,
+__device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, int& unit, int& b,
                                              int& hq) {
   const int nkv = p.B * p.Hkv;
   if ((nkv & 7) == 0) {
     const int x = wid & 7, slot = wid >> 3;
-    const int per_tile = (nkv >> 3) * p.G;
-    tile = p.n_qtiles - 1 - slot / per_tile;
-    const int r = slot % per_tile;
+    const int per_unit = (nkv >> 3) * p.G;
+    unit = p.n_units - 1 - slot / per_unit;
+    const int r = slot % per_unit;
     const int g = x + 8 * (r / p.G);
     b = g / p.Hkv;
     hq = (g % p.Hkv) * p.G + r % p.G;
   } else {
     const int nbh = p.B * p.Hq;
-    tile = p.n_qtiles - 1 - wid / nbh;
+    unit = p.n_units - 1 - wid / nbh;
     const int bh = wid % nbh;
     b = bh / p.Hq;
     hq = bh % p.Hq;
   }
 }
 
+// Scores S^T of one 128-key block: 4 tiles of 32 keys x the wave's 32 queries.
+// The K~ operands of head-dim step kc + 1 are read from LDS while the four
+// MFMAs of step kc run (the scheduling barriers keep the reads that early),
+// so the matrix core does not wait on LDS latency.
 template <bool SMOOTH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
+__device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
+                                            const uint16_t* dblk, const int (&koff)[4],
+                                            const int (&ksw)[4], const i32x4 (&qf)[8],
+                                            const i32x4& dB, int h) {
+  i32x4 a[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    a[0][t] = *reinterpret_cast<const i32x4*>(kblk + koff[t] * kRowBytes + 16 * ((8 * h) ^ ksw[t]));
+  if (SMOOTH) {
+    uint32_t dv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dv[t] = dblk[koff[t]];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const i32x4 dA = {h == 0 ? (int)(dv[t] | (dv[t] << 16)) : 0, h == 0 ? (int)dv[t] : 0, 0, 0};
+      s[t] = mfma32_bf16(dA, dB, f32x16{});
+    }
+  }
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    if (kc + 1 < 8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        a[(kc + 1) & 1][t] = *reinterpret_cast<const i32x4*>(kblk + koff[t] * kRowBytes +
+                                                            16 * ((8 * h + kc + 1) ^ ksw[t]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      s[t] = (SMOOTH || kc > 0) ? mfma32_f16(a[kc & 1][t], qf[kc], s[t])
+                                : mfma32_f16(a[kc & 1][t], qf[kc], f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// O^T += V^T P^T for one block on the FP8 MFMA (8 MFMAs: key half c, head-dim
+// tile dt); the V operand of MFMA i + 1 is read while MFMA i runs.
+__device__ __forceinline__ i32x8 v_operand(const uint8_t* vblk, int i, int h, int col) {
+  const int c = i >> 2, dt = i & 3;
+  const uint8_t* vt = vblk + (2 * c + h) * kVTileBytes + col * 16 + dt * 512;
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(vt);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(vt + kD * 16);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ void pv_block(f32x16 (&o)[4], const uint8_t* vblk, const i32x8 (&pb)[2],
+                                         int h, int col) {
+  i32x8 va[2];
+  va[0] = v_operand(vblk, 0, h, col);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 1 < 8) va[(i + 1) & 1] = v_operand(vblk, i + 1, h, col);
+    __builtin_amdgcn_sched_barrier(0);
+    o[i & 3] = mfma32_fp8(va[i & 1], pb[i >> 2], o[i & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Reductions over the lane pair (l, l ^ 32) by one register swap of the lane
+// halves: afterwards the first register holds the low lane's value and the
+// second the high lane's, in both lanes, so both get the same result.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Mask, online softmax and E4M3 rounding of P for one block; rescales the
+// output accumulators when a row max moved.
+__device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i32x8 (&pb)[2],
+                                              float& m_run, float& l_run, float lam, bool mask,
+                                              int k0, int lim, int h) {
+  if (mask) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 64 * (t >> 1) + 32 * h + 16 * (t & 1) + v;
+        s[t][v] = key <= lim ? s[t][v] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
+  mx = max_halves(mx);
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = fast_exp2(lam * (m_run - m_new));
+  const float nb = kLog2_448 - lam * m_new;
+  m_run = m_new;
+
+  float lsum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = 2 * c + (k >> 2), v0 = 4 * (k & 3);
+      const float e0 = fast_exp2(fmaf(s[t][v0], lam, nb));
+      const float e1 = fast_exp2(fmaf(s[t][v0 + 1], lam, nb));
+      const float e2 = fast_exp2(fmaf(s[t][v0 + 2], lam, nb));
+      const float e3 = fast_exp2(fmaf(s[t][v0 + 3], lam, nb));
+      lsum += (e0 + e1) + (e2 + e3);
+      uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
+      wd = cvt_fp8x2<true>(e2, e3, wd);
+      pb[c][k] = (int)wd;
+    }
+  }
+  l_run = fmaf(alpha, l_run, lsum);
+  if (!__all(alpha == 1.0f)) {  // a row max moved somewhere in this wave
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+  }
+}
+
+// Work unit: 256 query rows of one (batch, head) in two groups of 4 waves
+// (rows 0-127 and 128-255); each SIMD holds one wave of each group.  The
+// groups take turns: between two workgroup barriers one group runs its
+// matrix products (P.V of block j-1, then the scores of block j) while the
+// other runs the softmax of its previous block, so the matrix cores and the
+// vector ALUs of every SIMD are busy at the same time.  Both groups read
+// the same K~ / V / Delta_S blocks from LDS (double-buffered, loaded two
+// steps ahead by all 8 waves).
+template <bool SMOOTH>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
-  __shared__ __align__(16) uint8_t smem_k[kQTile * kRowBytes];  // K~ block (Q~ in the prologue)
-  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];     // V blocks j and j + 1
-  __shared__ uint16_t smem_delta[kBlk];
+  __shared__ __align__(16) uint8_t smem_k[2][kBlk * kRowBytes];  // K~ blocks (Q~ in the prologue)
+  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];      // V blocks
+  __shared__ uint16_t smem_delta[2][kBlk];
 
   const int N = p.N;
-  int tile, b, hq;
-  prefill_unit(p, blockIdx.x, tile, b, hq);
+  int unit, b, hq;
+  prefill_unit(p, blockIdx.x, unit, b, hq);
   const int bh = b * p.Hq + hq, hk = hq / p.G;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int grp = wave >> 2;                                   // row group
   const int h = lane >> 5, col = lane & 31;
-  const int row0 = tile * kQTile;
+  const int row0 = unit * kUnitRows;
 
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
   const float gK = *p.k_gscale;
@@ -139,9 +270,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;  // exp2 constant per unit of the MFMA score
 
-  // ---- prologue: NVFP4 of the query tile, expanded to FP16 in LDS --------
-  float* lse_part = reinterpret_cast<float*>(smem_v[1]);  // [128 rows][8 blocks]
-  for (int u = tid; u < kQTile * 8; u += 256) {
+  // ---- prologue: NVFP4 of the 256 query rows, expanded to FP16 in LDS ----
+  uint8_t* qstage = smem_k[0];                             // 256 rows x 256 bytes
+  float* lse_part = reinterpret_cast<float*>(smem_v[0]);  // [256 rows][8 blocks]
+  for (int u = tid; u < kUnitRows * 8; u += 512) {
     const int r = u >> 3, blk = u & 7;
     const int qrow = row0 + r;
     uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -169,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         packed[j] = __builtin_bit_cast(uint32_t, v2);
       }
     }
-    uint4* dst = reinterpret_cast<uint4*>(smem_k + r * kRowBytes);
+    uint4* dst = reinterpret_cast<uint4*>(qstage + r * kRowBytes);
     dst[(2 * blk) ^ qswz(r)] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[(2 * blk + 1) ^ qswz(r)] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
     lse_part[r * 8 + blk] = part;
@@ -182,7 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   i32x4 qf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = *reinterpret_cast<const i32x4*>(smem_k + qr * kRowBytes + 16 * ((8 * h + kc) ^ qswz(qr)));
+    qf[kc] = *reinterpret_cast<const i32x4*>(qstage + qr * kRowBytes + 16 * ((8 * h + kc) ^ qswz(qr)));
   float lse_off = 0.0f;
   if (SMOOTH && p.lse) {
 #pragma unroll
@@ -203,14 +335,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 
   const int my_row = row0 + qr;
+  const int grow0 = row0 + 128 * grp;  // first row of this wave's group
   const int nblk_all = (N + kBlk - 1) / kBlk;
-  const int nblk = p.causal ? min(tile + 1, nblk_all) : nblk_all;
+  // blocks per group (0 for a group past the end), and the loop length
+  const int n_a = p.causal ? min(2 * unit + 1, nblk_all) : nblk_all;
+  const int n_b = row0 + 128 < N ? (p.causal ? min(2 * unit + 2, nblk_all) : nblk_all) : 0;
+  const int n_own = grp ? n_b : n_a;
+  const int n_max = max(n_a, n_b);
+  const int lim = p.causal ? min(my_row, N - 1) : N - 1;  // last visible key of this row
   const int ntiles32 = (N + 31) / 32;
   const int64_t kvh = (int64_t)b * p.Hkv + hk;
   const uint8_t* ktil = p.k_f16 + kvh * N * kRowBytes;
   const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * kVTileBytes;
   const uint16_t* dbase = SMOOTH ? p.delta_s + (int64_t)bh * N : nullptr;
-  const uint32_t lds_k = lds_addr(smem_k);
+  const uint32_t lds_k0 = lds_addr(smem_k[0]), lds_k1 = lds_addr(smem_k[1]);
   const uint32_t lds_v0 = lds_addr(smem_v[0]), lds_v1 = lds_addr(smem_v[1]);
 
   // A-row rho of score tile t holds key 64*(t/2) + 32*hp + 16*(t%2) + vp of
@@ -218,127 +356,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // half h then holds key 64*(t/2) + 32*h + 16*(t%2) + v.
   const int hp = (col >> 2) & 1, vp = ((col >> 3) << 2) | (col & 3);
   int koff[4], ksw[4];
-  const uint8_t* krow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     koff[t] = 64 * (t >> 1) + 32 * hp + 16 * (t & 1) + vp;
     ksw[t] = kswz(koff[t]);
-    krow[t] = smem_k + koff[t] * kRowBytes;
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 o[4];
+  f32x16 o[4], s[4];
+  i32x8 pb[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
   __syncthreads();  // Q~ and the LSE parts are consumed: LDS is free for the blocks
-  issue_v_block(vbase, ntiles32, 0, lds_v0, wave, lane);
-  issue_k_block(ktil, N, 0, lds_k, wave, lane);
+  issue_k_block(ktil, N, 0, lds_k0, wave, lane);
   uint32_t dd = 0;
   if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 
-  for (int j = 0; j < nblk; ++j) {
-    const int k0 = j * kBlk;
-    wait_direct_loads();  // this wave's part of block j has landed
-    if (SMOOTH && tid < kBlk) smem_delta[tid] = (uint16_t)dd;
-    __syncthreads();  // block j is visible to every wave; V buffer (j+1)&1 is free
-    if (j + 1 < nblk) {
-      issue_v_block(vbase, ntiles32, k0 + kBlk, (j & 1) ? lds_v0 : lds_v1, wave, lane);
-      if (SMOOTH && tid < kBlk) dd = dbase[min(k0 + kBlk + tid, N - 1)];
+  // Steps alternate between the groups: in body j, group 0 runs its matrix
+  // phase (P.V of block j-1, scores of block j) in the first step and the
+  // softmax of block j in the second; group 1 runs the softmax of block j-1
+  // first and its matrix phase second.  The first step of body j publishes
+  // K~(j), Delta_S(j) and V(j-1) and starts the loads of K~(j+1),
+  // Delta_S(j+1) and V(j).  Both loops pass the same barriers.
+#define MPFA_STEP_OPEN(J)                                                                    \
+  do {                                                                                       \
+    wait_direct_loads(); /* this wave's loads of the previous body have landed */            \
+    if (SMOOTH && tid < kBlk) smem_delta[(J) & 1][tid] = (uint16_t)dd;                       \
+    __syncthreads();                                                                         \
+    if ((J) + 1 < n_max) {                                                                   \
+      issue_k_block(ktil, N, ((J) + 1) * kBlk, ((J) & 1) ? lds_k0 : lds_k1, wave, lane);     \
+      if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
+    }                                                                                        \
+    if ((J) < n_max) issue_v_block(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, \
+                                   wave, lane);                                              \
+  } while (0)
+#define MPFA_MATRIX(J)                                                                       \
+  do {                                                                                       \
+    if ((J) >= 1 && (J) <= n_own) pv_block(o, smem_v[((J) - 1) & 1], pb, h, col);           \
+    if ((J) < n_own) {                                                                       \
+      score_block<SMOOTH>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, ksw, qf, dB, h);    \
+    } else {                                                                                 \
+      /* defining s on this path too keeps the old scores from being live */                 \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \
+    }                                                                                        \
+  } while (0)
+#define MPFA_SOFTMAX(J)                                                                      \
+  do {                                                                                       \
+    if ((J) >= 0 && (J) < n_own) {                                                           \
+      const int k0 = (J) * kBlk;                                                             \
+      const bool mask = (p.causal && k0 + kBlk > grow0) || (k0 + kBlk > N);                 \
+      softmax_block(s, o, pb, m_run, l_run, lam, mask, k0, lim, h);                          \
+    } else {                                                                                 \
+      pb[0] = i32x8{}; /* as for s: keeps old P from being live */                           \
+      pb[1] = i32x8{};                                                                       \
+    }                                                                                        \
+  } while (0)
+  if (grp == 0) {
+    for (int j = 0; j <= n_max; ++j) {
+      MPFA_STEP_OPEN(j);
+      MPFA_MATRIX(j);
+      __syncthreads();
+      MPFA_SOFTMAX(j);
     }
-
-    // ---- scores S^T: 4 tiles of 32 keys x 32 queries --------------------
-    f32x16 s[4];
-    if (SMOOTH) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t dv = smem_delta[koff[t]];
-        const i32x4 dA = {h == 0 ? (int)(dv | (dv << 16)) : 0, h == 0 ? (int)dv : 0, 0, 0};
-        s[t] = mfma32_bf16(dA, dB, f32x16{});
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        s[t] = mfma32_f16(*reinterpret_cast<const i32x4*>(krow[t] + 16 * ((8 * h) ^ ksw[t])),
-                          qf[0], f32x16{});
-    }
-#pragma unroll
-    for (int kc = SMOOTH ? 0 : 1; kc < 8; ++kc)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        s[t] = mfma32_f16(
-            *reinterpret_cast<const i32x4*>(krow[t] + 16 * ((8 * h + kc) ^ ksw[t])), qf[kc], s[t]);
-
-    __syncthreads();  // every wave is done with K~ and Delta_S of block j
-    if (j + 1 < nblk) issue_k_block(ktil, N, k0 + kBlk, lds_k, wave, lane);
-
-    // ---- mask (diagonal or ragged block only) and online softmax --------
-    const bool need_mask = (p.causal && k0 + kBlk > row0) || (k0 + kBlk > N);
-    if (need_mask) {
-      const int lim = p.causal ? min(my_row, N - 1) : N - 1;  // last visible key
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + 64 * (t >> 1) + 32 * h + 16 * (t & 1) + v;
-          s[t][v] = key <= lim ? s[t][v] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(lam * (m_run - m_new));
-    const float nb = kLog2_448 - lam * m_new;
-    m_run = m_new;
-
-    float lsum = 0.0f;
-    i32x8 pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t = 2 * c + (k >> 2), v0 = 4 * (k & 3);
-        const float e0 = fast_exp2(fmaf(s[t][v0], lam, nb));
-        const float e1 = fast_exp2(fmaf(s[t][v0 + 1], lam, nb));
-        const float e2 = fast_exp2(fmaf(s[t][v0 + 2], lam, nb));
-        const float e3 = fast_exp2(fmaf(s[t][v0 + 3], lam, nb));
-        lsum += (e0 + e1) + (e2 + e3);
-        uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
-        wd = cvt_fp8x2<true>(e2, e3, wd);
-        pb[c][k] = (int)wd;
-      }
-    }
-    l_run = fmaf(alpha, l_run, lsum);
-
-    // ---- O^T = alpha O^T + V^T P^T on FP8 MFMA --------------------------
-    if (!__all(alpha == 1.0f)) {  // a row max moved somewhere in this wave
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    }
-    const uint8_t* vblk = smem_v[j & 1];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint8_t* vt = vblk + (2 * c + h) * kVTileBytes + col * 16;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(vt + dt * 512);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(vt + kD * 16 + dt * 512);
-        const i32x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[dt] = mfma32_fp8(va, pb[c], o[dt]);
-      }
+  } else {
+    for (int j = 0; j <= n_max; ++j) {
+      MPFA_STEP_OPEN(j);
+      MPFA_SOFTMAX(j - 1);
+      __syncthreads();
+      MPFA_MATRIX(j);
     }
   }
+#undef MPFA_STEP_OPEN
+#undef MPFA_MATRIX
+#undef MPFA_SOFTMAX
 
   // ---- epilogue -----------------------------------------------------------
   // An MFMA reads its operands from all 64 lanes whatever the execution mask,
   // while loads honour it; so nothing that feeds the accumulators may be moved
   // into a branch on the row.  Every lane normalises, only the stores of rows
   // past the end are skipped.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   const float inv = sV / l_tot;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] *= inv;
@@ -391,11 +489,11 @@ void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, ui
 }
 
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
-  const unsigned grid = (unsigned)((int64_t)p.n_qtiles * p.B * p.Hq);
+  const unsigned grid = (unsigned)((int64_t)p.n_units * p.B * p.Hq);
   if (p.delta_s)
-    hipLaunchKernelGGL(k_prefill<true>, dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_prefill<true>, dim3(grid), dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL(k_prefill<false>, dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_prefill<false>, dim3(grid), dim3(512), 0, st, p);
 }
 
 }  // namespace mpfa
