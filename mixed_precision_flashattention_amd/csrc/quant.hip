@@ -13,44 +13,106 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
-// Per (b, h, d): max over tokens of |x|.  Block: 256 threads = 2 token rows
-// x 128 channels; grid (token chunks, B*H).
-constexpr int kStatRows = 256;
+// Per-channel statistics over the tokens of each (batch, head) slice.  Grid
+// (row chunks, BH) with about 2048 blocks in all; block = 16 row lanes x 16
+// channel groups of 8 channels; each thread keeps 8 channel accumulators over
+// rows rl, rl + 16, ... of its chunk (four 16-byte loads in flight), the
+// block reduces its 16 row lanes in LDS and then updates the 128 channel
+// totals with one atomic each.
+__device__ __forceinline__ void load8(const void* p, int64_t i, int is_bf16, float* x) {
+  if (is_bf16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 a = s[0], b = s[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
 
-__global__ void k_channel_absmax(const void* __restrict__ x, int is_bf16, int N,
-                                 uint32_t* __restrict__ out) {
-  const int d = threadIdx.x & 127;
+constexpr int kStatBlocks = 2048;  // target number of blocks per statistics pass
+
+// Per (b, h, d): max over tokens of |x|.
+__global__ __launch_bounds__(256) void k_channel_absmax(const void* __restrict__ x, int is_bf16,
+                                                        int N, int rows_per_block,
+                                                        uint32_t* __restrict__ out) {
+  __shared__ float red[16][kD];
   const int64_t bh = blockIdx.y;
-  const int r_begin = blockIdx.x * kStatRows;
-  const int r_end = min(N, r_begin + kStatRows);
-  float m = 0.0f;
-  for (int r = r_begin + (threadIdx.x >> 7); r < r_end; r += 2)
-    m = fmaxf(m, fabsf(load_elem(x, (bh * N + r) * kD + d, is_bf16)));
-  atomic_max_nonneg(out + bh * kD + d, m);
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  const int r_begin = blockIdx.x * rows_per_block;
+  const int r_end = min(N, r_begin + rows_per_block);
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r_begin + rl; r < r_end; r += 64) {
+    float v[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      load8(x, (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg, is_bf16, v[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[k][j]));  // repeats are harmless
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rl][8 * cg + j] = m[j];
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t = fmaxf(t, red[i][threadIdx.x]);
+    atomic_max_nonneg(out + bh * kD + threadIdx.x, t);
+  }
 }
 
 // Per (b, h, d): 64-bit fixed-point sum of x at unit 2^(E-30), where the
 // channel amax M lies in [2^(E-1), 2^E).  Each term is rounded to the
 // nearest integer (half to even) in FP64, where the scaling is exact; the
 // integer sum is exact, so the result does not depend on order.
-__global__ void k_channel_fixsum(const void* __restrict__ x, int is_bf16, int N,
-                                 const uint32_t* __restrict__ absmax,
-                                 unsigned long long* __restrict__ sums) {
-  const int d = threadIdx.x & 127;
+__global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__ x, int is_bf16,
+                                                        int N, int rows_per_block,
+                                                        const uint32_t* __restrict__ absmax,
+                                                        unsigned long long* __restrict__ sums) {
+  __shared__ long long red[16][kD];
   const int64_t bh = blockIdx.y;
-  const float M = __uint_as_float(absmax[bh * kD + d]);
-  if (M == 0.0f) return;
-  int E;
-  frexpf(M, &E);
-  const double unit_inv = ldexp(1.0, 30 - E);
-  const int r_begin = blockIdx.x * kStatRows;
-  const int r_end = min(N, r_begin + kStatRows);
-  long long s = 0;
-  for (int r = r_begin + (threadIdx.x >> 7); r < r_end; r += 2) {
-    const double y = (double)load_elem(x, (bh * N + r) * kD + d, is_bf16) * unit_inv;
-    s += (long long)__builtin_rint(y);
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  double unit_inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float M = __uint_as_float(absmax[bh * kD + 8 * cg + j]);
+    int E = 0;
+    if (M != 0.0f) frexpf(M, &E);
+    unit_inv[j] = M != 0.0f ? ldexp(1.0, 30 - E) : 0.0;  // an all-zero channel sums to 0
   }
-  atomicAdd(sums + bh * kD + d, (unsigned long long)s);
+  const int r_begin = blockIdx.x * rows_per_block;
+  const int r_end = min(N, r_begin + rows_per_block);
+  long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r_begin + rl; r < r_end; r += 64) {
+    float v[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      load8(x, (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg, is_bf16, v[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (r + 16 * k < r_end) {  // every row counted exactly once
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += (long long)__builtin_rint((double)v[k][j] * unit_inv[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rl][8 * cg + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    long long t = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][threadIdx.x];
+    atomicAdd(sums + bh * kD + threadIdx.x, (unsigned long long)t);
+  }
 }
 
 // mean = fp32( (double)S / (double)N * 2^(E-30) ), each FP64 op rounded once.
@@ -72,30 +134,38 @@ __global__ void k_mean_finalize(const uint32_t* __restrict__ absmax,
 }
 
 // max |fp32(x - mean[bh, d])| over a whole [BH, N, 128] tensor (mean may be
-// NULL).  Grid (row chunks, BH): each thread takes 16-element groups of one
-// (batch, head) slice; one atomic per wave.
-constexpr int kAmaxGroups = 4096;  // 16-element groups per block (512 rows)
-
-__global__ void k_centered_amax(const void* __restrict__ x, int is_bf16, int N,
-                                const float* __restrict__ mean, uint32_t* __restrict__ out) {
+// NULL).  Same grid and thread layout as the channel statistics; each thread
+// keeps one running max, the block reduces it (wave shuffles, then LDS) and
+// issues a single atomic.
+__global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ x, int is_bf16,
+                                                       int N, int rows_per_block,
+                                                       const float* __restrict__ mean,
+                                                       uint32_t* __restrict__ out) {
+  __shared__ float red[4];
   const int64_t bh = blockIdx.y;
-  const int64_t n_groups = (int64_t)N * 8;
-  const int64_t g_begin = (int64_t)blockIdx.x * kAmaxGroups;
-  const int64_t g_end = min(n_groups, g_begin + kAmaxGroups);
-  const int d0 = (threadIdx.x & 7) * 16;  // blockDim is a multiple of 8
-  float mu[16];
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  float mu[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) mu[j] = mean ? mean[bh * kD + d0 + j] : 0.0f;
+  for (int j = 0; j < 8; ++j) mu[j] = mean ? mean[bh * kD + 8 * cg + j] : 0.0f;
+  const int r_begin = blockIdx.x * rows_per_block;
+  const int r_end = min(N, r_begin + rows_per_block);
   float m = 0.0f;
-  for (int64_t gi = g_begin + threadIdx.x; gi < g_end; gi += blockDim.x) {
-    float v[16];
-    load16(x, (bh * n_groups + gi) * 16, is_bf16, v);
+  for (int r = r_begin + rl; r < r_end; r += 128) {
+    float v[8][8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j] - mu[j]));
+    for (int k = 0; k < 8; ++k)  // a repeated row does not change the max
+      load8(x, (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg, is_bf16, v[k]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[k][j] - mu[j]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomic_max_nonneg(out, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
 }
 
 // NVFP4 codes and scales of K_c = fp32(K - k_mean) (k_mean NULL: K_c = K).
@@ -129,35 +199,43 @@ __global__ void k_quantize_k(const void* __restrict__ k, int is_bf16, int64_t n_
 // Delta_S[b, hk*G + g, t] = bf16(fp32(sum_d q_mean[b, hk*G+g, d] * K_c[b, hk, t, d])),
 // the sum in FP64 over ascending d (each product is exact in FP64, so a
 // fused multiply-add rounds exactly like an add of the product).
-// One thread per (b, hk, token) and group of up to 8 query heads.
-__global__ void k_delta_s(const void* __restrict__ k, int is_bf16, int Hkv, int G, int N,
-                          const float* __restrict__ k_mean, const float* __restrict__ q_mean,
-                          uint16_t* __restrict__ delta) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int bhk = blockIdx.y;       // b * Hkv + hk
+// Block: 64 tokens of one (b, hk) and up to 8 query heads (64 threads per
+// head).  The block stages K_c = fp32(K - k_mean) of its tokens in LDS with
+// coalesced loads (rows padded to 129 words, so the per-token reads below
+// hit 64 different banks), then thread (token, head) runs its FP64 sum.
+constexpr int kDsRows = 64;
+
+__global__ __launch_bounds__(512) void k_delta_s(const void* __restrict__ k, int is_bf16, int Hkv,
+                                                 int G, int N, const float* __restrict__ k_mean,
+                                                 const float* __restrict__ q_mean,
+                                                 uint16_t* __restrict__ delta) {
+  __shared__ float kc[kDsRows * (kD + 1)];
+  __shared__ float qm[8 * kD];
+  const int bhk = blockIdx.y;  // b * Hkv + hk
   const int g0 = blockIdx.z * 8;
-  if (t >= N) return;
   const int ng = min(8, G - g0);
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int64_t hq0 = (int64_t)b * Hkv * G + (int64_t)hk * G + g0;
+  const int t0 = blockIdx.x * kDsRows;
   const float* km = k_mean + (int64_t)bhk * kD;
-  const float* qm = q_mean + hq0 * kD;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int64_t row = ((int64_t)bhk * N + t) * kD;
-  for (int d0 = 0; d0 < kD; d0 += 16) {
-    float v[16];
-    load16(k, row + d0, is_bf16, v);
+  for (int e = threadIdx.x * 8; e < kDsRows * kD; e += blockDim.x * 8) {
+    const int r = e >> 7, d = e & 127;
+    float v[8];
+    load8(k, ((int64_t)bhk * N + min(t0 + r, N - 1)) * kD + d, is_bf16, v);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const double kc = (double)(v[j] - km[d0 + j]);
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g < ng) acc[g] = __builtin_fma((double)qm[g * kD + d0 + j], kc, acc[g]);
-    }
+    for (int j = 0; j < 8; ++j) kc[r * (kD + 1) + d + j] = v[j] - km[d + j];
   }
-#pragma unroll
-  for (int g = 0; g < 8; ++g)
-    if (g < ng) delta[(hq0 + g) * N + t] = (uint16_t)bf16_rne((float)acc[g]);
+  for (int e = threadIdx.x; e < ng * kD; e += blockDim.x) qm[e] = q_mean[hq0 * kD + e];
+  __syncthreads();
+  const int r = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int t = t0 + r;
+  if (t >= N || g >= ng) return;
+  const float* row = kc + r * (kD + 1);
+  const float* q = qm + g * kD;
+  double acc = 0.0;
+#pragma unroll 16
+  for (int d = 0; d < kD; ++d) acc = __builtin_fma((double)q[d], (double)row[d], acc);
+  delta[(hq0 + g) * N + t] = (uint16_t)bf16_rne((float)acc);
 }
 
 // FP8 E4M3 V in 32-token tiles, head-dim major inside a tile.  Block: 128
@@ -200,11 +278,20 @@ void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n, 256, 4096)), dim3(256), 0, st, p, n, v);
 }
 
+// Rows per block so that the whole pass has about kStatBlocks blocks.
+static inline int stat_rows_per_block(int BH, int N, int align) {
+  const int64_t xb = (kStatBlocks + BH - 1) / BH;
+  int64_t rows = (N + xb - 1) / xb;
+  rows = (rows + align - 1) / align * align;
+  return (int)(rows < align ? align : rows);
+}
+
 void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
                          unsigned long long* sums, float* mean, hipStream_t st) {
-  dim3 grid((N + kStatRows - 1) / kStatRows, BH);
-  hipLaunchKernelGGL(k_channel_absmax, grid, dim3(256), 0, st, x, is_bf16, N, absmax);
-  hipLaunchKernelGGL(k_channel_fixsum, grid, dim3(256), 0, st, x, is_bf16, N,
+  const int rows = stat_rows_per_block(BH, N, 64);
+  dim3 grid((unsigned)((N + rows - 1) / rows), BH);
+  hipLaunchKernelGGL(k_channel_absmax, grid, dim3(256), 0, st, x, is_bf16, N, rows, absmax);
+  hipLaunchKernelGGL(k_channel_fixsum, grid, dim3(256), 0, st, x, is_bf16, N, rows,
                      (const uint32_t*)absmax, sums);
   const int n = BH * kD;
   hipLaunchKernelGGL(k_mean_finalize, dim3((n + 255) / 256), dim3(256), 0, st,
@@ -213,9 +300,9 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
 
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
                           uint32_t* out, hipStream_t st) {
-  const int64_t n_groups = (int64_t)N * (kD / 16);
-  dim3 grid((unsigned)((n_groups + kAmaxGroups - 1) / kAmaxGroups), BH);
-  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, mean, out);
+  const int rows = stat_rows_per_block(BH, N, 128);
+  dim3 grid((unsigned)((N + rows - 1) / rows), BH);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out);
 }
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
@@ -228,9 +315,9 @@ void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const fl
 
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
                     const float* q_mean, uint16_t* delta, hipStream_t st) {
-  dim3 grid((N + 127) / 128, B * Hkv, (G + 7) / 8);
-  hipLaunchKernelGGL(k_delta_s, grid, dim3(128), 0, st, k, is_bf16, Hkv, G, N, k_mean, q_mean,
-                     delta);
+  dim3 grid((N + kDsRows - 1) / kDsRows, B * Hkv, (G + 7) / 8);
+  hipLaunchKernelGGL(k_delta_s, grid, dim3(kDsRows * min(G, 8)), 0, st, k, is_bf16, Hkv, G, N,
+                     k_mean, q_mean, delta);
 }
 
 void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
