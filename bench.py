@@ -43,9 +43,13 @@ PEAK_F16 = 2.5e15
 PEAK_F16_FP8 = 1.0 / (0.5 / PEAK_F16 + 0.5 / PEAK_FP8)
 
 
+# Sources of the kernels one call runs (the call's launch sequence is in
+# api.hip, its pre-passes in quant.hip).
 KERNEL_SOURCES = {
-    "prefill": ["csrc/prefill.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
-    "decode": ["csrc/decode.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
+    "prefill": ["csrc/api.hip", "csrc/prefill.hip", "csrc/quant.hip", "csrc/mpfa_device.hpp",
+                "csrc/mpfa_internal.hpp"],
+    "decode": ["csrc/api.hip", "csrc/decode.hip", "csrc/quant.hip", "csrc/mpfa_device.hpp",
+               "csrc/mpfa_internal.hpp"],
     "quant": ["csrc/quant.hip", "csrc/mpfa_device.hpp", "csrc/mpfa_internal.hpp"],
 }
 
@@ -194,14 +198,20 @@ def write_traffic(run_dir, args):
                            "write_kib": round(write_kib, 1), "fetch_factor": round(F, 5),
                            "write_factor": round(W, 5)},
            "command": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv "
-                      "-d DIR/pmc_<op>_<counter> -o run -- python bench.py --only <op>; "
+                      "-d DIR/pmc_<op>_<counter> -o run -- python bench.py --only <op> "
+                      "(op prefill_long: --only prefill --workload qwen14b_prefill_32k); "
                       "then python bench.py --write-traffic DIR",
            "calls": {}}
-    for op, kind, main_kernel, offsets, name in (
-            ("prefill", "prefill", "k_prefill<true>", (-2, -1, 0),
-             f"mpfa_prefill {args.workload}"),
-            ("decode", "decode", "k_decode_split<true>", (-2, -1, 0, 1),
-             f"mpfa_decode {args.decode_workload}")):
+    # dispatches of one call relative to its main kernel: prefill = fill, Q amax
+    # pre-pass, K expansion, attention; decode = fill, Q amax, split, combine
+    calls = [("prefill", "prefill", "k_prefill<true>", (-3, -2, -1, 0),
+              f"mpfa_prefill {args.workload}"),
+             ("decode", "decode", "k_decode_split<true>", (-2, -1, 0, 1),
+              f"mpfa_decode {args.decode_workload}")]
+    if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
+        calls.append(("prefill_long", "prefill", "k_prefill<true>", (-3, -2, -1, 0),
+                      f"mpfa_prefill {args.long_workload}"))
+    for op, kind, main_kernel, offsets, name in calls:
         fv, fn = load(op, "FETCH_SIZE")
         wv, wn = load(op, "WRITE_SIZE")
         parts = {}

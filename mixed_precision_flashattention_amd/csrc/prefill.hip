@@ -63,13 +63,15 @@ __device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_addr) {
 __device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// This wave's share (4 KB of 32) of K~ block k0.  Rows past the end repeat
-// the last key; those keys are masked out of the block.
+// Wave w's share of K~ block k0 when NW waves load it: 1 KB pieces (4 rows
+// each) 32/NW w .. 32/NW (w+1) - 1.  Rows past the end repeat the last key;
+// those keys are masked out of the block.
+template <int NW>
 __device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0, uint32_t dst,
-                                              int wave, int lane) {
+                                              int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int piece = 4 * wave + i;  // 1 KB = rows 4 piece .. 4 piece + 3
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int piece = (32 / NW) * w + i;  // 1 KB = rows 4 piece .. 4 piece + 3
     const int r = 4 * piece + (lane >> 4);
     const int chunk = (lane & 15) ^ kswz(r);  // the chunk that belongs in slot lane & 15
     const int key = min(k0 + r, N - 1);
@@ -77,12 +79,14 @@ __device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0
   }
 }
 
-// This wave's share (2 KB of 16) of V block k0: pieces (tile, half, 64 channels).
+// Wave w's share of V block k0 when NW waves load it: pieces (tile, half,
+// 64 channels) 16/NW w .. 16/NW (w+1) - 1.
+template <int NW>
 __device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32, int k0,
-                                              uint32_t dst, int wave, int lane) {
+                                              uint32_t dst, int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = 2 * wave + i;
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int piece = (16 / NW) * w + i;
     const int t = piece >> 2, half = (piece >> 1) & 1, ch0 = 64 * (piece & 1);
     const int tt = min(k0 / 32 + t, ntiles32 - 1);
     lds_load16(vbase + (int64_t)tt * kVTileBytes + (ch0 + lane) * 32 + half * 16,
@@ -369,27 +373,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
   __syncthreads();  // Q~ and the LSE parts are consumed: LDS is free for the blocks
-  issue_k_block(ktil, N, 0, lds_k0, wave, lane);
+  issue_k_block<8>(ktil, N, 0, lds_k0, wave, lane);
   uint32_t dd = 0;
   if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 
   // Steps alternate between the groups: in body j, group 0 runs its matrix
   // phase (P.V of block j-1, scores of block j) in the first step and the
   // softmax of block j in the second; group 1 runs the softmax of block j-1
-  // first and its matrix phase second.  The first step of body j publishes
-  // K~(j), Delta_S(j) and V(j-1) and starts the loads of K~(j+1),
-  // Delta_S(j+1) and V(j).  Both loops pass the same barriers.
+  // first and its matrix phase second.  Group 0 finishes its matrix phase
+  // first, so it issues the loads of K~(j+1), Delta_S(j+1) and V(j) before
+  // the middle barrier (their buffers were last read in body j-1); the
+  // barrier that opens body j+1 publishes them.  Both loops pass the same
+  // barriers.
 #define MPFA_STEP_OPEN(J)                                                                    \
   do {                                                                                       \
     wait_direct_loads(); /* this wave's loads of the previous body have landed */            \
     if (SMOOTH && tid < kBlk) smem_delta[(J) & 1][tid] = (uint16_t)dd;                       \
     __syncthreads();                                                                         \
+  } while (0)
+#define MPFA_ISSUE(J)                                                                        \
+  do {                                                                                       \
     if ((J) + 1 < n_max) {                                                                   \
-      issue_k_block(ktil, N, ((J) + 1) * kBlk, ((J) & 1) ? lds_k0 : lds_k1, wave, lane);     \
+      issue_k_block<4>(ktil, N, ((J) + 1) * kBlk, ((J) & 1) ? lds_k0 : lds_k1, wave, lane);  \
       if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
     }                                                                                        \
-    if ((J) < n_max) issue_v_block(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, \
-                                   wave, lane);                                              \
+    if ((J) < n_max)                                                                         \
+      issue_v_block<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, lane); \
   } while (0)
 #define MPFA_MATRIX(J)                                                                       \
   do {                                                                                       \
@@ -416,6 +425,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int j = 0; j <= n_max; ++j) {
       MPFA_STEP_OPEN(j);
       MPFA_MATRIX(j);
+      MPFA_ISSUE(j);
       __syncthreads();
       MPFA_SOFTMAX(j);
     }
@@ -428,6 +438,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
 #undef MPFA_STEP_OPEN
+#undef MPFA_ISSUE
 #undef MPFA_MATRIX
 #undef MPFA_SOFTMAX
 
