@@ -164,6 +164,38 @@ def accuracy_report(mpfa):
     return out
 
 
+def measure_prefill(mpfa, synth, dev, name, iters):
+    """One workload's prefill call (bf16 output, LSE when the workload asks
+    for it) timed with HIP events, against the FP4/FP8 roofline."""
+    import torch
+    pcfg = synth.config(name)
+    px = synth.device_inputs(pcfg, dev)
+    pkq = mpfa.quantize_k(px["k"], q=px["q"])
+    pvq = mpfa.quantize_v(px["v"])
+    del px["k"], px["v"]
+    pout = torch.empty(px["q"].shape, dtype=torch.bfloat16, device=dev)
+    plse = torch.empty(px["q"].shape[:3], dtype=torch.float32, device=dev) if pcfg.lse else None
+    pws = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, pcfg.B, pcfg.Hq, pcfg.Hkv,
+                                                pcfg.N), dtype=torch.uint8, device=dev)
+
+    def call():
+        mpfa.prefill(px["q"], pkq, pvq, pcfg.scale, causal=True, out=pout, lse=plse,
+                     with_lse=pcfg.lse, ws=pws)
+
+    ms = time_calls(call, iters, 1)
+    fl = prefill_flops(pcfg.B, pcfg.Hq, pcfg.N)
+    ach = fl / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill {pcfg.name}: {ms:.3f} ms -> {ach:.1f} TFLOP/s "
+        f"({ach * 1e12 / PEAK_MIXED:.3f} of the FP4/FP8 roofline)")
+    return {"workload": pcfg.name, "batch": pcfg.B, "q_heads": pcfg.Hq, "kv_heads": pcfg.Hkv,
+            "seq_len": pcfg.N, "lse": pcfg.lse, "ms": round(ms, 4), "flops_per_call": fl,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2),
+                         "peak": round(PEAK_MIXED / 1e12, 1), "unit": "TFLOP/s",
+                         "frac": round(ach * 1e12 / PEAK_MIXED, 4),
+                         "traffic": measured_traffic(f"mpfa_prefill {pcfg.name}")},
+            "frac_of_fp16_fp8_instruction_peak": round(ach * 1e12 / PEAK_F16_FP8, 4)}
+
+
 def write_traffic(run_dir, args):
     """profiles/traffic.json from six counter runs of `bench.py --only X`
     (X in prefill, decode, copy; one FETCH_SIZE and one WRITE_SIZE pass each).
@@ -274,6 +306,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--long-workload", default="qwen14b_prefill_32k")
     ap.add_argument("--no-32k", action="store_true")
+    ap.add_argument("--lse-workload", default="llama8b_prefill_128k_lse")
+    ap.add_argument("--no-128k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -386,38 +420,21 @@ def main():
         "prefill_ms": round(ms_prefill, 4), "prefill_direct_ms": round(ms_direct, 4),
         "stage_one_ms": round(ms_stage1, 4),
         "compensation_overhead": round(ms_prefill / ms_direct - 1.0, 4),
+        "env": {"gpu": torch.cuda.get_device_name(0),
+                "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+                "hip": torch.version.hip, "torch": torch.__version__},
     }
     del q, k, v, x, kq, vq, out
     torch.cuda.empty_cache()
 
-    # ---- the long-context prefill the roofline target is stated for --------
+    # ---- the long-context prefills: 32K (the roofline target's configuration)
+    # and the 128K two-sequence prefill that also writes the LSE ------------
     if not args.no_32k:
-        pcfg = synth.config(args.long_workload)
-        px = synth.device_inputs(pcfg, dev)
-        pkq = mpfa.quantize_k(px["k"], q=px["q"])
-        pvq = mpfa.quantize_v(px["v"])
-        del px["k"], px["v"]
-        pout = torch.empty(px["q"].shape, dtype=torch.bfloat16, device=dev)
-        pws = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, pcfg.B, pcfg.Hq, pcfg.Hkv,
-                                                    pcfg.N), dtype=torch.uint8, device=dev)
-
-        def long_call():
-            mpfa.prefill(px["q"], pkq, pvq, pcfg.scale, causal=True, out=pout, ws=pws)
-
-        ms_long = time_calls(long_call, max(3, args.steps // 2), 1)
-        lflops = prefill_flops(pcfg.B, pcfg.Hq, pcfg.N)
-        lach = lflops / (ms_long * 1e-3) / 1e12
-        log(f"[bench] prefill {pcfg.name}: {ms_long:.3f} ms -> {lach:.1f} TFLOP/s "
-            f"({lach * 1e12 / PEAK_MIXED:.3f} of the FP4/FP8 roofline)")
-        result["prefill_long"] = {
-            "workload": pcfg.name, "batch": pcfg.B, "q_heads": pcfg.Hq, "kv_heads": pcfg.Hkv,
-            "seq_len": pcfg.N, "ms": round(ms_long, 4), "flops_per_call": lflops,
-            "roofline": {"bound": "mfma", "achieved": round(lach, 2),
-                         "peak": round(PEAK_MIXED / 1e12, 1), "unit": "TFLOP/s",
-                         "frac": round(lach * 1e12 / PEAK_MIXED, 4),
-                         "traffic": measured_traffic(f"mpfa_prefill {pcfg.name}")},
-            "frac_of_fp16_fp8_instruction_peak": round(lach * 1e12 / PEAK_F16_FP8, 4)}
-        del px, pkq, pvq, pout, pws
+        result["prefill_long"] = measure_prefill(mpfa, synth, dev, args.long_workload,
+                                                 max(3, args.steps // 2))
+        torch.cuda.empty_cache()
+    if not args.no_128k:
+        result["prefill_128k_lse"] = measure_prefill(mpfa, synth, dev, args.lse_workload, 2)
         torch.cuda.empty_cache()
 
     # ---- decode -----------------------------------------------------------
