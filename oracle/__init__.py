@@ -235,6 +235,7 @@ def merge_states(m, l, acc, scale):
 
 from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     Operands,
+    append_kv,
     decode,
     decode_partitions,
     exact_attention,
@@ -250,5 +251,5 @@ __all__ = [
     "bf16_rne", "bf16_to_f64", "channel_mean", "amax", "nvfp4_global_scale", "nvfp4_quantize",
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
     "quantize_k", "quantize_v", "quantize_q", "prefill_rows", "decode", "decode_partitions",
-    "exact_attention", "Operands"
+    "exact_attention", "Operands", "append_kv"
 ]

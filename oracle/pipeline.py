@@ -74,6 +74,49 @@ def quantize_q(q, q_mean=None):
     return codes, sf, np.float32(g)
 
 
+def append_kv(k_new, v_new, pos, cache, q_mean=None, k_mean=None):
+    """Decode-time cache write (MpFA §6 "Online quantization"): the new tokens
+    are centred against the frozen per-request means and quantized with the
+    cache's frozen scales; in smoothing mode their compensation entries are
+    computed in the same pass.
+
+    Reading: the per-tensor global scales of the K and V caches are frozen with
+    the means (the pages freeze the statistics for the sequence lifetime and
+    re-quantizing the whole cache per token is not an option), so values out
+    of their range saturate in the encoders.
+
+    k_new, v_new [B, Hkv, T, D]; token t of batch entry b goes to position
+    pos[b] + t.  cache: dict with k_fp4 [B, Hkv, Ncap, D/2], k_sf
+    [B, Hkv, Ncap, D/16], k_gscale, v_fp8 [B, Hkv, Ncap, D] (row layout),
+    v_scale and, in smoothing mode, delta_s [B, Hq, Ncap] (smoothing iff
+    k_mean is given; q_mean [B, Hq, D] then too).  Returns an updated copy."""
+    k_new = np.asarray(k_new, dtype=F32)
+    v_new = np.asarray(v_new, dtype=F32)
+    B, Hkv, T, D = k_new.shape
+    out = {name: (np.array(a, copy=True) if isinstance(a, np.ndarray) else a)
+           for name, a in cache.items()}
+    smooth = k_mean is not None
+    if smooth:
+        k_mean = np.asarray(k_mean, dtype=F32)
+        q_mean = np.asarray(q_mean, dtype=F32)
+        Hq = q_mean.shape[1]
+        G = Hq // Hkv
+    g = np.float32(cache["k_gscale"])
+    s = np.float32(cache["v_scale"])
+    for b in range(B):
+        rows = slice(int(pos[b]), int(pos[b]) + T)
+        for hk in range(Hkv):
+            kc = (k_new[b, hk] - k_mean[b, hk][None, :]).astype(F32) if smooth else k_new[b, hk]
+            codes, sf = nvfp4_quantize(kc, g)
+            out["k_fp4"][b, hk, rows] = codes
+            out["k_sf"][b, hk, rows] = sf
+            out["v_fp8"][b, hk, rows] = fp8_quantize(v_new[b, hk], s)
+            if smooth:
+                for h in range(hk * G, (hk + 1) * G):
+                    out["delta_s"][b, h, rows] = delta_s(q_mean[b, h], kc)
+    return out
+
+
 def _finalize(m, l, acc, s_v, scale, lse_offset, out_f64=False):
     o = acc * float(s_v) / (P_SCALE * l[:, None])
     if not out_f64:
@@ -100,6 +143,7 @@ class Operands:
         B, Hq = q.shape[:2]
         Hkv = k.shape[1]
         self.G = Hq // Hkv
+        self.n_kv = k.shape[2]
         self.smooth = smooth
         self.identity = identity
         self._q, self._k, self._v = q, k, v
@@ -127,6 +171,36 @@ class Operands:
         self.s_v = float(vq["v_scale"])
         self.quant_p = True
         self._table = e4m3_table()
+
+    @classmethod
+    def from_cache(cls, q, cache, n_kv, q_mean=None, k_mean=None):
+        """Operands of a decode over the first n_kv positions of existing
+        caches (as written by quantize_k / quantize_v / append_kv): the
+        cache codes and their frozen scales are used as they are; Q is
+        quantized per call as in __init__ (centred by q_mean in smoothing
+        mode, which is on iff cache holds delta_s)."""
+        self = cls.__new__(cls)
+        q = np.asarray(q, dtype=F32)
+        self.smooth = "delta_s" in cache and cache["delta_s"] is not None
+        self.identity = False
+        self.G = q.shape[1] // cache["k_fp4"].shape[1]
+        self.n_kv = n_kv
+        self._q = q
+        self.kq = {"k_fp4": cache["k_fp4"][:, :, :n_kv], "k_sf": cache["k_sf"][:, :, :n_kv],
+                   "k_gscale": np.float32(cache["k_gscale"])}
+        self.vq = {"v_fp8": cache["v_fp8"][:, :, :n_kv], "v_scale": np.float32(cache["v_scale"])}
+        if self.smooth:
+            self.k_mean = np.asarray(k_mean, dtype=F32)
+            self._delta = cache["delta_s"][:, :, :n_kv]
+            self.q_codes, self.q_sf, self.q_gscale = quantize_q(q, q_mean)
+        else:
+            self.k_mean = None
+            self._delta = None
+            self.q_codes, self.q_sf, self.q_gscale = quantize_q(q, None)
+        self.s_v = float(self.vq["v_scale"])
+        self.quant_p = True
+        self._table = e4m3_table()
+        return self
 
     def q(self, b, h, pos):
         if self.identity:
@@ -219,7 +293,7 @@ def decode(q, k, v, q_mean, num_splits, scale, smooth=True, identity=False, out_
     if q.ndim == 3:
         q = q[:, :, None, :]
     B, Hq, _, D = q.shape
-    N = np.asarray(k).shape[2]
+    N = ops.n_kv if (ops is not None and k is None) else np.asarray(k).shape[2]
     if ops is None:
         ops = Operands(q, k, v, scale, smooth, identity, q_mean=q_mean if smooth else None)
     G = ops.G
