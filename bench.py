@@ -473,7 +473,15 @@ def main():
                          "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4),
                          "traffic": measured_traffic("mpfa_decode llama8b_decode_128k")},
             "direct_ms": round(ms_dec_direct, 4), "direct_GBps": round(gbs_d, 1)}
-        del dkq, dvq, dq, dout, dws, dx
+        # decode-time cache write of one new token per request (centring against
+        # the frozen means, NVFP4 K / FP8 V with the frozen scales, Delta_S)
+        kn = torch.randn((dcfg.B, dcfg.Hkv, 1, D), device=dev).to(torch.bfloat16)
+        vn = torch.randn((dcfg.B, dcfg.Hkv, 1, D), device=dev).to(torch.bfloat16)
+        pos = torch.full((dcfg.B,), dcfg.N - 1, dtype=torch.int32, device=dev)
+        ms_app = time_calls(lambda: mpfa.append_kv(kn, vn, pos, dkq, dvq), max(args.steps, 10), 3)
+        log(f"[bench] append of one token per request: {ms_app * 1e3:.1f} us")
+        result["decode"]["append_one_token_us"] = round(ms_app * 1e3, 2)
+        del dkq, dvq, dq, dout, dws, dx, kn, vn, pos
         torch.cuda.empty_cache()
 
     if not args.no_accuracy:

@@ -135,6 +135,38 @@ int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D
                         float* v_scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mpfa_append_kv -- decode-time cache write of new tokens (paper section 6,
+ * "Online quantization": a newly appended token is centred against the
+ * per-request means frozen at prefill and written to the low-bit caches in
+ * the same pass that produces its compensation entries).
+ *
+ * k_new, v_new: [B, Hkv, T, D] in kv_dtype; token t of batch entry b is
+ * written to cache position pos[b] + t, where pos is a device int32 array
+ * [B] (the caller's per-request lengths).  Caches of capacity N_cap tokens,
+ * in the layouts mpfa_quantize_k_nvfp4 / mpfa_quantize_v_fp8 write:
+ * k_fp4 [B, Hkv, N_cap, 64], k_sf [B, Hkv, N_cap, 8], v_fp8
+ * [B, Hkv, ceil(N_cap/32), 128, 32], delta_s [B, Hq, N_cap] (bf16 bits).
+ * The new rows are quantized exactly as the first stage would quantize
+ * them with the same statistics: K_c = fp32(K - k_mean) (k_mean may be NULL:
+ * direct mode), NVFP4 with the frozen global scale *k_gscale, FP8 with the
+ * frozen *v_scale (values out of range saturate), and in smoothing mode
+ * delta_s[b, h, p] = bf16(q_mean[b, h] . K_c) for the Hq / Hkv query heads
+ * of each KV head.  Smoothing iff k_mean != NULL; then q_mean [B, Hq, 128]
+ * and delta_s are required and Hq / Hkv <= 120.
+ *
+ * Only the T rows of each batch entry are written.  Positions are read on
+ * the device: an entry with pos[b] < 0 or pos[b] + T > N_cap is skipped
+ * (nothing written for it), which the host cannot report.
+ * No workspace.  Returns MPFA_ERR_INVALID for T < 1 or T > N_cap, null or
+ * misaligned pointers, delta_s without k_mean.
+ */
+int mpfa_append_kv(const void* k_new, const void* v_new, int kv_dtype, int B, int Hkv, int T,
+                   int D, int N_cap, const int32_t* pos, int Hq, const float* q_mean,
+                   const float* k_mean, const float* k_gscale, const float* v_scale,
+                   uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta_s,
+                   void* stream);
+
+/*
  * mpfa_prefill -- QK4PV8 attention over a whole sequence (paper section 5.1,
  * "second stage"; sections 5.2, 4.1).
  *

@@ -28,7 +28,7 @@ HEAD_DIM = 128
 V_TILE = 32  # tokens per head-dim-major V tile
 
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
-           "mpfa_quantize_v_fp8", "mpfa_prefill", "mpfa_decode")
+           "mpfa_quantize_v_fp8", "mpfa_append_kv", "mpfa_prefill", "mpfa_decode")
 
 _lib = None
 
@@ -57,6 +57,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, sz, P]
     L.mpfa_quantize_v_fp8.restype = i32
     L.mpfa_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, sz, P]
+    L.mpfa_append_kv.restype = i32
+    L.mpfa_append_kv.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P,
+                                 P]
     L.mpfa_prefill.restype = i32
     L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
                                P, i32, P, P, sz, P]
@@ -151,6 +154,25 @@ def mpfa_prefill(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, 
         float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_prefill", st)
+
+
+def mpfa_append_kv(k_new, v_new, pos, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8,
+                   delta_s, Hq=None, stream=None):
+    """k_new, v_new [B, Hkv, T, 128]; pos int32 [B]; caches of capacity
+    k_fp4.shape[2] tokens (smoothing iff k_mean is given)."""
+    _check(k_new, v_new, pos, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8, delta_s)
+    import torch
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be an int32 tensor")
+    B, Hkv, T, D = k_new.shape
+    N_cap = k_fp4.shape[2]
+    if Hq is None:
+        Hq = q_mean.shape[1] if q_mean is not None else 0
+    st = load_library().mpfa_append_kv(
+        _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, T, D, N_cap, _ptr(pos), Hq,
+        _ptr(q_mean), _ptr(k_mean), _ptr(k_gscale), _ptr(v_scale), _ptr(k_fp4), _ptr(k_sf),
+        _ptr(v_fp8), _ptr(delta_s), _stream(stream))
+    _raise("mpfa_append_kv", st)
 
 
 def mpfa_decode(q, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
@@ -253,6 +275,17 @@ def decode(q, kq, vq, softmax_scale, num_splits, out_dtype=None, with_lse=False,
                 kq.get("delta_s") if smooth else None, softmax_scale, num_splits, out,
                 lse if with_lse else None, ws, stream=stream)
     return out, (lse if with_lse else None)
+
+
+def append_kv(k_new, v_new, pos, kq, vq, stream=None):
+    """Write new tokens into the caches returned by quantize_k / quantize_v
+    (capacity = their length) at positions pos[b] + t, with their frozen
+    means and scales; smoothing iff kq holds delta_s."""
+    smooth = "delta_s" in kq
+    mpfa_append_kv(k_new, v_new, pos, kq.get("q_mean") if smooth else None,
+                   kq.get("k_mean") if smooth else None, kq["k_gscale"], vq["v_scale"],
+                   kq["k_fp4"], kq["k_sf"], vq["v_fp8"], kq.get("delta_s") if smooth else None,
+                   stream=stream)
 
 
 def v_tiles_to_rows(v_fp8_tiled, N: int):

@@ -171,6 +171,36 @@ int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D
   return launch_status();
 }
 
+int mpfa_append_kv(const void* k_new, const void* v_new, int kv_dtype, int B, int Hkv, int T,
+                   int D, int N_cap, const int32_t* pos, int Hq, const float* q_mean,
+                   const float* k_mean, const float* k_gscale, const float* v_scale,
+                   uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta_s,
+                   void* stream) {
+  int st = check_sizes(B, Hkv, N_cap, D);
+  if (st) return st;
+  if (!dtype_ok(kv_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (T < 1 || T > N_cap || T > 65535) return MPFA_ERR_INVALID;
+  if (!k_new || !v_new || !pos || !k_gscale || !v_scale || !k_fp4 || !k_sf || !v_fp8)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_fp4) || !aligned16(k_sf) ||
+      !aligned16(v_fp8))
+    return MPFA_ERR_INVALID;
+  const bool smooth = k_mean != nullptr;
+  int G = 0;
+  if (smooth) {
+    if (!q_mean || !delta_s) return MPFA_ERR_INVALID;
+    if ((st = check_heads(Hq, Hkv, B))) return st;
+    G = Hq / Hkv;
+    if (G > kD - 8) return MPFA_ERR_UNSUPPORTED;
+  } else if (delta_s) {
+    return MPFA_ERR_INVALID;  // a compensation cache needs the means
+  }
+  launch_append_kv(k_new, v_new, kv_dtype == MPFA_BF16, B, Hkv, G, T, N_cap, pos,
+                   smooth ? q_mean : nullptr, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8,
+                   smooth ? delta_s : nullptr, (hipStream_t)stream);
+  return launch_status();
+}
+
 int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,

@@ -61,6 +61,12 @@ void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, co
 void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
                              float* vscale, uint8_t* out, hipStream_t st);
 
+void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, int Hkv, int G,
+                      int T, int N_cap, const int32_t* pos, const float* q_mean,
+                      const float* k_mean, const float* k_gscale, const float* v_scale,
+                      uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta,
+                      hipStream_t st);
+
 // prefill.hip
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, uint8_t* k_f16,
                      hipStream_t st);

@@ -267,6 +267,60 @@ __global__ void k_quantize_v(const void* __restrict__ v, int is_bf16, int N, int
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// Decode-time cache write of T new tokens per (batch, KV head) (paper
+// section 6 "Online quantization": the new token is centred against the
+// frozen per-request means and quantized with the cache's frozen scales; its
+// compensation entries are written in the same pass).  Block = 128 threads
+// for one (b, hk, token): thread d centres channel d into LDS and writes its
+// FP8 V byte; threads 0-7 then quantize the row's eight NVFP4 blocks and
+// threads 8 .. 8+G-1 its G Delta_S entries (FP64 over ascending channels).
+// A batch entry whose position is outside [0, N_cap - T] is skipped whole.
+__global__ __launch_bounds__(128) void k_append_kv(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int is_bf16, int Hkv, int G,
+    int T, int N_cap, const int32_t* __restrict__ pos, const float* __restrict__ q_mean,
+    const float* __restrict__ k_mean, const float* __restrict__ k_gscale,
+    const float* __restrict__ v_scale, uint8_t* __restrict__ k_fp4, uint8_t* __restrict__ k_sf,
+    uint8_t* __restrict__ v_fp8, uint16_t* __restrict__ delta) {
+  __shared__ float kc[kD];
+  const int t = blockIdx.x;
+  const int bhk = blockIdx.y;  // b * Hkv + hk
+  const int b = bhk / Hkv;
+  const int p0 = pos[b];
+  if (p0 < 0 || p0 > N_cap - T) return;  // uniform over the block
+  const int p = p0 + t;
+  const int d = threadIdx.x;
+  const int64_t src = ((int64_t)bhk * T + t) * kD + d;
+  float x = load_elem(k_new, src, is_bf16);
+  if (k_mean) x = x - k_mean[(int64_t)bhk * kD + d];
+  kc[d] = x;
+  const int ntiles = (N_cap + 31) / 32;
+  const float s = *v_scale;
+  v_fp8[(((int64_t)bhk * ntiles + p / 32) * kD + d) * 32 + (p & 31)] =
+      (uint8_t)e4m3_encode(load_elem(v_new, src, is_bf16) / s);
+  __syncthreads();
+  const int64_t row = (int64_t)bhk * N_cap + p;
+  if (d < 8) {
+    float xb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xb[j] = kc[16 * d + j];
+    uint32_t c[16];
+    const uint32_t sc = nvfp4_block(xb, *k_gscale, c);
+    uint2 packed;
+    packed.x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
+               (c[6] << 24) | (c[7] << 28);
+    packed.y = c[8] | (c[9] << 4) | (c[10] << 8) | (c[11] << 12) | (c[12] << 16) | (c[13] << 20) |
+               (c[14] << 24) | (c[15] << 28);
+    reinterpret_cast<uint2*>(k_fp4)[row * 8 + d] = packed;
+    k_sf[row * 8 + d] = (uint8_t)sc;
+  } else if (k_mean && d < 8 + G) {
+    const int64_t hq = (int64_t)bhk * G + (d - 8);
+    const float* qm = q_mean + hq * kD;
+    double acc = 0.0;
+    for (int c = 0; c < kD; ++c) acc = __builtin_fma((double)qm[c], (double)kc[c], acc);
+    delta[hq * N_cap + p] = (uint16_t)bf16_rne((float)acc);
+  }
+}
+
 // ------------------------------------------------------------- launchers --
 static inline unsigned grid_for(int64_t n, int block, unsigned cap) {
   int64_t g = (n + block - 1) / block;
@@ -325,6 +379,15 @@ void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const ui
   const int n_tiles = (N + 31) / 32;
   hipLaunchKernelGGL(k_quantize_v, dim3(n_tiles, BH), dim3(128), 0, st, v, is_bf16, N, n_tiles,
                      amax, vscale, out);
+}
+
+void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, int Hkv, int G,
+                      int T, int N_cap, const int32_t* pos, const float* q_mean,
+                      const float* k_mean, const float* k_gscale, const float* v_scale,
+                      uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(k_append_kv, dim3(T, B * Hkv), dim3(kD), 0, st, k_new, v_new, is_bf16, Hkv, G,
+                     T, N_cap, pos, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8, delta);
 }
 
 }  // namespace mpfa

@@ -153,3 +153,28 @@ def test_quantizers_reject_bad_arguments(lib):
     assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, 256, None) == -2
     assert qv(f.p, 1, 1, 2, 64, 128, None, f.p, f.p, 256, None) == -1
     assert qv(f.p, 1, 1, 2, 64, 128, f.p, f.p, f.p, 8, None) == -3
+
+
+def _append(lib, f, **kw):
+    a = dict(k_new=f.p, v_new=f.p, dtype=1, B=2, Hkv=2, T=1, D=128, N_cap=64, pos=f.p, Hq=4,
+             q_mean=f.p, k_mean=f.p, k_gscale=f.p, v_scale=f.p, k_fp4=f.p, k_sf=f.p, v_fp8=f.p,
+             delta_s=f.p, stream=None)
+    a.update(kw)
+    return lib.mpfa_append_kv(*a.values())
+
+
+def test_append_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP = -1, -2
+    assert _append(lib, f, T=0) == INVALID
+    assert _append(lib, f, T=65) == INVALID  # more tokens than the cache holds
+    assert _append(lib, f, pos=None) == INVALID
+    assert _append(lib, f, k_gscale=None) == INVALID
+    assert _append(lib, f, k_fp4=f.mis) == INVALID
+    assert _append(lib, f, q_mean=None) == INVALID  # smoothing needs both means
+    assert _append(lib, f, delta_s=None) == INVALID
+    assert _append(lib, f, k_mean=None, q_mean=None) == INVALID  # delta_s without the means
+    assert _append(lib, f, Hq=3) == INVALID
+    assert _append(lib, f, D=64) == UNSUP
+    assert _append(lib, f, dtype=7) == UNSUP
+    assert _append(lib, f, Hq=2 * 121) == UNSUP  # a group of 121 query heads
