@@ -55,12 +55,17 @@ KERNEL_SOURCES = {
 
 
 def source_hash(kind):
-    """sha256 of the sources a kernel is built from (package-relative paths)."""
+    """sha256 of the sources a kernel is built from (package-relative paths),
+    with comments and whitespace removed, so only a change of code counts."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "mixed_precision_flashattention_amd", rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mixed_precision_flashattention_amd", rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

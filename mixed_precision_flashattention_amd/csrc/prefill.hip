@@ -6,19 +6,21 @@
 // bits, range [2^-10, 2688]: exact in FP16; the per-tensor global scale stays
 // out and is folded into the exp2 constant).
 //
-// Work unit: one (batch, query head, 128-row query tile); 4 waves of 32 rows;
-// two workgroups share a CU (<= 256 registers per wave), so one workgroup's
-// softmax overlaps the other's matrix products.  Per 128-key block:
+// Work unit: one (batch, query head, 256-row query tile) per workgroup of 8
+// waves, one workgroup per CU.  The waves form two row groups of 4 (rows
+// 0-127 and 128-255, 32 rows per wave), and each SIMD holds one wave of each
+// group.  The groups alternate between workgroup barriers: one runs its
+// matrix products while the other runs its softmax, so the matrix cores and
+// the vector ALUs of a SIMD work at the same time.  Per 128-key block:
 //   * K~ rows, the FP8 V tiles and Delta_S reach LDS by direct global->LDS
-//     loads (no registers, no VALU); V is double-buffered and loaded one
-//     block ahead, K~ is loaded as soon as every wave has finished its score
-//     products of the previous block;
+//     loads (no registers, no VALU), double-buffered and issued one block
+//     ahead by the first row group after its matrix products;
 //   * each wave computes S^T (keys x its 32 queries) on MFMA: with
 //     smoothing, a first bf16 step writes Delta_S * (1 / (gQ gK)) into the
 //     accumulator (the rank-one term of section 5.2 -- no element-wise add on
 //     the softmax path), then 8 f16 steps accumulate Q~ K~^T over the head
 //     dimension, the four 32-key tiles interleaved so no step waits on the
-//     previous one;
+//     previous one; Q~ stays in registers for the whole loop;
 //   * softmax in the S^T layout: each lane owns one query and 64 of the 128
 //     keys, so the row max is in-lane plus one exchange with lane ^ 32; the
 //     global scales and the softmax scale are one constant in the exp2
