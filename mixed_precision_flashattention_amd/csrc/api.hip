@@ -53,7 +53,8 @@ inline PrefillWs prefill_layout(int B, int Hkv, int N) {
   PrefillWs w;
   w.amax = 0;
   w.k_f16 = kAlign;
-  w.total = align_up(w.k_f16 + (size_t)B * Hkv * N * kD * 2);
+  // K~ block images: 32 KB per (batch, KV head, 128-key block)
+  w.total = align_up(w.k_f16 + (size_t)B * Hkv * ((N + kBlk - 1) / kBlk) * kBlk * kD * 2);
   return w;
 }
 
@@ -229,7 +230,7 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
   launch_fill_u32(amax, kAlign / 4, 0u, s);
   launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, delta_s ? q_mean : nullptr, amax, s);
-  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv * N, k_f16, s);
+  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_f16, s);
   PrefillParams p;
   p.q = q;
   p.q_bf16 = q_dtype == MPFA_BF16;

@@ -68,8 +68,8 @@ void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, 
                       hipStream_t st);
 
 // prefill.hip
-void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, uint8_t* k_f16,
-                     hipStream_t st);
+void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
+                     uint8_t* k_f16, hipStream_t st);
 void launch_prefill(const PrefillParams& p, hipStream_t st);
 
 // decode.hip

@@ -35,13 +35,18 @@
 namespace mpfa {
 
 constexpr int kUnitRows = 256;  // query rows per workgroup (two groups of 128)
-constexpr int kRowBytes = 256;  // one K~ or Q~ row in LDS: 128 f16
-// K~ in LDS: 256-byte rows whose 16 chunks of 16 bytes are permuted by key:
-// chunk c of key k sits at c ^ kswz(k).  A 16-lane pass of an operand read
-// touches keys {0-3, 32-35, 4-7, 36-39} + base of one chunk column, and
-// kswz gives those keys 16 distinct chunk slots, so no two lanes of a pass
-// share a bank.
-__device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+constexpr int kRowBytes = 256;  // one Q~ row in LDS: 128 f16
+// K~ block image (32 KB per 128 keys, the same bytes in the workspace and in
+// LDS): 16 chunk columns of 2 KB, one per 8 head-dim elements; chunk c of
+// key k sits at c * 2048 + 16 * kslot(k).  An operand read of head-dim step
+// kc is then a per-lane base plus the immediate kc * 2048 (no address
+// arithmetic per read), and a direct load is a contiguous 1 KB copy.  A
+// 16-lane pass of an operand read touches keys {0-3, 32-35, 4-7, 36-39} +
+// base in one chunk column; kslot moves keys 32-63 (mod 64) by 8 slots, so
+// those 16 keys fill 16 distinct 16-byte slots of a 256-byte bank window.
+constexpr int kKChunkBytes = kBlk * 16;
+constexpr int kKBlockBytes = kBlk * kRowBytes;
+__device__ __forceinline__ int kslot(int k) { return k ^ (((k >> 5) & 1) << 3); }
 // Q~ staging rows use chunk c ^ (row & 15): the operand read (16 rows, one
 // chunk column) and the quantizer's writes (8 rows x 8 chunk pairs) are both
 // spread over all 16 chunk slots.
@@ -62,22 +67,26 @@ __device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_addr) {
                : "v"(src), "s"(lds_addr)
                : "memory");
 }
+// The same with a uniform 64-bit base in SGPRs and a non-negative 32-bit
+// per-lane offset (the scalar-base form adds the offset zero-extended).
+__device__ __forceinline__ void lds_load16_s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory");
+}
 __device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// Wave w's share of K~ block k0 when NW waves load it: 1 KB pieces (4 rows
-// each) 32/NW w .. 32/NW (w+1) - 1.  Rows past the end repeat the last key;
-// those keys are masked out of the block.
+// Wave w's share of K~ block image kimg when NW waves load it: 1 KB pieces
+// 32/NW w .. 32/NW (w+1) - 1, each a contiguous copy (lane i moves bytes
+// 16 i .. 16 i + 15 of the piece).
 template <int NW>
-__device__ __forceinline__ void issue_k_block(const uint8_t* ktil, int N, int k0, uint32_t dst,
-                                              int w, int lane) {
+__device__ __forceinline__ void issue_k_block(const uint8_t* kimg, uint32_t dst, int w, int lane) {
 #pragma unroll
   for (int i = 0; i < 32 / NW; ++i) {
-    const int piece = (32 / NW) * w + i;  // 1 KB = rows 4 piece .. 4 piece + 3
-    const int r = 4 * piece + (lane >> 4);
-    const int chunk = (lane & 15) ^ kswz(r);  // the chunk that belongs in slot lane & 15
-    const int key = min(k0 + r, N - 1);
-    lds_load16(ktil + (int64_t)key * kRowBytes + 16 * chunk, dst + piece * 1024);
+    const int piece = (32 / NW) * w + i;
+    lds_load16_s(kimg + piece * 1024, 16 * lane, dst + piece * 1024);
   }
 }
 
@@ -129,12 +138,14 @@ __device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, in
 template <bool SMOOTH>
 __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
                                             const uint16_t* dblk, const int (&koff)[4],
-                                            const int (&ksw)[4], const i32x4 (&qf)[8],
+                                            const int (&kbase)[4], const i32x4 (&qf)[8],
                                             const i32x4& dB, int h) {
+  const uint8_t* at[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) at[t] = kblk + kbase[t];
   i32x4 a[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    a[0][t] = *reinterpret_cast<const i32x4*>(kblk + koff[t] * kRowBytes + 16 * ((8 * h) ^ ksw[t]));
+  for (int t = 0; t < 4; ++t) a[0][t] = *reinterpret_cast<const i32x4*>(at[t]);
   if (SMOOTH) {
     uint32_t dv[4];
 #pragma unroll
@@ -150,8 +161,7 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
     if (kc + 1 < 8) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        a[(kc + 1) & 1][t] = *reinterpret_cast<const i32x4*>(kblk + koff[t] * kRowBytes +
-                                                            16 * ((8 * h + kc + 1) ^ ksw[t]));
+        a[(kc + 1) & 1][t] = *reinterpret_cast<const i32x4*>(at[t] + (kc + 1) * kKChunkBytes);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int lim = p.causal ? min(my_row, N - 1) : N - 1;  // last visible key of this row
   const int ntiles32 = (N + 31) / 32;
   const int64_t kvh = (int64_t)b * p.Hkv + hk;
-  const uint8_t* ktil = p.k_f16 + kvh * N * kRowBytes;
+  const uint8_t* kimg = p.k_f16 + kvh * nblk_all * kKBlockBytes;
   const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * kVTileBytes;
   const uint16_t* dbase = SMOOTH ? p.delta_s + (int64_t)bh * N : nullptr;
   const uint32_t lds_k0 = lds_addr(smem_k[0]), lds_k1 = lds_addr(smem_k[1]);
@@ -361,11 +371,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // the block (hp, vp from rho below); the MFMA output register v of lane
   // half h then holds key 64*(t/2) + 32*h + 16*(t%2) + v.
   const int hp = (col >> 2) & 1, vp = ((col >> 3) << 2) | (col & 3);
-  int koff[4], ksw[4];
+  int koff[4], kbase[4];  // A-row key of tile t; its chunk 8 h in the block image
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     koff[t] = 64 * (t >> 1) + 32 * hp + 16 * (t & 1) + vp;
-    ksw[t] = kswz(koff[t]);
+    kbase[t] = 8 * h * kKChunkBytes + 16 * kslot(koff[t]);
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
   __syncthreads();  // Q~ and the LSE parts are consumed: LDS is free for the blocks
-  issue_k_block<8>(ktil, N, 0, lds_k0, wave, lane);
+  issue_k_block<8>(kimg, lds_k0, wave, lane);
   uint32_t dd = 0;
   if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 
@@ -396,7 +406,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #define MPFA_ISSUE(J)                                                                        \
   do {                                                                                       \
     if ((J) + 1 < n_max) {                                                                   \
-      issue_k_block<4>(ktil, N, ((J) + 1) * kBlk, ((J) & 1) ? lds_k0 : lds_k1, wave, lane);  \
+      issue_k_block<4>(kimg + (int64_t)((J) + 1) * kKBlockBytes, ((J) & 1) ? lds_k0 : lds_k1,   \
+                       wave, lane);                                                          \
       if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
     }                                                                                        \
     if ((J) < n_max)                                                                         \
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   do {                                                                                       \
     if ((J) >= 1 && (J) <= n_own) pv_block(o, smem_v[((J) - 1) & 1], pb, h, col);           \
     if ((J) < n_own) {                                                                       \
-      score_block<SMOOTH>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, ksw, qf, dB, h);    \
+      score_block<SMOOTH>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, kbase, qf, dB, h);  \
     } else {                                                                                 \
       /* defining s on this path too keeps the old scores from being live */                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \
@@ -477,27 +488,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
         kLn2 * (lam * m_run + log2f(l_tot)) - kLn2 * kLog2_448 + lse_off;
 }
 
-// K~ = E2M1 code value x E4M3 block scale in FP16, row-major [rows][128]:
-// one thread per 16-element block (8 code bytes, one scale byte -> 32 bytes).
+// K~ = E2M1 code value x E4M3 block scale in FP16, written as block images
+// (one 32 KB image per (batch, KV head, 128-key block), layout above); keys
+// past N in the last block are zero.  Thread g = ((image * 8) + e) * 128 +
+// slot expands 16-element block e of the key in that slot into chunks 2e and
+// 2e + 1, so consecutive threads write consecutive 16-byte slots.
 __global__ __launch_bounds__(256) void k_expand_k(const uint2* __restrict__ codes,
-                                                  const uint8_t* __restrict__ sf,
-                                                  int64_t n_blocks, uint4* __restrict__ out) {
+                                                  const uint8_t* __restrict__ sf, int N, int nkb,
+                                                  int64_t n_threads, uint4* __restrict__ out) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= n_blocks) return;
-  const uint2 w = codes[g];
-  const f16x2 s2 = e4m3_scale_f16x2(sf[g]);
-  uint32_t e[8];
-  expand_fp4x8(w.x, s2, e);
-  expand_fp4x8(w.y, s2, e + 4);
-  out[2 * g] = make_uint4(e[0], e[1], e[2], e[3]);
-  out[2 * g + 1] = make_uint4(e[4], e[5], e[6], e[7]);
+  if (g >= n_threads) return;
+  const int slot = (int)(g & (kBlk - 1));
+  const int e = (int)((g >> 7) & 7);
+  const int64_t img = g >> 10;  // bhk * nkb + kb
+  const int64_t bhk = img / nkb;
+  const int key = (int)(img - bhk * nkb) * kBlk + kslot(slot);
+  uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (key < N) {
+    const int64_t blk = ((bhk * N + key) << 3) + e;  // 16-element block in k_fp4 / k_sf
+    const uint2 w = codes[blk];
+    const f16x2 s2 = e4m3_scale_f16x2(sf[blk]);
+    expand_fp4x8(w.x, s2, v);
+    expand_fp4x8(w.y, s2, v + 4);
+  }
+  uint4* dst = out + img * (kKBlockBytes / 16) + (2 * e) * kBlk + slot;
+  dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
+  dst[kBlk] = make_uint4(v[4], v[5], v[6], v[7]);
 }
 
-void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t rows, uint8_t* k_f16,
-                     hipStream_t st) {
-  const int64_t n_blocks = rows * (kD / 16);
-  hipLaunchKernelGGL(k_expand_k, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint2*>(k_fp4), k_sf, n_blocks,
+void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
+                     uint8_t* k_f16, hipStream_t st) {
+  const int nkb = (N + kBlk - 1) / kBlk;
+  const int64_t n_threads = bhk * nkb * kBlk * 8;
+  hipLaunchKernelGGL(k_expand_k, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint2*>(k_fp4), k_sf, N, nkb, n_threads,
                      reinterpret_cast<uint4*>(k_f16));
 }
 

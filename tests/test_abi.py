@@ -77,8 +77,9 @@ def test_workspace_sizes(lib):
     assert ws(0, 1, 32, 8, 1024, 128, 1) > ws(0, 1, 0, 8, 1024, 128, 1)
     assert ws(1, 1, 0, 8, 1024, 128, 1) == 256
     # prefill: the Q amax slot + K expanded to FP16 (B * Hkv * N * 128 halves)
-    assert ws(2, 1, 32, 8, 1024, 128, 1) == 256 + 8 * 1024 * 256
-    assert ws(2, 2, 32, 8, 1001, 128, 1) == 256 + (2 * 8 * 1001 * 256 + 255) // 256 * 256
+    assert ws(2, 1, 32, 8, 1024, 128, 1) == 256 + 8 * 8 * 32768
+    assert ws(2, 2, 32, 8, 1001, 128, 1) == 256 + 2 * 8 * 8 * 32768
+    assert ws(2, 1, 4, 1, 1, 128, 1) == 256 + 32768
     assert ws(9, 1, 32, 8, 1024, 128, 1) == 0
     assert ws(3, 1, 32, 8, 1024, 128, 0) == 0
     assert ws(0, 0, 32, 8, 1024, 128, 1) == 0
