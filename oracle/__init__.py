@@ -234,11 +234,15 @@ def merge_states(m, l, acc, scale):
 
 
 from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
+    PAGE,
     Operands,
     append_kv,
+    append_kv_paged,
     decode,
+    decode_paged,
     decode_partitions,
     exact_attention,
+    gather_pages,
     prefill_rows,
     quantize_k,
     quantize_q,
@@ -251,5 +255,6 @@ __all__ = [
     "bf16_rne", "bf16_to_f64", "channel_mean", "amax", "nvfp4_global_scale", "nvfp4_quantize",
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
     "quantize_k", "quantize_v", "quantize_q", "prefill_rows", "decode", "decode_partitions",
-    "exact_attention", "Operands", "append_kv"
+    "exact_attention", "Operands", "append_kv", "PAGE", "gather_pages", "decode_paged",
+    "append_kv_paged"
 ]

@@ -333,6 +333,106 @@ def decode(q, k, v, q_mean, num_splits, scale, smooth=True, identity=False, out_
     return O, LSE
 
 
+# ------------------------------------------------------------ paged cache --
+PAGE = KV_BLOCK  # tokens per cache page
+
+
+def gather_pages(pool, block_table, b, n):
+    """Request b's first n positions of a paged cache, as a contiguous cache
+    with batch size 1 (the layout quantize_k / quantize_v / append_kv use).
+
+    pool: k_fp4 [P, Hkv, PAGE, D/2], k_sf [P, Hkv, PAGE, D/16], v_fp8 [P, Hkv,
+    PAGE, D] (row layout), optionally delta_s [P, Hq, PAGE], and the
+    per-request frozen scales k_gscale [B], v_scale [B].  Logical page i of
+    request b is physical page block_table[b, i] (MpFA §6 "Serving system":
+    the compensation side cache follows the same physical page indices)."""
+    npg = -(-n // PAGE)
+    pages = np.asarray(block_table[b, :npg], dtype=np.int64)
+
+    def rows(a):  # [npg, H, PAGE, ...] -> [1, H, npg * PAGE, ...][:, :, :n]
+        x = np.asarray(a)[pages]
+        x = np.moveaxis(x, 0, 1)
+        x = x.reshape((x.shape[0], npg * PAGE) + x.shape[3:])
+        return x[None, :, :n]
+
+    cache = {"k_fp4": rows(pool["k_fp4"]), "k_sf": rows(pool["k_sf"]), "v_fp8": rows(pool["v_fp8"]),
+             "k_gscale": np.float32(pool["k_gscale"][b]), "v_scale": np.float32(pool["v_scale"][b])}
+    if pool.get("delta_s") is not None:
+        cache["delta_s"] = rows(pool["delta_s"])
+    return cache
+
+
+def decode_paged(q, pool, block_table, seq_lens, q_mean, k_mean, num_splits, scale, out_f64=False):
+    """Split-KV decode over a paged cache with per-request lengths (MpFA §5.3;
+    §6 "Serving system": fixed-size pages, a constant number of KV
+    partitions, the Delta_S side cache indexed by the same pages).
+
+    q [B, Hq, D] (or [B, Hq, 1, D]); smoothing iff pool holds delta_s (then
+    q_mean [B, Hq, D] and k_mean [B, Hkv, D] are the frozen per-request means).
+    Readings: Q is quantized once over the whole query tensor of the call, as
+    in decode(); request b sees its first seq_lens[b] positions, clamped to
+    the capacity of its block-table row, cut into num_splits partitions of
+    its own (decode_partitions of its length); the K and V scales are the
+    request's own frozen scales.  A request with no positions returns O = 0
+    and LSE = -inf.  Returns (O [B, Hq, D], LSE [B, Hq])."""
+    q = np.asarray(q, dtype=F32)
+    if q.ndim == 3:
+        q = q[:, :, None, :]
+    B, Hq, _, D = q.shape
+    smooth = pool.get("delta_s") is not None
+    qm = np.asarray(q_mean, dtype=F32) if smooth else None
+    codes, sf, g = quantize_q(q, qm)
+    cap = block_table.shape[1] * PAGE
+    O = np.zeros((B, Hq, D), dtype=F64 if out_f64 else F32)
+    LSE = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(min(max(int(seq_lens[b]), 0), cap))
+        if n == 0:
+            continue
+        cache = gather_pages(pool, block_table, b, n)
+        ops = Operands.from_cache(q[b:b + 1], cache, n, q_mean=qm[b:b + 1] if smooth else None,
+                                  k_mean=np.asarray(k_mean)[b:b + 1] if smooth else None)
+        ops.q_codes, ops.q_sf, ops.q_gscale = codes[b:b + 1], sf[b:b + 1], g
+        o, lse = decode(q[b:b + 1], None, None, ops.k_mean, num_splits, scale, smooth=smooth,
+                        out_f64=out_f64, ops=ops)
+        O[b], LSE[b] = o[0], lse[0]
+    return O, LSE
+
+
+def append_kv_paged(k_new, v_new, pos, pool, block_table, q_mean=None, k_mean=None):
+    """Decode-time write of one new token per request into a paged cache (MpFA
+    §6 "Online quantization" and "Serving system"): the token of request b
+    goes to position pos[b], i.e. slot pos[b] % PAGE of physical page
+    block_table[b, pos[b] // PAGE], quantized as in append_kv with the
+    request's own frozen scales and means.  A request whose position is
+    outside its block-table row, or whose page index is outside the pool,
+    writes nothing.  k_new, v_new [B, Hkv, 1, D].  Returns an updated copy."""
+    k_new = np.asarray(k_new, dtype=F32)
+    v_new = np.asarray(v_new, dtype=F32)
+    B = k_new.shape[0]
+    out = {name: (np.array(a, copy=True) if isinstance(a, np.ndarray) else a) for name, a in pool.items()}
+    smooth = k_mean is not None
+    n_pages = out["k_fp4"].shape[0]
+    for b in range(B):
+        p = int(pos[b])
+        if p < 0 or p >= block_table.shape[1] * PAGE:
+            continue
+        pg = int(block_table[b, p // PAGE])
+        if pg < 0 or pg >= n_pages:
+            continue
+        page = {"k_fp4": out["k_fp4"][pg][None], "k_sf": out["k_sf"][pg][None],
+                "v_fp8": out["v_fp8"][pg][None], "k_gscale": out["k_gscale"][b],
+                "v_scale": out["v_scale"][b]}
+        if smooth:
+            page["delta_s"] = out["delta_s"][pg][None]
+        page = append_kv(k_new[b:b + 1], v_new[b:b + 1], [p % PAGE], page,
+                         q_mean=np.asarray(q_mean)[b:b + 1] if smooth else None,
+                         k_mean=np.asarray(k_mean)[b:b + 1] if smooth else None)
+        for name in ("k_fp4", "k_sf", "v_fp8") + (("delta_s",) if smooth else ()):
+            out[name][pg] = page[name][0]
+    return out
+
+
 def exact_attention(q, k, v, scale, causal=True, rows=None):
     """FP64 softmax(scale * Q K^T + mask) V and its natural-log LSE on the
     unquantized inputs (report-only error reference)."""
