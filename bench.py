@@ -13,7 +13,9 @@ the prefill call alone (the dominant kernel, against the mixed FP4/FP8 MFMA
 roofline), the direct (unsmoothed) prefill, the Qwen3-14B-shaped 32K causal
 prefill (40 query / 8 KV heads) against the same roofline, and the split-KV
 decode of the Llama-3.1-8B-shaped 128K cache (batch 16, 32 splits) as KV
-bytes per second against HBM bandwidth.  The CPU oracle is timed on a bounded sample of the
+bytes per second against HBM bandwidth, the same caches as a shuffled pool
+of 128-token pages (paged decode, full and ragged lengths), and the
+one-token cache write.  The CPU oracle is timed on a bounded sample of the
 prefill workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -199,6 +201,55 @@ def measure_prefill(mpfa, synth, dev, name, iters):
                          "frac": round(ach * 1e12 / PEAK_MIXED, 4),
                          "traffic": measured_traffic(f"mpfa_prefill {pcfg.name}")},
             "frac_of_fp16_fp8_instruction_peak": round(ach * 1e12 / PEAK_F16_FP8, 4)}
+
+
+def measure_decode_paged(mpfa, dcfg, dkq, dvq, dq, dout, dws, iters):
+    """The decode workload's caches scattered into a shuffled pool of 128-token
+    pages: the paged decode at every request's full length (same bytes as the
+    contiguous decode) and at ragged lengths (uniform in [N/8, N], seeded)."""
+    import torch
+    B, Hq, Hkv, N, D = dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.N, 128
+    P = mpfa.PAGE_SIZE
+    npg = N // P
+    g = torch.Generator(device="cpu").manual_seed(7)
+    perm = torch.randperm(B * npg, generator=g).to(dq.device)
+    pool = {}
+    for name, t, shape in (("k_fp4", dkq["k_fp4"], (B, Hkv, npg, P, 64)),
+                           ("k_sf", dkq["k_sf"], (B, Hkv, npg, P, 8)),
+                           ("v_fp8", dvq["v_fp8"], (B, Hkv, npg, 4, D, 32)),
+                           ("delta_s", dkq["delta_s"], (B, Hq, npg, P))):
+        x = t.reshape(shape).transpose(1, 2).reshape((B * npg,) + (shape[1],) + shape[3:])
+        pool[name] = torch.empty_like(x)
+        pool[name][perm] = x
+    pool["k_gscale"] = dkq["k_gscale"].reshape(1).repeat(B).contiguous()
+    pool["v_scale"] = dvq["v_scale"].reshape(1).repeat(B).contiguous()
+    pool["q_mean"], pool["k_mean"] = dkq["q_mean"], dkq["k_mean"]
+    table = perm.reshape(B, npg).to(torch.int32).contiguous()
+    full = torch.full((B,), N, dtype=torch.int32, device=dq.device)
+    ragged_host = torch.randint(N // 8, N + 1, (B,), generator=g, dtype=torch.int32)
+    ragged = ragged_host.to(dq.device)
+
+    def call(lens):
+        mpfa.decode_paged(dq, pool, table, lens, dcfg.scale, dcfg.num_splits, out=dout, ws=dws)
+
+    ms_full = time_calls(lambda: call(full), iters, 3)
+    ms_rag = time_calls(lambda: call(ragged), iters, 3)
+    per_tok = Hkv * (64 + 8 + 128) + Hq * 2
+    by_full = B * N * per_tok
+    by_rag = int(ragged_host.sum()) * per_tok
+    gbs_full = by_full / (ms_full * 1e-3) / 1e9
+    gbs_rag = by_rag / (ms_rag * 1e-3) / 1e9
+    log(f"[bench] paged decode {ms_full:.3f} ms -> {gbs_full:.0f} GB/s; ragged lengths "
+        f"{ms_rag:.3f} ms -> {gbs_rag:.0f} GB/s")
+    del pool, table
+    torch.cuda.empty_cache()
+    return {"workload": dcfg.name + " in 128-token pages (shuffled)", "ms": round(ms_full, 4),
+            "value": round(gbs_full, 1), "unit": "GB/s", "bytes_per_call": by_full,
+            "roofline": {"bound": "hbm", "achieved": round(gbs_full, 1), "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": round(gbs_full * 1e9 / PEAK_HBM, 4),
+                         "traffic": None},
+            "ragged": {"lengths": "uniform in [N/8, N], seed 7", "tokens": int(ragged_host.sum()),
+                       "ms": round(ms_rag, 4), "GBps": round(gbs_rag, 1)}}
 
 
 def write_traffic(run_dir, args):
@@ -486,6 +537,8 @@ def main():
         ms_app = time_calls(lambda: mpfa.append_kv(kn, vn, pos, dkq, dvq), max(args.steps, 10), 3)
         log(f"[bench] append of one token per request: {ms_app * 1e3:.1f} us")
         result["decode"]["append_one_token_us"] = round(ms_app * 1e3, 2)
+        result["decode_paged"] = measure_decode_paged(mpfa, dcfg, dkq, dvq, dq, dout, dws,
+                                                      max(args.steps, 10))
         del dkq, dvq, dq, dout, dws, dx, kn, vn, pos
         torch.cuda.empty_cache()
 

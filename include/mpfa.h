@@ -167,6 +167,44 @@ int mpfa_append_kv(const void* k_new, const void* v_new, int kv_dtype, int B, in
                    void* stream);
 
 /*
+ * Paged caches (paper section 6 "Serving system": fixed-size cache pages, a
+ * constant number of KV partitions, the Delta_S side cache following the
+ * same physical page indices).  A pool of num_pages pages of page_size = 128
+ * tokens (one softmax block; other sizes give MPFA_ERR_UNSUPPORTED):
+ *   k_fp4   [num_pages, Hkv, 128, 64]      NVFP4 codes (element 2t low nibble)
+ *   k_sf    [num_pages, Hkv, 128, 8]       E4M3 block scales
+ *   v_fp8   [num_pages, Hkv, 4, 128, 32]   FP8 V, four head-dim-major 32-token tiles
+ *   delta_s [num_pages, Hq, 128]           bf16 compensation entries (smoothing)
+ * block_table: device int32 [B, max_pages]; logical page i of request b
+ * (its positions 128 i .. 128 i + 127) is physical page block_table[b, i].
+ * A page belongs to one request: its Delta_S rows are that request's query
+ * heads.  k_gscale and v_scale are per request: device float [B], the
+ * scales each request's cache was quantized with (frozen at its prefill).
+ */
+
+/*
+ * mpfa_append_kv_paged -- decode-time write of one new token per request
+ * into a paged cache (paper section 6 "Online quantization" and "Serving
+ * system"); the quantization is that of mpfa_append_kv with request b's
+ * frozen scales k_gscale[b], v_scale[b] and means.
+ *
+ * k_new, v_new: [B, Hkv, 1, 128] in kv_dtype; the token of request b goes to
+ * position pos[b] (device int32 [B]), i.e. slot pos[b] % 128 of page
+ * block_table[b, pos[b] / 128].  Read on the device: a request with pos[b]
+ * outside [0, 128 max_pages) or a page index outside [0, num_pages) is
+ * skipped (nothing written for it).  Smoothing iff k_mean != NULL; then
+ * q_mean [B, Hq, 128] and delta_s are required and Hq / Hkv <= 120.
+ * No workspace.  Returns MPFA_ERR_INVALID for max_pages < 1, num_pages < 1,
+ * null or misaligned pointers, delta_s without k_mean.
+ */
+int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int B, int Hkv, int D,
+                         const int32_t* pos, const int32_t* block_table, int max_pages,
+                         int num_pages, int page_size, int Hq, const float* q_mean,
+                         const float* k_mean, const float* k_gscale, const float* v_scale,
+                         uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta_s,
+                         void* stream);
+
+/*
  * mpfa_prefill -- QK4PV8 attention over a whole sequence (paper section 5.1,
  * "second stage"; sections 5.2, 4.1).
  *
@@ -216,6 +254,36 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
                 const float* v_scale, const uint16_t* delta_s, float softmax_scale,
                 int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
                 void* stream);
+
+/*
+ * mpfa_decode_paged -- mpfa_decode over a paged cache (layout above) with
+ * per-request lengths: request b attends to its positions
+ * 0 .. seq_lens[b] - 1 (seq_lens: device int32 [B], read on the device and
+ * clamped to [0, 128 max_pages]), cut into num_splits partitions of whole
+ * 128-key blocks by its own length (partition length
+ * 128 * ceil(seq_lens[b] / (128 * num_splits))), with its own frozen scales
+ * k_gscale[b], v_scale[b].  Q is quantized once over the whole [B, Hq]
+ * query tensor of the call, as in mpfa_decode.  A request with no positions
+ * returns O = 0 and LSE = -inf.  Page slots past a request's length are
+ * never used (their V bytes are masked, whatever they hold).  Page indices
+ * are read on the device; one outside [0, num_pages) is clamped into the
+ * pool (every access stays inside it; that request's result is unspecified).
+ *
+ * q: [B, Hq, 1, 128]; q_mean [B, Hq, 128] and k_mean [B, Hkv, 128] the frozen
+ * per-request means (smoothing iff delta_s != NULL).  out: [B, Hq, 128];
+ * lse: [B, Hq] or NULL.  Hq / Hkv <= MPFA_DECODE_MAX_GROUP.
+ * ws: mpfa_workspace_bytes(MPFA_OP_DECODE, B, Hq, Hkv, 1, 128, num_splits)
+ * (the decode workspace does not depend on the lengths).
+ * Returns MPFA_ERR_INVALID for num_splits, max_pages or num_pages < 1, null or
+ * misaligned pointers, 128 max_pages + 128 num_splits >= 2^31.
+ */
+int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
+                      const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                      const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                      const float* v_scale, const uint16_t* delta_s, const int32_t* block_table,
+                      const int32_t* seq_lens, int max_pages, int num_pages, int page_size,
+                      float softmax_scale, int num_splits, void* out, int out_dtype, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,9 @@ HEAD_DIM = 128
 V_TILE = 32  # tokens per head-dim-major V tile
 
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
-           "mpfa_quantize_v_fp8", "mpfa_append_kv", "mpfa_prefill", "mpfa_decode")
+           "mpfa_quantize_v_fp8", "mpfa_append_kv", "mpfa_append_kv_paged", "mpfa_prefill",
+           "mpfa_decode", "mpfa_decode_paged")
+PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
 
@@ -66,6 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_decode.restype = i32
     L.mpfa_decode.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
                               P, i32, P, P, sz, P]
+    L.mpfa_append_kv_paged.restype = i32
+    L.mpfa_append_kv_paged.argtypes = [P, P, i32, i32, i32, i32, P, P, i32, i32, i32, i32, P, P, P,
+                                       P, P, P, P, P, P]
+    L.mpfa_decode_paged.restype = i32
+    L.mpfa_decode_paged.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32,
+                                    i32, i32, f32, i32, P, i32, P, P, sz, P]
     _lib = L
     return L
 
@@ -188,6 +196,47 @@ def mpfa_decode(q, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_sc
     _raise("mpfa_decode", st)
 
 
+def _int32(*ts):
+    import torch
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise TypeError("block tables, lengths and positions must be int32 tensors")
+
+
+def mpfa_append_kv_paged(k_new, v_new, pos, block_table, q_mean, k_mean, k_gscale, v_scale, k_fp4,
+                         k_sf, v_fp8, delta_s, Hq=None, stream=None):
+    """k_new, v_new [B, Hkv, 1, 128]; pos, block_table int32 [B], [B, max_pages];
+    a page pool k_fp4 [P, Hkv, 128, 64] ... (smoothing iff k_mean is given)."""
+    _check(k_new, v_new, pos, block_table, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8,
+           delta_s)
+    _int32(pos, block_table)
+    B, Hkv, _, D = k_new.shape
+    if Hq is None:
+        Hq = q_mean.shape[1] if q_mean is not None else 0
+    st = load_library().mpfa_append_kv_paged(
+        _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, D, _ptr(pos), _ptr(block_table),
+        block_table.shape[1], k_fp4.shape[0], PAGE_SIZE, Hq, _ptr(q_mean), _ptr(k_mean),
+        _ptr(k_gscale), _ptr(v_scale), _ptr(k_fp4), _ptr(k_sf), _ptr(v_fp8), _ptr(delta_s),
+        _stream(stream))
+    _raise("mpfa_append_kv_paged", st)
+
+
+def mpfa_decode_paged(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
+                      block_table, seq_lens, softmax_scale, num_splits, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, block_table, seq_lens,
+           out, lse, ws)
+    _int32(block_table, seq_lens)
+    B, Hq = q.shape[0], q.shape[1]
+    D = q.shape[-1]
+    st = load_library().mpfa_decode_paged(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf),
+        _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s), _ptr(block_table),
+        _ptr(seq_lens), block_table.shape[1], k_fp4.shape[0], PAGE_SIZE, float(softmax_scale),
+        int(num_splits), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_decode_paged", st)
+
+
 # ------------------------------------------------------ allocating helpers --
 def _workspace(op, B, Hq, Hkv, N, num_splits, device):
     import torch
@@ -286,6 +335,42 @@ def append_kv(k_new, v_new, pos, kq, vq, stream=None):
                    kq.get("k_mean") if smooth else None, kq["k_gscale"], vq["v_scale"],
                    kq["k_fp4"], kq["k_sf"], vq["v_fp8"], kq.get("delta_s") if smooth else None,
                    stream=stream)
+
+
+def decode_paged(q, pool, block_table, seq_lens, softmax_scale, num_splits, out_dtype=None,
+                 with_lse=False, ws=None, out=None, lse=None, stream=None):
+    """Split-KV decode over a paged cache.  pool: k_fp4 [P, Hkv, 128, 64],
+    k_sf [P, Hkv, 128, 8], v_fp8 [P, Hkv, 4, 128, 32], per-request k_gscale
+    and v_scale [B] and, in smoothing mode, delta_s [P, Hq, 128], q_mean
+    [B, Hq, 128], k_mean [B, Hkv, 128].  Returns (out [B, Hq, 128], lse or None)."""
+    import torch
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = pool["k_fp4"].shape[1]
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(MPFA_OP_DECODE, B, Hq, Hkv, 1, num_splits, q.device)
+    smooth = pool.get("delta_s") is not None
+    mpfa_decode_paged(q, Hkv, pool.get("q_mean") if smooth else None,
+                      pool.get("k_mean") if smooth else None, pool["k_fp4"], pool["k_sf"],
+                      pool["k_gscale"], pool["v_fp8"], pool["v_scale"],
+                      pool.get("delta_s") if smooth else None, block_table, seq_lens, softmax_scale,
+                      num_splits, out, lse if with_lse else None, ws, stream=stream)
+    return out, (lse if with_lse else None)
+
+
+def append_kv_paged(k_new, v_new, pos, pool, block_table, stream=None):
+    """Write one new token per request into a paged cache (pool as in
+    decode_paged) at positions pos[b], with each request's frozen means and
+    scales; smoothing iff the pool holds delta_s."""
+    smooth = pool.get("delta_s") is not None
+    mpfa_append_kv_paged(k_new, v_new, pos, block_table, pool.get("q_mean") if smooth else None,
+                         pool.get("k_mean") if smooth else None, pool["k_gscale"], pool["v_scale"],
+                         pool["k_fp4"], pool["k_sf"], pool["v_fp8"],
+                         pool.get("delta_s") if smooth else None, stream=stream)
 
 
 def v_tiles_to_rows(v_fp8_tiled, N: int):

@@ -202,6 +202,42 @@ int mpfa_append_kv(const void* k_new, const void* v_new, int kv_dtype, int B, in
   return launch_status();
 }
 
+int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int B, int Hkv, int D,
+                         const int32_t* pos, const int32_t* block_table, int max_pages,
+                         int num_pages, int page_size, int Hq, const float* q_mean,
+                         const float* k_mean, const float* k_gscale, const float* v_scale,
+                         uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta_s,
+                         void* stream) {
+  int st = check_sizes(B, Hkv, 1, D);
+  if (st) return st;
+  if (!dtype_ok(kv_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (page_size != kBlk) return MPFA_ERR_UNSUPPORTED;
+  if (max_pages < 1 || num_pages < 1 || (int64_t)max_pages * kBlk > (int64_t)INT32_MAX)
+    return MPFA_ERR_INVALID;
+  if ((int64_t)B * Hkv > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+  if (!k_new || !v_new || !pos || !block_table || !k_gscale || !v_scale || !k_fp4 || !k_sf ||
+      !v_fp8)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_fp4) || !aligned16(k_sf) ||
+      !aligned16(v_fp8))
+    return MPFA_ERR_INVALID;
+  const bool smooth = k_mean != nullptr;
+  int G = 0;
+  if (smooth) {
+    if (!q_mean || !delta_s) return MPFA_ERR_INVALID;
+    if ((st = check_heads(Hq, Hkv, B))) return st;
+    G = Hq / Hkv;
+    if (G > kD - 8) return MPFA_ERR_UNSUPPORTED;
+  } else if (delta_s) {
+    return MPFA_ERR_INVALID;  // a compensation cache needs the means
+  }
+  launch_append_kv_paged(k_new, v_new, kv_dtype == MPFA_BF16, B, Hkv, G, pos, block_table,
+                         max_pages, num_pages, smooth ? q_mean : nullptr, k_mean, k_gscale,
+                         v_scale, k_fp4, k_sf, v_fp8, smooth ? delta_s : nullptr,
+                         (hipStream_t)stream);
+  return launch_status();
+}
+
 int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
@@ -314,6 +350,80 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   p.out = out;
   p.out_bf16 = out_dtype == MPFA_BF16;
   p.lse = lse;
+  p.paged = 0;
+  p.block_table = nullptr;
+  p.seq_lens = nullptr;
+  p.max_pages = p.num_pages = 0;
+  launch_decode(p, s);
+  return launch_status();
+}
+
+int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
+                      const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                      const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                      const float* v_scale, const uint16_t* delta_s, const int32_t* block_table,
+                      const int32_t* seq_lens, int max_pages, int num_pages, int page_size,
+                      float softmax_scale, int num_splits, void* out, int out_dtype, float* lse,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(B, Hkv, 1, D);
+  if (st) return st;
+  if ((st = check_heads(Hq, Hkv, B))) return st;
+  if (Hq / Hkv > MPFA_DECODE_MAX_GROUP) return MPFA_ERR_UNSUPPORTED;
+  if (page_size != kBlk) return MPFA_ERR_UNSUPPORTED;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (num_splits < 1 || max_pages < 1 || num_pages < 1) return MPFA_ERR_INVALID;
+  if ((int64_t)max_pages * kBlk + (int64_t)kBlk * num_splits > (int64_t)INT32_MAX)
+    return MPFA_ERR_INVALID;
+  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !block_table || !seq_lens ||
+      !out || !ws)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_fp8) ||
+      !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
+    return MPFA_ERR_INVALID;
+  if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
+                  !aligned16(delta_s)))
+    return MPFA_ERR_INVALID;
+  if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
+  if ((int64_t)B * Hkv * num_splits > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+  const DecodeWs L = decode_layout(B, Hq, num_splits);
+  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  uint32_t* amax = (uint32_t*)(w + L.amax);
+  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
+  DecodeParams p;
+  p.q = q;
+  p.q_bf16 = q_dtype == MPFA_BF16;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = 0;  // per request
+  p.G = Hq / Hkv;
+  p.P = num_splits;
+  p.chunk = 0;
+  p.q_mean = delta_s ? q_mean : nullptr;
+  p.k_mean = delta_s ? k_mean : nullptr;
+  p.k_fp4 = k_fp4;
+  p.k_sf = k_sf;
+  p.k_gscale = k_gscale;
+  p.v_fp8 = v_fp8;
+  p.v_scale = v_scale;
+  p.delta_s = delta_s;
+  p.scale = softmax_scale;
+  p.q_amax = amax;
+  p.ws_m = (float*)(w + L.m);
+  p.ws_l = (float*)(w + L.l);
+  p.ws_acc = (float*)(w + L.acc);
+  p.out = out;
+  p.out_bf16 = out_dtype == MPFA_BF16;
+  p.lse = lse;
+  p.paged = 1;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
   launch_decode(p, s);
   return launch_status();
 }

@@ -13,6 +13,12 @@
 // operand (V^T) is read directly from the head-dim-major V tiles.  Each
 // partition leaves (m, l, acc) in the workspace; a second kernel merges the
 // partitions by log-sum-exp.
+//
+// The same kernels serve a paged cache (paper section 6 "Serving system"):
+// 128-token pages (one softmax block each), a block table per request, the
+// Delta_S side cache indexed by the same physical pages, per-request lengths
+// and frozen scales; the number of partitions stays fixed and each request
+// is cut into them by its own length.
 #include "mpfa_internal.hpp"
 
 namespace mpfa {
@@ -33,35 +39,77 @@ struct DecodeBlockRegs {
   i32x8 v[8];
 };
 
+// Where the 128-key block starting at key k0 lives: its first K code row,
+// scale row, V tile and Delta_S entry (row g of the group at d + g * dstride),
+// and the last key / tile index inside the block that holds data.
+struct DecodeBlockPtrs {
+  const uint8_t* k;
+  const uint8_t* s;
+  const uint8_t* v;
+  const uint16_t* d;
+  int64_t dstride;
+  int klast, vlast;
+};
+
 struct DecodeCtx {
   const uint8_t* kbase;
   const uint8_t* sbase;
   const uint8_t* vbase;
   const uint16_t* dbase;  // Delta_S row of the group's first query head
   int N, G, ntiles32;
+  // paged cache: this request's block-table row, the pool size and strides
+  const int32_t* table;
+  int num_pages, Hkv, hk, Hq;
+  int64_t hq0;
 };
 
-// Keys past the end are clamped to the last token (and masked later).
-template <bool SMOOTH>
+template <bool PAGED>
+__device__ __forceinline__ DecodeBlockPtrs block_ptrs(const DecodeCtx& c, int k0) {
+  DecodeBlockPtrs b;
+  if (PAGED) {
+    // a page index outside the pool is clamped into it (the result for such
+    // a request is unspecified, but every access stays inside the pool)
+    const int pg = min(max(c.table[k0 / kBlk], 0), c.num_pages - 1);
+    const int64_t slab = (int64_t)pg * c.Hkv + c.hk;
+    b.k = c.kbase + slab * kBlk * 64;
+    b.s = c.sbase + slab * kBlk * 8;
+    b.v = c.vbase + slab * 4 * kVTileBytes;
+    b.d = c.dbase ? c.dbase + ((int64_t)pg * c.Hq + c.hq0) * kBlk : nullptr;
+    b.dstride = kBlk;
+    b.klast = kBlk - 1;
+    b.vlast = 3;
+  } else {
+    b.k = c.kbase + (int64_t)k0 * 64;
+    b.s = c.sbase + (int64_t)k0 * 8;
+    b.v = c.vbase + (int64_t)(k0 / 32) * kVTileBytes;
+    b.d = c.dbase ? c.dbase + k0 : nullptr;
+    b.dstride = c.N;
+    b.klast = c.N - 1 - k0;  // keys past the end are clamped to the last one (masked later)
+    b.vlast = c.ntiles32 - 1 - k0 / 32;
+  }
+  return b;
+}
+
+template <bool SMOOTH, bool PAGED>
 __device__ __forceinline__ void decode_load(DecodeBlockRegs& r, const DecodeCtx& c, int k0,
                                             int lane) {
   const int h = lane >> 5, col = lane & 31;
+  const DecodeBlockPtrs bp = block_ptrs<PAGED>(c, k0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int key = min(k0 + 32 * t + col, c.N - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(c.kbase + (int64_t)key * 64 + 32 * h);
+    const int key = min(32 * t + col, bp.klast);
+    const uint4* src = reinterpret_cast<const uint4*>(bp.k + (int64_t)key * 64 + 32 * h);
     r.k[t][0] = src[0];
     r.k[t][1] = src[1];
-    r.sc[t] = *reinterpret_cast<const uint32_t*>(c.sbase + (int64_t)key * 8 + 4 * h);
+    r.sc[t] = *reinterpret_cast<const uint32_t*>(bp.s + (int64_t)key * 8 + 4 * h);
     if (SMOOTH) {
 #pragma unroll
       for (int g = 0; g < 8; ++g)
-        r.dl[t][g] = g < c.G ? c.dbase[(int64_t)g * c.N + key] : 0u;
+        r.dl[t][g] = g < c.G ? bp.d[(int64_t)g * bp.dstride + key] : 0u;
     }
   }
   const int n = lane & 15, kg = lane >> 4;
-  const int tt = min(k0 / 32 + kg, c.ntiles32 - 1);
-  const uint8_t* vt = c.vbase + (int64_t)tt * kVTileBytes;
+  const uint8_t* vt = bp.v + (int64_t)min(kg, bp.vlast) * kVTileBytes;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) r.v[dt] = *reinterpret_cast<const i32x8*>(vt + (16 * dt + n) * 32);
 }
@@ -143,12 +191,27 @@ __device__ __forceinline__ void decode_compute(const DecodeBlockRegs& r, DecodeS
   const i32x8 pbv = n < 8 ? *reinterpret_cast<const i32x8*>(sp + n * kPStride + 32 * kg)
                           : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   const float a_o = n < 8 ? salpha[n] : 1.0f;
+  if (k0 + kBlk > p1) {
+    // The last block of the range: V bytes of keys past its end may be bytes
+    // nobody wrote (a NaN code times P = 0 would still be NaN), so they are
+    // cleared.  Lane group kg holds keys k0 + 32 kg .. + 31, 4 per dword.
+    const int nv = min(max(p1 - (k0 + 32 * kg), 0), 32);
+    i32x8 vm;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma16_fp8(r.v[dt], pbv, st.o[dt] * a_o);
+    for (int w = 0; w < 8; ++w) {
+      const int keep = min(max(nv - 4 * w, 0), 4);
+      vm[w] = keep == 4 ? -1 : (int)((1u << (8 * keep)) - 1u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma16_fp8(r.v[dt] & vm, pbv, st.o[dt] * a_o);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma16_fp8(r.v[dt], pbv, st.o[dt] * a_o);
+  }
   __syncthreads();
 }
 
-template <bool SMOOTH>
+template <bool SMOOTH, bool PAGED>
 __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   __shared__ __align__(16) uint8_t sq[8 * kQStride];
   __shared__ __align__(16) uint8_t sp[8 * kPStride];
@@ -160,8 +223,12 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)hk * G;  // first query head of the group
-  const int p0 = part * p.chunk;
-  const int p1 = min(p0 + p.chunk, N);
+  // paged: this request's length, clamped to its block-table row, cut into
+  // P partitions of whole 128-key blocks
+  const int Nb = PAGED ? min(max(p.seq_lens[b], 0), p.max_pages * kBlk) : N;
+  const int chunk = PAGED ? (Nb + kBlk * P - 1) / (kBlk * P) * kBlk : p.chunk;
+  const int p0 = part * chunk;
+  const int p1 = min(p0 + chunk, Nb);
 
   if (p0 >= p1) {  // empty partition: neutral state
     if (lane < G) {
@@ -174,7 +241,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   }
 
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
-  const float gK = *p.k_gscale;
+  const float gK = PAGED ? p.k_gscale[b] : *p.k_gscale;
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;
 
@@ -228,11 +295,24 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   c.N = N;
   c.G = G;
   c.ntiles32 = (N + 31) / 32;
-  const int64_t kvh = (int64_t)b * p.Hkv + hk;
-  c.kbase = p.k_fp4 + kvh * N * 64;
-  c.sbase = p.k_sf + kvh * N * 8;
-  c.vbase = p.v_fp8 + kvh * c.ntiles32 * kVTileBytes;
-  c.dbase = SMOOTH ? p.delta_s + hq0 * N : nullptr;
+  if (PAGED) {
+    c.kbase = p.k_fp4;
+    c.sbase = p.k_sf;
+    c.vbase = p.v_fp8;
+    c.dbase = SMOOTH ? p.delta_s : nullptr;
+    c.table = p.block_table + (int64_t)b * p.max_pages;
+    c.num_pages = p.num_pages;
+    c.Hkv = p.Hkv;
+    c.hk = hk;
+    c.Hq = p.Hq;
+    c.hq0 = (int64_t)hk * G;  // the group's first query head within the page's Hq rows
+  } else {
+    const int64_t kvh = (int64_t)b * p.Hkv + hk;
+    c.kbase = p.k_fp4 + kvh * N * 64;
+    c.sbase = p.k_sf + kvh * N * 8;
+    c.vbase = p.v_fp8 + kvh * c.ntiles32 * kVTileBytes;
+    c.dbase = SMOOTH ? p.delta_s + hq0 * N : nullptr;
+  }
 
   DecodeState st;
 #pragma unroll
@@ -246,12 +326,12 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   // Two register stages: the loads of the next block are in flight while
   // the current one is computed.
   DecodeBlockRegs ra, rb;
-  decode_load<SMOOTH>(ra, c, p0, lane);
+  decode_load<SMOOTH, PAGED>(ra, c, p0, lane);
   for (int k0 = p0; k0 < p1; k0 += 2 * kBlk) {
-    if (k0 + kBlk < p1) decode_load<SMOOTH>(rb, c, k0 + kBlk, lane);
+    if (k0 + kBlk < p1) decode_load<SMOOTH, PAGED>(rb, c, k0 + kBlk, lane);
     decode_compute<SMOOTH>(ra, st, k0, p1, lane, lam, qa, dA, sp, salpha);
     if (k0 + kBlk >= p1) break;
-    if (k0 + 2 * kBlk < p1) decode_load<SMOOTH>(ra, c, k0 + 2 * kBlk, lane);
+    if (k0 + 2 * kBlk < p1) decode_load<SMOOTH, PAGED>(ra, c, k0 + 2 * kBlk, lane);
     decode_compute<SMOOTH>(rb, st, k0 + kBlk, p1, lane, lam, qa, dA, sp, salpha);
   }
 
@@ -284,8 +364,9 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
   const int bhq = blockIdx.x;
   const int d = threadIdx.x;
   const int P = p.P;
+  const int b = bhq / p.Hq;
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
-  const float gK = *p.k_gscale;
+  const float gK = p.paged ? p.k_gscale[b] : *p.k_gscale;
   const float lam = p.scale * kLog2e * gQ * gK;
   const float* wm = p.ws_m + (int64_t)bhq * P;
   const float* wl = p.ws_l + (int64_t)bhq * P;
@@ -300,7 +381,9 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
     l = fmaf(w, wl[i], l);
     acc = fmaf(w, wa[(int64_t)i * kD + d], acc);
   }
-  const float o = acc * (*p.v_scale / l);
+  // a request with no keys (paged, length 0) has l = 0: O = 0, LSE = -inf
+  const float vs = p.paged ? p.v_scale[b] : *p.v_scale;
+  const float o = l > 0.0f ? acc * (vs / l) : 0.0f;
   if (p.out_bf16)
     reinterpret_cast<uint16_t*>(p.out)[(int64_t)bhq * kD + d] = (uint16_t)bf16_rne(o);
   else
@@ -308,7 +391,7 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
   if (p.lse) {
     float off = 0.0f;
     if (p.delta_s) {
-      const int b = bhq / p.Hq, hk = (bhq % p.Hq) / p.G;
+      const int hk = (bhq % p.Hq) / p.G;
       red[d] = load_elem(p.q, (int64_t)bhq * kD + d, p.q_bf16) *
                p.k_mean[((int64_t)b * p.Hkv + hk) * kD + d];
       __syncthreads();
@@ -318,16 +401,23 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
       }
       off = p.scale * red[0];
     }
-    if (d == 0) p.lse[bhq] = kLn2 * (lam * m + log2f(l)) - kLn2 * kLog2_448 + off;
+    if (d == 0)
+      p.lse[bhq] = l > 0.0f ? kLn2 * (lam * m + log2f(l)) - kLn2 * kLog2_448 + off : -INFINITY;
   }
 }
 
 void launch_decode(const DecodeParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.P);
-  if (p.delta_s)
-    hipLaunchKernelGGL(k_decode_split<true>, dim3(grid), dim3(64), 0, st, p);
-  else
-    hipLaunchKernelGGL(k_decode_split<false>, dim3(grid), dim3(64), 0, st, p);
+  if (p.paged) {
+    if (p.delta_s)
+      hipLaunchKernelGGL((k_decode_split<true, true>), dim3(grid), dim3(64), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_decode_split<false, true>), dim3(grid), dim3(64), 0, st, p);
+  } else if (p.delta_s) {
+    hipLaunchKernelGGL((k_decode_split<true, false>), dim3(grid), dim3(64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((k_decode_split<false, false>), dim3(grid), dim3(64), 0, st, p);
+  }
   hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(p.B * p.Hq)), dim3(128), 0, st, p);
 }
 

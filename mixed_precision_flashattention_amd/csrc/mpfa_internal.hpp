@@ -45,6 +45,12 @@ struct DecodeParams {
   void* out;
   int out_bf16;
   float* lse;
+  // paged cache (k_gscale and v_scale are then per request, [B]): logical
+  // 128-token page i of request b is physical page block_table[b * max_pages + i]
+  int paged;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_pages, num_pages;
 };
 
 // quant.hip
@@ -66,6 +72,11 @@ void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, 
                       const float* k_mean, const float* k_gscale, const float* v_scale,
                       uint8_t* k_fp4, uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta,
                       hipStream_t st);
+void launch_append_kv_paged(const void* k_new, const void* v_new, int is_bf16, int B, int Hkv,
+                            int G, const int32_t* pos, const int32_t* block_table, int max_pages,
+                            int num_pages, const float* q_mean, const float* k_mean,
+                            const float* k_gscale, const float* v_scale, uint8_t* k_fp4,
+                            uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta, hipStream_t st);
 
 // prefill.hip
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,

@@ -267,14 +267,60 @@ __global__ void k_quantize_v(const void* __restrict__ v, int is_bf16, int N, int
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-// Decode-time cache write of T new tokens per (batch, KV head) (paper
-// section 6 "Online quantization": the new token is centred against the
-// frozen per-request means and quantized with the cache's frozen scales; its
-// compensation entries are written in the same pass).  Block = 128 threads
-// for one (b, hk, token): thread d centres channel d into LDS and writes its
-// FP8 V byte; threads 0-7 then quantize the row's eight NVFP4 blocks and
-// threads 8 .. 8+G-1 its G Delta_S entries (FP64 over ascending channels).
-// A batch entry whose position is outside [0, N_cap - T] is skipped whole.
+// Decode-time cache write (paper section 6 "Online quantization": the new
+// token is centred against the frozen per-request means and quantized with
+// the cache's frozen scales; its compensation entries are written in the
+// same pass).  Block = 128 threads for one (b, hk, token): thread d centres
+// channel d into LDS and writes its FP8 V byte; threads 0-7 then quantize
+// the row's eight NVFP4 blocks and threads 8 .. 8+G-1 its G Delta_S entries
+// (FP64 over ascending channels).
+//
+// Where one appended token goes: its K code row (64 bytes), scale row (8
+// bytes), the V byte of channel 0 (channel d at + 32 d), and the Delta_S
+// entry of the group's first query head (head g at + g * dstride).
+struct AppendDst {
+  uint8_t* k;
+  uint8_t* s;
+  uint8_t* v;
+  uint16_t* d;
+  int64_t dstride;
+};
+
+__device__ __forceinline__ void append_token(const void* k_new, const void* v_new, int is_bf16,
+                                             int64_t src_row, const float* k_mean_row,
+                                             const float* q_mean_g0, int G, float gK, float vS,
+                                             const AppendDst& o, float* kc) {
+  const int d = threadIdx.x;
+  const int64_t src = src_row * kD + d;
+  float x = load_elem(k_new, src, is_bf16);
+  if (k_mean_row) x = x - k_mean_row[d];
+  kc[d] = x;
+  o.v[d * 32] = (uint8_t)e4m3_encode(load_elem(v_new, src, is_bf16) / vS);
+  __syncthreads();
+  if (d < 8) {
+    float xb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xb[j] = kc[16 * d + j];
+    uint32_t c[16];
+    const uint32_t sc = nvfp4_block(xb, gK, c);
+    uint2 packed;
+    packed.x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
+               (c[6] << 24) | (c[7] << 28);
+    packed.y = c[8] | (c[9] << 4) | (c[10] << 8) | (c[11] << 12) | (c[12] << 16) | (c[13] << 20) |
+               (c[14] << 24) | (c[15] << 28);
+    reinterpret_cast<uint2*>(o.k)[d] = packed;
+    o.s[d] = (uint8_t)sc;
+  } else if (k_mean_row && d < 8 + G) {
+    const float* qm = q_mean_g0 + (int64_t)(d - 8) * kD;
+    double acc = 0.0;
+    for (int c = 0; c < kD; ++c) acc = __builtin_fma((double)qm[c], (double)kc[c], acc);
+    o.d[(int64_t)(d - 8) * o.dstride] = (uint16_t)bf16_rne((float)acc);
+  }
+}
+
+// Contiguous caches [B, Hkv, N_cap, ...]: T new tokens per (batch, KV head)
+// at positions pos[b] .. pos[b] + T - 1; a batch entry whose position is
+// outside [0, N_cap - T] is skipped whole.
 __global__ __launch_bounds__(128) void k_append_kv(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int is_bf16, int Hkv, int G,
     int T, int N_cap, const int32_t* __restrict__ pos, const float* __restrict__ q_mean,
@@ -288,37 +334,48 @@ __global__ __launch_bounds__(128) void k_append_kv(
   const int p0 = pos[b];
   if (p0 < 0 || p0 > N_cap - T) return;  // uniform over the block
   const int p = p0 + t;
-  const int d = threadIdx.x;
-  const int64_t src = ((int64_t)bhk * T + t) * kD + d;
-  float x = load_elem(k_new, src, is_bf16);
-  if (k_mean) x = x - k_mean[(int64_t)bhk * kD + d];
-  kc[d] = x;
   const int ntiles = (N_cap + 31) / 32;
-  const float s = *v_scale;
-  v_fp8[(((int64_t)bhk * ntiles + p / 32) * kD + d) * 32 + (p & 31)] =
-      (uint8_t)e4m3_encode(load_elem(v_new, src, is_bf16) / s);
-  __syncthreads();
   const int64_t row = (int64_t)bhk * N_cap + p;
-  if (d < 8) {
-    float xb[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) xb[j] = kc[16 * d + j];
-    uint32_t c[16];
-    const uint32_t sc = nvfp4_block(xb, *k_gscale, c);
-    uint2 packed;
-    packed.x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
-               (c[6] << 24) | (c[7] << 28);
-    packed.y = c[8] | (c[9] << 4) | (c[10] << 8) | (c[11] << 12) | (c[12] << 16) | (c[13] << 20) |
-               (c[14] << 24) | (c[15] << 28);
-    reinterpret_cast<uint2*>(k_fp4)[row * 8 + d] = packed;
-    k_sf[row * 8 + d] = (uint8_t)sc;
-  } else if (k_mean && d < 8 + G) {
-    const int64_t hq = (int64_t)bhk * G + (d - 8);
-    const float* qm = q_mean + hq * kD;
-    double acc = 0.0;
-    for (int c = 0; c < kD; ++c) acc = __builtin_fma((double)qm[c], (double)kc[c], acc);
-    delta[hq * N_cap + p] = (uint16_t)bf16_rne((float)acc);
-  }
+  AppendDst o;
+  o.k = k_fp4 + row * 64;
+  o.s = k_sf + row * 8;
+  o.v = v_fp8 + ((int64_t)bhk * ntiles + p / 32) * kD * 32 + (p & 31);
+  o.d = k_mean ? delta + (int64_t)bhk * G * N_cap + p : nullptr;  // head b*Hq + hk*G = bhk*G
+  o.dstride = N_cap;
+  append_token(k_new, v_new, is_bf16, (int64_t)bhk * T + t, k_mean ? k_mean + (int64_t)bhk * kD : nullptr,
+               k_mean ? q_mean + (int64_t)bhk * G * kD : nullptr, G, *k_gscale, *v_scale, o, kc);
+}
+
+// Paged caches (128-token pages; pool [num_pages, Hkv, 128, ...], Delta_S
+// [num_pages, Hq, 128]): one new token per request at position pos[b], i.e.
+// slot pos[b] % 128 of page block_table[b * max_pages + pos[b] / 128], with
+// the request's own frozen scales.  A request whose position is outside its
+// table row or whose page index is outside the pool writes nothing.
+__global__ __launch_bounds__(128) void k_append_kv_paged(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int is_bf16, int Hkv, int G,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ table, int max_pages,
+    int num_pages, const float* __restrict__ q_mean, const float* __restrict__ k_mean,
+    const float* __restrict__ k_gscale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ k_fp4, uint8_t* __restrict__ k_sf, uint8_t* __restrict__ v_fp8,
+    uint16_t* __restrict__ delta) {
+  __shared__ float kc[kD];
+  const int bhk = blockIdx.x;  // b * Hkv + hk
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int p = pos[b];
+  if (p < 0 || p >= max_pages * kBlk) return;  // uniform over the block
+  const int pg = table[(int64_t)b * max_pages + p / kBlk];
+  if (pg < 0 || pg >= num_pages) return;
+  const int slot = p % kBlk;
+  const int64_t slab = (int64_t)pg * Hkv + hk;
+  AppendDst o;
+  o.k = k_fp4 + (slab * kBlk + slot) * 64;
+  o.s = k_sf + (slab * kBlk + slot) * 8;
+  o.v = v_fp8 + (slab * 4 + slot / 32) * kD * 32 + (slot & 31);
+  o.d = k_mean ? delta + ((int64_t)pg * Hkv * G + (int64_t)hk * G) * kBlk + slot : nullptr;
+  o.dstride = kBlk;
+  append_token(k_new, v_new, is_bf16, bhk, k_mean ? k_mean + (int64_t)bhk * kD : nullptr,
+               k_mean ? q_mean + (int64_t)bhk * G * kD : nullptr, G, k_gscale[b], v_scale[b], o,
+               kc);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -388,6 +445,16 @@ void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, 
                       hipStream_t st) {
   hipLaunchKernelGGL(k_append_kv, dim3(T, B * Hkv), dim3(kD), 0, st, k_new, v_new, is_bf16, Hkv, G,
                      T, N_cap, pos, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8, delta);
+}
+
+void launch_append_kv_paged(const void* k_new, const void* v_new, int is_bf16, int B, int Hkv,
+                            int G, const int32_t* pos, const int32_t* block_table, int max_pages,
+                            int num_pages, const float* q_mean, const float* k_mean,
+                            const float* k_gscale, const float* v_scale, uint8_t* k_fp4,
+                            uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta, hipStream_t st) {
+  hipLaunchKernelGGL(k_append_kv_paged, dim3(B * Hkv), dim3(kD), 0, st, k_new, v_new, is_bf16, Hkv,
+                     G, pos, block_table, max_pages, num_pages, q_mean, k_mean, k_gscale, v_scale,
+                     k_fp4, k_sf, v_fp8, delta);
 }
 
 }  // namespace mpfa

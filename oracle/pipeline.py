@@ -362,7 +362,8 @@ def gather_pages(pool, block_table, b, n):
     return cache
 
 
-def decode_paged(q, pool, block_table, seq_lens, q_mean, k_mean, num_splits, scale, out_f64=False):
+def decode_paged(q, pool, block_table, seq_lens, q_mean, k_mean, num_splits, scale, out_f64=False,
+                 heads=None):
     """Split-KV decode over a paged cache with per-request lengths (MpFA §5.3;
     §6 "Serving system": fixed-size pages, a constant number of KV
     partitions, the Delta_S side cache indexed by the same pages).
@@ -374,7 +375,9 @@ def decode_paged(q, pool, block_table, seq_lens, q_mean, k_mean, num_splits, sca
     the capacity of its block-table row, cut into num_splits partitions of
     its own (decode_partitions of its length); the K and V scales are the
     request's own frozen scales.  A request with no positions returns O = 0
-    and LSE = -inf.  Returns (O [B, Hq, D], LSE [B, Hq])."""
+    and LSE = -inf.  heads: None (every (b, q-head)) or a list of (b, q-head)
+    pairs to compute (the others are left at O = 0, LSE = -inf).
+    Returns (O [B, Hq, D], LSE [B, Hq])."""
     q = np.asarray(q, dtype=F32)
     if q.ndim == 3:
         q = q[:, :, None, :]
@@ -385,17 +388,27 @@ def decode_paged(q, pool, block_table, seq_lens, q_mean, k_mean, num_splits, sca
     cap = block_table.shape[1] * PAGE
     O = np.zeros((B, Hq, D), dtype=F64 if out_f64 else F32)
     LSE = np.full((B, Hq), -np.inf)
+    want = None if heads is None else {}
+    if heads is not None:
+        for b, h in heads:
+            want.setdefault(int(b), []).append(int(h))
     for b in range(B):
         n = int(min(max(int(seq_lens[b]), 0), cap))
-        if n == 0:
+        if n == 0 or (want is not None and b not in want):
             continue
         cache = gather_pages(pool, block_table, b, n)
         ops = Operands.from_cache(q[b:b + 1], cache, n, q_mean=qm[b:b + 1] if smooth else None,
                                   k_mean=np.asarray(k_mean)[b:b + 1] if smooth else None)
         ops.q_codes, ops.q_sf, ops.q_gscale = codes[b:b + 1], sf[b:b + 1], g
-        o, lse = decode(q[b:b + 1], None, None, ops.k_mean, num_splits, scale, smooth=smooth,
-                        out_f64=out_f64, ops=ops)
-        O[b], LSE[b] = o[0], lse[0]
+        if want is None:
+            o, lse = decode(q[b:b + 1], None, None, ops.k_mean, num_splits, scale, smooth=smooth,
+                            out_f64=out_f64, ops=ops)
+            O[b], LSE[b] = o[0], lse[0]
+        else:
+            hs = want[b]
+            o, lse = decode(q[b:b + 1], None, None, ops.k_mean, num_splits, scale, smooth=smooth,
+                            out_f64=out_f64, ops=ops, heads=[(0, h) for h in hs])
+            O[b, hs], LSE[b, hs] = o, lse
     return O, LSE
 
 

@@ -179,3 +179,54 @@ def test_append_rejects_bad_arguments(lib):
     assert _append(lib, f, D=64) == UNSUP
     assert _append(lib, f, dtype=7) == UNSUP
     assert _append(lib, f, Hq=2 * 121) == UNSUP  # a group of 121 query heads
+
+
+def _append_paged(lib, f, **kw):
+    a = dict(k_new=f.p, v_new=f.p, dtype=1, B=2, Hkv=2, D=128, pos=f.p, table=f.p, max_pages=4,
+             num_pages=8, page_size=128, Hq=4, q_mean=f.p, k_mean=f.p, k_gscale=f.p, v_scale=f.p,
+             k_fp4=f.p, k_sf=f.p, v_fp8=f.p, delta_s=f.p, stream=None)
+    a.update(kw)
+    return lib.mpfa_append_kv_paged(*a.values())
+
+
+def test_paged_append_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP = -1, -2
+    assert _append_paged(lib, f, page_size=64) == UNSUP
+    assert _append_paged(lib, f, max_pages=0) == INVALID
+    assert _append_paged(lib, f, num_pages=0) == INVALID
+    assert _append_paged(lib, f, max_pages=1 << 24) == INVALID  # 128 max_pages overflows int32
+    assert _append_paged(lib, f, table=None) == INVALID
+    assert _append_paged(lib, f, pos=None) == INVALID
+    assert _append_paged(lib, f, k_sf=f.mis) == INVALID
+    assert _append_paged(lib, f, delta_s=None) == INVALID
+    assert _append_paged(lib, f, k_mean=None, q_mean=None) == INVALID
+    assert _append_paged(lib, f, Hq=3) == INVALID
+    assert _append_paged(lib, f, D=64) == UNSUP
+
+
+def _decode_paged(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=2, Hq=8, Hkv=2, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, table=f.p, lens=f.p,
+             max_pages=4, num_pages=8, page_size=128, scale=0.1, splits=4, out=f.p, out_dtype=1,
+             lse=None, ws=f.p, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.mpfa_decode_paged(*a.values())
+
+
+def test_paged_decode_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP, WS = -1, -2, -3
+    assert _decode_paged(lib, f, page_size=256) == UNSUP
+    assert _decode_paged(lib, f, Hq=18) == UNSUP
+    assert _decode_paged(lib, f, splits=0) == INVALID
+    assert _decode_paged(lib, f, max_pages=0) == INVALID
+    assert _decode_paged(lib, f, num_pages=0) == INVALID
+    assert _decode_paged(lib, f, max_pages=(1 << 24) - 1, splits=1 << 20) == INVALID
+    assert _decode_paged(lib, f, table=None) == INVALID
+    assert _decode_paged(lib, f, lens=None) == INVALID
+    assert _decode_paged(lib, f, k_gscale=None) == INVALID
+    assert _decode_paged(lib, f, q_mean=None) == INVALID
+    assert _decode_paged(lib, f, ws_bytes=256) == WS
+    assert _decode_paged(lib, f, scale=0.0) == INVALID
+    assert _decode_paged(lib, f, D=64) == UNSUP
