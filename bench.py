@@ -294,7 +294,7 @@ def write_traffic(run_dir, args):
     # pre-pass, K expansion, attention; decode = fill, Q amax, split, combine
     calls = [("prefill", "prefill", "k_prefill<true>", (-3, -2, -1, 0),
               f"mpfa_prefill {args.workload}"),
-             ("decode", "decode", "k_decode_split<true>", (-2, -1, 0, 1),
+             ("decode", "decode", "k_decode_split<true, false>", (-2, -1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
         calls.append(("prefill_long", "prefill", "k_prefill<true>", (-3, -2, -1, 0),

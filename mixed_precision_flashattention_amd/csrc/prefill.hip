@@ -490,39 +490,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // K~ = E2M1 code value x E4M3 block scale in FP16, written as block images
 // (one 32 KB image per (batch, KV head, 128-key block), layout above); keys
-// past N in the last block are zero.  Thread g = ((image * 8) + e) * 128 +
-// slot expands 16-element block e of the key in that slot into chunks 2e and
-// 2e + 1, so consecutive threads write consecutive 16-byte slots.
-__global__ __launch_bounds__(256) void k_expand_k(const uint2* __restrict__ codes,
-                                                  const uint8_t* __restrict__ sf, int N, int nkb,
+// past N in the last block are zero.  Thread g = image * 128 + slot expands
+// the whole key in that slot: it reads the key's 64 code bytes and 8 scale
+// bytes in one piece and writes its 16 chunks, so consecutive threads read
+// consecutive rows and write consecutive 16-byte slots of each chunk column.
+__global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ codes,
+                                                  const uint2* __restrict__ sf, int N, int nkb,
                                                   int64_t n_threads, uint4* __restrict__ out) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= n_threads) return;
   const int slot = (int)(g & (kBlk - 1));
-  const int e = (int)((g >> 7) & 7);
-  const int64_t img = g >> 10;  // bhk * nkb + kb
+  const int64_t img = g >> 7;  // bhk * nkb + kb
   const int64_t bhk = img / nkb;
   const int key = (int)(img - bhk * nkb) * kBlk + kslot(slot);
-  uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (key < N) {
-    const int64_t blk = ((bhk * N + key) << 3) + e;  // 16-element block in k_fp4 / k_sf
-    const uint2 w = codes[blk];
-    const f16x2 s2 = e4m3_scale_f16x2(sf[blk]);
-    expand_fp4x8(w.x, s2, v);
-    expand_fp4x8(w.y, s2, v + 4);
+  uint4* dst = out + img * (kKBlockBytes / 16) + slot;
+  if (key >= N) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dst[c * kBlk] = make_uint4(0, 0, 0, 0);
+    return;
   }
-  uint4* dst = out + img * (kKBlockBytes / 16) + (2 * e) * kBlk + slot;
-  dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-  dst[kBlk] = make_uint4(v[4], v[5], v[6], v[7]);
+  const int64_t row = bhk * N + key;
+  const uint2 sc = sf[row];
+  const uint32_t scw[2] = {sc.x, sc.y};
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {  // 16 code bytes = blocks 2 q4 and 2 q4 + 1
+    const uint4 w = codes[row * 4 + q4];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int e = 2 * q4 + half;
+      const f16x2 s2 = e4m3_scale_f16x2((scw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      uint32_t v[8];
+      expand_fp4x8(ww[2 * half], s2, v);
+      expand_fp4x8(ww[2 * half + 1], s2, v + 4);
+      dst[(2 * e) * kBlk] = make_uint4(v[0], v[1], v[2], v[3]);
+      dst[(2 * e + 1) * kBlk] = make_uint4(v[4], v[5], v[6], v[7]);
+    }
+  }
 }
 
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
                      uint8_t* k_f16, hipStream_t st) {
   const int nkb = (N + kBlk - 1) / kBlk;
-  const int64_t n_threads = bhk * nkb * kBlk * 8;
+  const int64_t n_threads = bhk * nkb * kBlk;
   hipLaunchKernelGGL(k_expand_k, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint2*>(k_fp4), k_sf, N, nkb, n_threads,
-                     reinterpret_cast<uint4*>(k_f16));
+                     reinterpret_cast<const uint4*>(k_fp4), reinterpret_cast<const uint2*>(k_sf), N,
+                     nkb, n_threads, reinterpret_cast<uint4*>(k_f16));
 }
 
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
