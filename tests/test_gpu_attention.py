@@ -121,6 +121,31 @@ def test_decode_gqa5_direct(mpfa, oracle_mod):
                   smooth=False)
 
 
+@pytest.mark.parametrize("smooth", [True, False])
+def test_prefill_mha_xcd_mapping(mpfa, oracle_mod, smooth):
+    """Hq = Hkv (no grouping) with B * Hkv = 8, the XCD-aware workgroup order
+    (KV heads dealt to the 8 XCDs), two 256-row units with a ragged tail."""
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=2, Hq=4, Hkv=4, N=400),
+                   smooth=smooth)
+
+
+def test_prefill_gqa2_xcd_mapping_bf16_out(mpfa, oracle_mod):
+    """Eight KV heads of two query heads each (XCD-aware order), bf16 output."""
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=16, Hkv=8, N=300),
+                   out_bf16=True)
+
+
+@pytest.mark.parametrize("smooth", [True, False])
+def test_decode_mha(mpfa, oracle_mod, smooth):
+    """Hq = Hkv: one real row per score tile."""
+    from mixed_precision_flashattention_amd import synth
+    _check_decode(mpfa, oracle_mod,
+                  synth.config("llama8b_decode_128k", B=3, Hq=2, Hkv=2, N=515, num_splits=4),
+                  smooth=smooth)
+
+
 def test_decode_gqa8(mpfa, oracle_mod):
     from mixed_precision_flashattention_amd import synth
     _check_decode(mpfa, oracle_mod,
