@@ -291,13 +291,14 @@ def write_traffic(run_dir, args):
                       "then python bench.py --write-traffic DIR",
            "calls": {}}
     # dispatches of one call relative to its main kernel: prefill = fill, Q amax
-    # pre-pass, K expansion, attention; decode = fill, Q amax, split, combine
-    calls = [("prefill", "prefill", "k_prefill<true>", (-3, -2, -1, 0),
+    # pre-pass and its fold, K expansion, attention; decode = fill, Q amax and
+    # its fold, split, combine
+    calls = [("prefill", "prefill", "k_prefill<true>", (-4, -3, -2, -1, 0),
               f"mpfa_prefill {args.workload}"),
-             ("decode", "decode", "k_decode_split<true, false>", (-2, -1, 0, 1),
+             ("decode", "decode", "k_decode_split<true, false>", (-3, -2, -1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
-        calls.append(("prefill_long", "prefill", "k_prefill<true>", (-3, -2, -1, 0),
+        calls.append(("prefill_long", "prefill", "k_prefill<true>", (-4, -3, -2, -1, 0),
                       f"mpfa_prefill {args.long_workload}"))
     for op, kind, main_kernel, offsets, name in calls:
         fv, fn = load(op, "FETCH_SIZE")
@@ -409,7 +410,8 @@ def main():
     out = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=dev)
     ws_k = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_QUANTIZE_K, B, Hq, Hkv, N),
                        dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(256, dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_QUANTIZE_V, B, 0, Hkv, N),
+                       dtype=torch.uint8, device=dev)
     ws_p = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, B, Hq, Hkv, N),
                        dtype=torch.uint8, device=dev)
 

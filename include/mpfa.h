@@ -224,7 +224,7 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
  * out: [B, Hq, N, 128] in out_dtype (MPFA_BF16, the paper's output, or
  * MPFA_F32).  lse: [B, Hq, N] float, or NULL.
  * ws: mpfa_workspace_bytes(MPFA_OP_PREFILL, B, Hq, Hkv, N, 128, 1) bytes
- * (256 + B * Hkv * ceil(N / 128) * 32768, rounded up to 256): the per-call
+ * (8192 + B * Hkv * ceil(N / 128) * 32768, rounded up to 256): the per-call
  * Q amax and the K cache expanded once per call to exact FP16 operands
  * (code value x block scale, 32 KB per 128-key block, zero past N), which
  * the attention kernel copies into LDS block by block.

@@ -26,7 +26,7 @@ inline QuantKWs quant_k_layout(int B, int Hq, int Hkv) {
   w.ksum = align_up(w.qmax + nq * 4);
   w.qsum = align_up(w.ksum + nk * 8);
   w.amax = align_up(w.qsum + nq * 8);
-  w.total = align_up(w.amax + 4);
+  w.total = align_up(w.amax + kAmaxBytes);
   return w;
 }
 
@@ -37,22 +37,22 @@ inline DecodeWs decode_layout(int B, int Hq, int P) {
   DecodeWs w;
   const size_t ns = (size_t)B * Hq * P;
   w.amax = 0;
-  w.m = align_up(4);
+  w.m = align_up(kAmaxBytes);
   w.l = align_up(w.m + ns * 4);
   w.acc = align_up(w.l + ns * 4);
   w.total = align_up(w.acc + ns * kD * 4);
   return w;
 }
 
-// Prefill: the Q amax word, then K~ (the K cache expanded to FP16,
-// [B, Hkv, N, 128] halves).
+// Prefill: the Q amax slots, then K~ (the K cache expanded to FP16 block
+// images).
 struct PrefillWs {
   size_t amax, k_f16, total;
 };
 inline PrefillWs prefill_layout(int B, int Hkv, int N) {
   PrefillWs w;
   w.amax = 0;
-  w.k_f16 = kAlign;
+  w.k_f16 = kAmaxBytes;
   // K~ block images: 32 KB per (batch, KV head, 128-key block)
   w.total = align_up(w.k_f16 + (size_t)B * Hkv * ((N + kBlk - 1) / kBlk) * kBlk * kD * 2);
   return w;
@@ -88,7 +88,7 @@ size_t mpfa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int nu
     case MPFA_OP_QUANTIZE_K:
       return quant_k_layout(B, Hq > 0 ? Hq : 0, Hkv).total;
     case MPFA_OP_QUANTIZE_V:
-      return kAlign;
+      return kAmaxBytes;
     case MPFA_OP_PREFILL:
       return prefill_layout(B, Hkv, N).total;
     case MPFA_OP_DECODE:
@@ -161,12 +161,12 @@ int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D
   if (!dtype_ok(v_dtype)) return MPFA_ERR_UNSUPPORTED;
   if (!v || !v_fp8 || !v_scale || !ws) return MPFA_ERR_INVALID;
   if (!aligned16(v) || !aligned16(v_fp8) || !aligned16(ws)) return MPFA_ERR_INVALID;
-  if (ws_bytes < kAlign) return MPFA_ERR_WORKSPACE;
+  if (ws_bytes < kAmaxBytes) return MPFA_ERR_WORKSPACE;
   if ((N + 31) / 32 > 65535 * 64) return MPFA_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)ws;
   const int vb = v_dtype == MPFA_BF16;
-  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
   launch_centered_amax(v, vb, B * Hkv, N, nullptr, amax, s);
   launch_quantize_v_codes(v, vb, B * Hkv, N, amax, v_scale, v_fp8, s);
   return launch_status();
@@ -264,7 +264,7 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
   uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
-  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
   launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, delta_s ? q_mean : nullptr, amax, s);
   launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_f16, s);
   PrefillParams p;
@@ -321,7 +321,7 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
-  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
   launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
   DecodeParams p;
   p.q = q;
@@ -391,7 +391,7 @@ int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
-  launch_fill_u32(amax, kAlign / 4, 0u, s);
+  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
   launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
   DecodeParams p;
   p.q = q;

@@ -54,6 +54,12 @@ struct DecodeParams {
 };
 
 // quant.hip
+// A tensor amax is reduced into kAmaxSlots words, one per 128-byte line
+// (atomics on one address serialize across the GPU), then folded into the
+// first word, which is what every consumer reads.
+constexpr int kAmaxSlots = 64;
+constexpr int kAmaxSlotWords = 32;
+constexpr size_t kAmaxBytes = (size_t)kAmaxSlots * kAmaxSlotWords * 4;
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
                          unsigned long long* sums, float* mean, hipStream_t st);

@@ -164,8 +164,19 @@ __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ 
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0)
-    atomic_max_nonneg(out, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  if (threadIdx.x == 0) {
+    const int slot = (blockIdx.x + blockIdx.y * gridDim.x) % kAmaxSlots;
+    atomic_max_nonneg(out + slot * kAmaxSlotWords,
+                      fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  }
+}
+
+// The slots of a reduced amax folded into its first word (one wave).
+__global__ __launch_bounds__(64) void k_amax_fold(uint32_t* __restrict__ out) {
+  uint32_t m = out[threadIdx.x * kAmaxSlotWords];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (threadIdx.x == 0) out[0] = m;
 }
 
 // NVFP4 codes and scales of K_c = fp32(K - k_mean) (k_mean NULL: K_c = K).
@@ -414,6 +425,7 @@ void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float
   const int rows = stat_rows_per_block(BH, N, 128);
   dim3 grid((unsigned)((N + rows - 1) / rows), BH);
   hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out);
+  hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, out);
 }
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,

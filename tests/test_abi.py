@@ -67,19 +67,22 @@ def test_status_strings(lib):
 
 def test_workspace_sizes(lib):
     ws = lib.mpfa_workspace_bytes
-    # decode: amax slot + m, l [B*Hq*P] + acc [B*Hq*P*128] floats, 256-aligned
+    # decode: the amax slots (64 x 128 B) + m, l [B*Hq*P] + acc [B*Hq*P*128]
+    # floats, 256-aligned
+    AMAX = 64 * 128
     B, Hq, Hkv, N, P = 16, 32, 8, 131072, 32
     n = ws(3, B, Hq, Hkv, N, 128, P)
     assert n % 256 == 0
-    assert n >= B * Hq * P * (2 + 128) * 4
-    assert n < B * Hq * P * (2 + 128) * 4 + 4 * 256
+    assert n >= AMAX + B * Hq * P * (2 + 128) * 4
+    assert n < AMAX + B * Hq * P * (2 + 128) * 4 + 4 * 256
     # quantize_k with a query tensor needs the query statistics too
     assert ws(0, 1, 32, 8, 1024, 128, 1) > ws(0, 1, 0, 8, 1024, 128, 1)
-    assert ws(1, 1, 0, 8, 1024, 128, 1) == 256
-    # prefill: the Q amax slot + K expanded to FP16 (B * Hkv * N * 128 halves)
-    assert ws(2, 1, 32, 8, 1024, 128, 1) == 256 + 8 * 8 * 32768
-    assert ws(2, 2, 32, 8, 1001, 128, 1) == 256 + 2 * 8 * 8 * 32768
-    assert ws(2, 1, 4, 1, 1, 128, 1) == 256 + 32768
+    assert ws(1, 1, 0, 8, 1024, 128, 1) == AMAX
+    # prefill: the Q amax slots + K expanded to FP16 block images (32 KB per
+    # (batch, KV head, 128-key block))
+    assert ws(2, 1, 32, 8, 1024, 128, 1) == AMAX + 8 * 8 * 32768
+    assert ws(2, 2, 32, 8, 1001, 128, 1) == AMAX + 2 * 8 * 8 * 32768
+    assert ws(2, 1, 4, 1, 1, 128, 1) == AMAX + 32768
     assert ws(9, 1, 32, 8, 1024, 128, 1) == 0
     assert ws(3, 1, 32, 8, 1024, 128, 0) == 0
     assert ws(0, 0, 32, 8, 1024, 128, 1) == 0
