@@ -12,9 +12,10 @@
 // group.  The groups alternate between workgroup barriers: one runs its
 // matrix products while the other runs its softmax, so the matrix cores and
 // the vector ALUs of a SIMD work at the same time.  Per 128-key block:
-//   * K~ rows, the FP8 V tiles and Delta_S reach LDS by direct global->LDS
-//     loads (no registers, no VALU), double-buffered and issued one block
-//     ahead by the first row group after its matrix products;
+//   * K~ block images, the FP8 V tiles and Delta_S reach LDS by direct
+//     global->LDS loads (no registers, no VALU address work), double-buffered
+//     and issued one block ahead by the first row group after its matrix
+//     products;
 //   * each wave computes S^T (keys x its 32 queries) on MFMA: with
 //     smoothing, a first bf16 step writes Delta_S * (1 / (gQ gK)) into the
 //     accumulator (the rank-one term of section 5.2 -- no element-wise add on
