@@ -31,7 +31,7 @@ inline QuantKWs quant_k_layout(int B, int Hq, int Hkv) {
 }
 
 struct DecodeWs {
-  size_t amax, m, l, acc, total;
+  size_t amax, m, l, acc, order, total;
 };
 inline DecodeWs decode_layout(int B, int Hq, int P) {
   DecodeWs w;
@@ -40,7 +40,8 @@ inline DecodeWs decode_layout(int B, int Hq, int P) {
   w.m = align_up(kAmaxBytes);
   w.l = align_up(w.m + ns * 4);
   w.acc = align_up(w.l + ns * 4);
-  w.total = align_up(w.acc + ns * kD * 4);
+  w.order = align_up(w.acc + ns * kD * 4);  // paged decode: request order
+  w.total = align_up(w.order + (size_t)B * 4);
   return w;
 }
 
@@ -354,6 +355,7 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   p.block_table = nullptr;
   p.seq_lens = nullptr;
   p.max_pages = p.num_pages = 0;
+  p.order = nullptr;
   launch_decode(p, s);
   return launch_status();
 }
@@ -424,6 +426,7 @@ int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
   p.seq_lens = seq_lens;
   p.max_pages = max_pages;
   p.num_pages = num_pages;
+  p.order = (int*)(w + L.order);
   launch_decode(p, s);
   return launch_status();
 }

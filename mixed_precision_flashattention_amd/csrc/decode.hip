@@ -220,7 +220,9 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   const int N = p.N, G = p.G, P = p.P;
   const int part = blockIdx.x % P;
   const int bhk = blockIdx.x / P;
-  const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  // paged: workgroups are dealt longest request first (ragged lengths would
+  // otherwise leave the longest partitions for the end of the grid)
+  const int b = PAGED ? p.order[bhk / p.Hkv] : bhk / p.Hkv, hk = bhk % p.Hkv;
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int64_t hq0 = (int64_t)b * p.Hq + (int64_t)hk * G;  // first query head of the group
   // paged: this request's length, clamped to its block-table row, cut into
@@ -406,7 +408,31 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeParams p) {
   }
 }
 
+// Requests ranked by descending clamped length (ties by index): order[rank]
+// = request, one thread per request counting the longer ones (B^2 work, so
+// batches above kOrderMaxB keep their own order).
+constexpr int kOrderMaxB = 4096;
+__global__ __launch_bounds__(256) void k_decode_order(const int32_t* __restrict__ seq_lens, int B,
+                                                      int cap, int* __restrict__ order) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  if (B > kOrderMaxB) {
+    order[b] = b;
+    return;
+  }
+  const int lb = min(max(seq_lens[b], 0), cap);
+  int rank = 0;
+  for (int i = 0; i < B; ++i) {
+    const int li = min(max(seq_lens[i], 0), cap);
+    rank += (li > lb) || (li == lb && i < b);
+  }
+  order[rank] = b;
+}
+
 void launch_decode(const DecodeParams& p, hipStream_t st) {
+  if (p.paged)
+    hipLaunchKernelGGL(k_decode_order, dim3((p.B + 255) / 256), dim3(256), 0, st, p.seq_lens, p.B,
+                       p.max_pages * kBlk, p.order);
   const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.P);
   if (p.paged) {
     if (p.delta_s)

@@ -51,6 +51,7 @@ struct DecodeParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int max_pages, num_pages;
+  int* order;  // paged: requests by descending length (written by the launch)
 };
 
 // quant.hip
