@@ -232,7 +232,7 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
   const float nb = kLog2_448 - lam * m_new;
   m_run = m_new;
 
-  float lsum = 0.0f;
+  float lsum;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -242,8 +242,12 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
       const float e1 = fast_exp2(fmaf(s[t][v0 + 1], lam, nb));
       const float e2 = fast_exp2(fmaf(s[t][v0 + 2], lam, nb));
       const float e3 = fast_exp2(fmaf(s[t][v0 + 3], lam, nb));
-      lsum += (e0 + e1) + (e2 + e3);
-      uint32_t wd = cvt_fp8x2<false>(e0, e1, 0u);
+      const float part = (e0 + e1) + (e2 + e3);
+      lsum = (c == 0 && k == 0) ? part : lsum + part;
+      // The low half is written first and the high half second, so the
+      // register's old content does not matter; a value that dies here lets
+      // the compiler convert in place (a constant 0 costs a move per word).
+      uint32_t wd = cvt_fp8x2<false>(e0, e1, __float_as_uint(part));
       wd = cvt_fp8x2<true>(e2, e3, wd);
       pb[c][k] = (int)wd;
     }
