@@ -39,15 +39,16 @@ constexpr int kUnitRows = 256;  // query rows per workgroup (two groups of 128)
 constexpr int kRowBytes = 256;  // one Q~ row in LDS: 128 f16
 // K~ block image (32 KB per 128 keys, the same bytes in the workspace and in
 // LDS): 16 chunk columns of 2 KB, one per 8 head-dim elements; chunk c of
-// key k sits at c * 2048 + 16 * kslot(k).  An operand read of head-dim step
-// kc is then a per-lane base plus the immediate kc * 2048 (no address
-// arithmetic per read), and a direct load is a contiguous 1 KB copy.  A
-// 16-lane pass of an operand read touches keys {0-3, 32-35, 4-7, 36-39} +
-// base in one chunk column; kslot moves keys 32-63 (mod 64) by 8 slots, so
-// those 16 keys fill 16 distinct 16-byte slots of a 256-byte bank window.
+// key k sits at c * 2048 + 16 k.  An operand read of head-dim step kc is
+// then a per-lane base plus the immediate kc * 2048 (no address arithmetic
+// per read), and a direct load is a contiguous 1 KB copy.  The lanes of an
+// operand read touch keys {0-3, 32-35, 4-7, 36-39, ...} + base of one
+// column: with keys in consecutive 16-byte slots that read is free of bank
+// conflicts on gfx950 (measured with the bank-conflict counter on this very
+// address pattern; moving keys 32-63 by 8 slots made every read a 2-way
+// conflict).
 constexpr int kKChunkBytes = kBlk * 16;
 constexpr int kKBlockBytes = kBlk * kRowBytes;
-__device__ __forceinline__ int kslot(int k) { return k ^ (((k >> 5) & 1) << 3); }
 // Q~ staging rows use chunk c ^ (row & 15): the operand read (16 rows, one
 // chunk column) and the quantizer's writes (8 rows x 8 chunk pairs) are both
 // spread over all 16 chunk slots.
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     koff[t] = 64 * (t >> 1) + 32 * hp + 16 * (t & 1) + vp;
-    kbase[t] = 8 * h * kKChunkBytes + 16 * kslot(koff[t]);
+    kbase[t] = 8 * h * kKChunkBytes + 16 * koff[t];
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ code
   const int slot = (int)(g & (kBlk - 1));
   const int64_t img = g >> 7;  // bhk * nkb + kb
   const int64_t bhk = img / nkb;
-  const int key = (int)(img - bhk * nkb) * kBlk + kslot(slot);
+  const int key = (int)(img - bhk * nkb) * kBlk + slot;
   uint4* dst = out + img * (kKBlockBytes / 16) + slot;
   if (key >= N) {
 #pragma unroll
