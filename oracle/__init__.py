@@ -235,6 +235,7 @@ def merge_states(m, l, acc, scale):
 
 from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     PAGE,
+    Q_TILE,
     Operands,
     append_kv,
     append_kv_paged,
@@ -244,9 +245,13 @@ from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     exact_attention,
     gather_pages,
     prefill_rows,
+    prefill_tile_mean_rows,
     quantize_k,
     quantize_q,
+    quantize_q_tiles,
     quantize_v,
+    tile_means,
+    tile_operand,
 )
 
 __all__ = [
@@ -256,5 +261,6 @@ __all__ = [
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
     "quantize_k", "quantize_v", "quantize_q", "prefill_rows", "decode", "decode_partitions",
     "exact_attention", "Operands", "append_kv", "PAGE", "gather_pages", "decode_paged",
-    "append_kv_paged"
+    "append_kv_paged", "Q_TILE", "tile_means", "quantize_q_tiles", "tile_operand",
+    "prefill_tile_mean_rows"
 ]

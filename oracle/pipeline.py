@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (KV_BLOCK, P_SCALE, amax, attn_state, bf16_to_f64, channel_mean, delta_s,
+from . import (KV_BLOCK, P_SCALE, amax, attn_state, bf16_rne, bf16_to_f64, channel_mean, delta_s,
                e4m3_table, fp8_quantize, fp8_scale, merge_states, nvfp4_dequantize,
                nvfp4_global_scale, nvfp4_quantize)
 
@@ -31,6 +31,9 @@ def quantize_k(k, q=None, q_mean=None, smooth=True):
     smooth: K_c = fp32(K - Kbar) with Kbar the per-(b, kv-head) channel mean;
     Qbar is the per-(b, q-head) mean of ``q`` when given, else ``q_mean``
     (frozen means, as in decode); delta_s[b, h, j] = bf16(Qbar[b, h] . K_c[b, h//G, j]).
+    With neither ``q`` nor ``q_mean`` only K is centred (no delta_s): the
+    cache of the per-query-tile mean mode, which computes its compensation in
+    the attention stage.
     direct: K_c = K, no means and no delta_s.
     Then NVFP4 with a global scale from the amax of the whole K_c tensor."""
     k = np.asarray(k, dtype=F32)
@@ -38,17 +41,19 @@ def quantize_k(k, q=None, q_mean=None, smooth=True):
     out = {}
     if smooth:
         k_mean = channel_mean(k)
+        kc = (k - k_mean[:, :, None, :]).astype(F32)
+        out.update(k_mean=k_mean)
         if q is not None:
             q_mean = channel_mean(np.asarray(q, dtype=F32))
-        q_mean = np.asarray(q_mean, dtype=F32)
-        kc = (k - k_mean[:, :, None, :]).astype(F32)
-        Hq = q_mean.shape[1]
-        G = Hq // Hkv
-        ds = np.empty((B, Hq, N), dtype=np.uint16)
-        for b in range(B):
-            for h in range(Hq):
-                ds[b, h] = delta_s(q_mean[b, h], kc[b, h // G])
-        out.update(k_mean=k_mean, q_mean=q_mean, delta_s=ds)
+        if q_mean is not None:
+            q_mean = np.asarray(q_mean, dtype=F32)
+            Hq = q_mean.shape[1]
+            G = Hq // Hkv
+            ds = np.empty((B, Hq, N), dtype=np.uint16)
+            for b in range(B):
+                for h in range(Hq):
+                    ds[b, h] = delta_s(q_mean[b, h], kc[b, h // G])
+            out.update(q_mean=q_mean, delta_s=ds)
     else:
         kc = k
     g = nvfp4_global_scale(amax(kc))
@@ -265,6 +270,118 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
                 if smooth:
                     off = scale * (q[b, h][pos].astype(F64) @ ops.k_mean[b, hk].astype(F64))
                 o, lse = _finalize(m, l, acc, ops.s_v, scale, off, out_f64)
+                O[sel] = o
+                LSE[sel] = lse
+    return O, LSE, rows
+
+
+# --------------------------------------------- per-query-tile mean mode --
+Q_TILE = KV_BLOCK  # query rows per mean in the per-tile mode
+
+
+def tile_means(q, tile=Q_TILE):
+    """Channel means of Q per (b, q-head, tile of ``tile`` consecutive rows),
+    by the same order-free fixed-point rule as the sequence means; the last
+    tile averages only the rows it has.  q [B, H, N, D] -> [B, H, ceil(N/tile), D] fp32.
+
+    Reading: the per-tile mode centres each query row by the mean of its own
+    128-row tile instead of the sequence mean (the paper smooths Q by a mean
+    over the queries, MpFA §3.2, §5.1; the tile is the query tile of the
+    attention stage)."""
+    q = np.asarray(q, dtype=F32)
+    B, H, N, D = q.shape
+    nt = -(-N // tile)
+    out = np.empty((B, H, nt, D), dtype=F32)
+    for t in range(nt):
+        out[:, :, t] = channel_mean(np.ascontiguousarray(q[:, :, t * tile:(t + 1) * tile]))
+    return out
+
+
+def quantize_q_tiles(q, tm, tile=Q_TILE):
+    """NVFP4 of Q_c = fp32(Q - Qbar_tile(row)), one global scale from the amax
+    of the whole tile-centred tensor.  Returns (codes, scales, g)."""
+    q = np.asarray(q, dtype=F32)
+    N = q.shape[2]
+    rep = np.repeat(np.asarray(tm, dtype=F32), tile, axis=2)[:, :, :N]
+    qc = (q - rep).astype(F32)
+    g = nvfp4_global_scale(amax(qc))
+    codes, sf = nvfp4_quantize(qc, g)
+    return codes, sf, np.float32(g)
+
+
+def tile_operand(codes, sf, g, tm, tile=Q_TILE):
+    """The query operand of the per-tile mode, FP64, in absolute units.
+
+    Reading: the tile mean's compensation Qbar_tile . K~_c[j] is added to the
+    scores by folding the mean into the query operand of the score product,
+    (Q~_c + Qbar_tile) . K~_c, so the centred product and the compensation
+    share one matrix product.  The fold is carried in BF16, as the paper
+    carries its compensation term (MpFA §5.2, a BF16 product): in units of
+    the Q global scale g, u = fp32(code value x block scale + fp32(Qbar / g))
+    (the first term is exact in fp32), operand = bf16_rne(u) * g."""
+    N = codes.shape[2]
+    qsc = nvfp4_dequantize(codes, sf, 1.0).astype(F32)  # code value x block scale, exact
+    qb = (np.asarray(tm, dtype=F32) / np.float32(g)).astype(F32)
+    rep = np.repeat(qb, tile, axis=2)[:, :, :N]
+    u = (qsc + rep).astype(F32)
+    return bf16_to_f64(bf16_rne(u)) * float(g)
+
+
+def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=None, out_f64=False):
+    """Prefill in the per-query-tile mean mode for the selected rows.
+
+    K is centred by its sequence mean Kbar and quantized as in smoothing mode
+    (without delta_s); Q by the mean of each row's 128-row tile
+    (``tile_means``, ``quantize_q_tiles``); the scores are
+    tile_operand(Q) . K~_c^T, i.e. Q~_c . K~_c^T plus the column term
+    Qbar_tile . K~_c[j]; the rest is the prefill of ``prefill_rows``.  The
+    LSE adds back the row term scale * (Q_i . Kbar), as in smoothing mode.
+    identity: no quantizer (the operand is Q_c + Qbar_tile in FP64, K~_c = K_c,
+    P not rounded).  Returns (O, LSE, rows)."""
+    q = np.asarray(q, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    v = np.asarray(v, dtype=F32)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    tm = tile_means(q)
+    k_mean = channel_mean(k)
+    if identity:
+        rep = np.repeat(tm, Q_TILE, axis=2)[:, :, :N]
+        qop = (q - rep).astype(F32).astype(F64) + rep.astype(F64)
+        kdeq = lambda b, hk: (k[b, hk] - k_mean[b, hk][None, :]).astype(F64)
+        vdeq = lambda b, hk: v[b, hk].astype(F64)
+        s_v, quant_p = 1.0, False
+    else:
+        kq = quantize_k(k)
+        vq = quantize_v(v)
+        codes, sf, g = quantize_q_tiles(q, tm)
+        qop = tile_operand(codes, sf, g, tm)
+        kdeq = lambda b, hk: nvfp4_dequantize(kq["k_fp4"][b, hk], kq["k_sf"][b, hk], kq["k_gscale"])
+        table = e4m3_table()
+        vdeq = lambda b, hk: table[vq["v_fp8"][b, hk]]
+        s_v, quant_p = float(vq["v_scale"]), True
+    if rows is None:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.empty((len(rows), D), dtype=F64 if out_f64 else F32)
+    LSE = np.empty(len(rows))
+    for b in range(B):
+        for hk in range(Hkv):
+            kt = vt = None
+            for h in range(hk * G, (hk + 1) * G):
+                sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+                if len(sel) == 0:
+                    continue
+                if kt is None:
+                    kt, vt = kdeq(b, hk), vdeq(b, hk)
+                pos = rows[sel, 2]
+                row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
+                m, l, acc = attn_state(np.ascontiguousarray(qop[b, h][pos]), row_pos, kt, vt, None, 0, N,
+                                       scale, quant_p)
+                off = scale * (q[b, h][pos].astype(F64) @ k_mean[b, hk].astype(F64))
+                o, lse = _finalize(m, l, acc, s_v, scale, off, out_f64)
                 O[sel] = o
                 LSE[sel] = lse
     return O, LSE, rows
