@@ -103,6 +103,10 @@ const char* mpfa_status_string(int status);
  *   - delta_s[b, h, t] <- bf16(fp32(sum_d q_mean[b, h, d] * K_c[b, h/G, t, d]))
  *     with the sum in FP64 over ascending d (the per-token compensation
  *     vector computed "with one GEMV", section 5.1).
+ * Centring only (k_mean non-NULL, delta_s and q NULL; q_mean ignored):
+ * k_mean and K_c as above, no Q mean and no delta_s -- the K cache of
+ * mpfa_prefill_tile_mean, which computes its compensation itself.  q
+ * non-NULL without delta_s returns MPFA_ERR_INVALID.
  * Direct mode (q_mean, k_mean, delta_s all NULL; q ignored): K_c = K.
  * Then NVFP4 of K_c: k_gscale <- amax(|K_c|) / 2688 (1 if the amax is 0),
  * per 16-element block an E4M3 scale code of amax_block / (6 * k_gscale) and
@@ -234,6 +238,39 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
                  const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
                  void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_prefill_tile_mean -- mpfa_prefill with the queries smoothed per
+ * 128-row query tile instead of per sequence (the query smoothing of paper
+ * sections 3.2 and 5.1 at the granularity of the attention stage's query
+ * tile; the compensation is computed in the attention stage, so no Delta_S
+ * side cache exists in this mode).
+ *
+ *   q_tile_mean[b, h, t, :] <- channel mean of rows 128 t .. min(128 t + 127,
+ *     N - 1) of Q [b, h], by the order-free fixed-point rule of the sequence
+ *     means (the last tile averages only its rows);
+ *   Q_c = fp32(Q_i - q_tile_mean[tile of i]); NVFP4 with global scale
+ *     gQ = amax(|Q_c|) / 2688 over the whole call;
+ *   query operand of row i, channel d, in units of gQ:
+ *     bf16_rne(fp32(code value x block scale + fp32(q_tile_mean / gQ)))
+ *   S_ij = operand_i . K~_c[j] (FP32 accumulation) -- the centred product
+ *     plus the column term Qbar_tile . K~_c[j];
+ * then the online softmax, P.V and epilogue of mpfa_prefill; lse adds back
+ * scale * (Q_i . k_mean).
+ *
+ * K must be cached centred (mpfa_quantize_k_nvfp4 in centring-only or
+ * smoothing mode; k_mean is that call's k_mean).  q_tile_mean: OUTPUT,
+ * device float [B, Hq, ceil(N / 128), 128].  The other arguments, the output
+ * layouts and the workspace (mpfa_workspace_bytes(MPFA_OP_PREFILL, ...); the
+ * K cache is expanded to BF16 operands here, same size) are those of
+ * mpfa_prefill.  Returns MPFA_ERR_INVALID for a null k_mean or q_tile_mean
+ * and as mpfa_prefill does.
+ */
+int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                           const float* k_mean, const uint8_t* k_fp4, const uint8_t* k_sf,
+                           const float* k_gscale, const uint8_t* v_fp8, const float* v_scale,
+                           float softmax_scale, int causal, void* out, int out_dtype, float* lse,
+                           float* q_tile_mean, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mpfa_decode -- one query token per (batch, query head) against N_kv cached

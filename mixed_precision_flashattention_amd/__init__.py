@@ -29,7 +29,7 @@ V_TILE = 32  # tokens per head-dim-major V tile
 
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
            "mpfa_quantize_v_fp8", "mpfa_append_kv", "mpfa_append_kv_paged", "mpfa_prefill",
-           "mpfa_decode", "mpfa_decode_paged")
+           "mpfa_decode", "mpfa_decode_paged", "mpfa_prefill_tile_mean")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -65,6 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_prefill.restype = i32
     L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
                                P, i32, P, P, sz, P]
+    L.mpfa_prefill_tile_mean.restype = i32
+    L.mpfa_prefill_tile_mean.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f32, i32,
+                                         P, i32, P, P, P, sz, P]
     L.mpfa_decode.restype = i32
     L.mpfa_decode.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
                               P, i32, P, P, sz, P]
@@ -164,6 +167,18 @@ def mpfa_prefill(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, 
     _raise("mpfa_prefill", st)
 
 
+def mpfa_prefill_tile_mean(q, Hkv, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, softmax_scale,
+                           causal, out, lse, q_tile_mean, ws, stream=None):
+    _check(q, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, out, lse, q_tile_mean, ws)
+    B, Hq, N, D = q.shape
+    st = load_library().mpfa_prefill_tile_mean(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf),
+        _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), float(softmax_scale), int(bool(causal)),
+        _ptr(out), _dtype_code(out), _ptr(lse), _ptr(q_tile_mean), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_prefill_tile_mean", st)
+
+
 def mpfa_append_kv(k_new, v_new, pos, q_mean, k_mean, k_gscale, v_scale, k_fp4, k_sf, v_fp8,
                    delta_s, Hq=None, stream=None):
     """k_new, v_new [B, Hkv, T, 128]; pos int32 [B]; caches of capacity
@@ -246,14 +261,21 @@ def _workspace(op, B, Hq, Hkv, N, num_splits, device):
 
 def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
     """Allocate and fill the NVFP4 K cache.  Returns a dict with k_fp4, k_sf,
-    k_gscale and, in smoothing mode, k_mean, q_mean and delta_s."""
+    k_gscale and, in smoothing mode, k_mean, q_mean and delta_s.  Smoothing
+    with neither q nor q_mean only centres K (k_mean, no delta_s): the cache
+    of ``prefill_tile_mean``."""
     import torch
     B, Hkv, N, D = k.shape
     dev = k.device
     out = {"k_fp4": torch.empty((B, Hkv, N, D // 2), dtype=torch.uint8, device=dev),
            "k_sf": torch.empty((B, Hkv, N, D // 16), dtype=torch.uint8, device=dev),
            "k_gscale": torch.empty(1, dtype=torch.float32, device=dev)}
-    if smooth:
+    if smooth and q is None and q_mean is None:
+        out["k_mean"] = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev)
+        ws = _workspace(MPFA_OP_QUANTIZE_K, B, 0, Hkv, N, 1, dev)
+        mpfa_quantize_k_nvfp4(k, None, None, out["k_mean"], out["k_fp4"], out["k_sf"],
+                              out["k_gscale"], None, ws, Hq=0, stream=stream)
+    elif smooth:
         if Hq is None:
             Hq = q.shape[1] if q is not None else q_mean.shape[1]
         if q is not None:
@@ -303,6 +325,29 @@ def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=Fals
                  kq.get("delta_s") if smooth else None, softmax_scale, causal, out,
                  lse if with_lse else None, ws, stream=stream)
     return out, (lse if with_lse else None)
+
+
+def prefill_tile_mean(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False,
+                      ws=None, out=None, lse=None, q_tile_mean=None, stream=None):
+    """Prefill with the queries smoothed per 128-row tile; kq must hold a
+    centred K cache (``quantize_k(k)`` with neither q nor q_mean, or a
+    smoothing-mode cache).  Returns (out, lse or None, q_tile_mean)."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = kq["k_fp4"].shape[1]
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if q_tile_mean is None:
+        q_tile_mean = torch.empty((B, Hq, (N + 127) // 128, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(MPFA_OP_PREFILL, B, Hq, Hkv, N, 1, q.device)
+    mpfa_prefill_tile_mean(q, Hkv, kq["k_mean"], kq["k_fp4"], kq["k_sf"], kq["k_gscale"],
+                           vq["v_fp8"], vq["v_scale"], softmax_scale, causal, out,
+                           lse if with_lse else None, q_tile_mean, ws, stream=stream)
+    return out, (lse if with_lse else None), q_tile_mean
 
 
 def decode(q, kq, vq, softmax_scale, num_splits, out_dtype=None, with_lse=False, ws=None, out=None,

@@ -121,16 +121,22 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
   if (!k || !k_fp4 || !k_sf || !k_gscale || !ws) return MPFA_ERR_INVALID;
   if (!aligned16(k) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(ws))
     return MPFA_ERR_INVALID;
-  const bool smooth = k_mean != nullptr || delta_s != nullptr;
+  // smooth: K centred and delta_s written; centred only (k_mean without
+  // delta_s, no q): the cache of the per-tile mean prefill; direct: neither.
+  const bool center = k_mean != nullptr;
+  const bool smooth = delta_s != nullptr;
   if (smooth) {
-    if (!k_mean || !delta_s || !q_mean) return MPFA_ERR_INVALID;
+    if (!k_mean || !q_mean) return MPFA_ERR_INVALID;
     if ((st = check_heads(Hq, Hkv, B))) return st;
     if (q) {
       if (!dtype_ok(q_dtype)) return MPFA_ERR_UNSUPPORTED;
       if (!aligned16(q)) return MPFA_ERR_INVALID;
     }
-    if (!aligned16(q_mean) || !aligned16(k_mean) || !aligned16(delta_s)) return MPFA_ERR_INVALID;
+    if (!aligned16(q_mean) || !aligned16(delta_s)) return MPFA_ERR_INVALID;
+  } else if (center && q) {
+    return MPFA_ERR_INVALID;  // a Q mean is only needed for delta_s
   }
+  if (center && !aligned16(k_mean)) return MPFA_ERR_INVALID;
   const int Hq_ws = (smooth && q) ? Hq : 0;
   const QuantKWs L = quant_k_layout(B, Hq_ws, Hkv);
   if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
@@ -141,10 +147,10 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
   const int kb = k_dtype == MPFA_BF16;
   launch_fill_u32((uint32_t*)w, (int64_t)(L.total / 4), 0u, s);
   const float* kc_mean = nullptr;
-  if (smooth) {
+  if (center) {
     launch_channel_mean(k, kb, B * Hkv, N, (uint32_t*)(w + L.kmax),
                         (unsigned long long*)(w + L.ksum), k_mean, s);
-    if (q)
+    if (smooth && q)
       launch_channel_mean(q, q_dtype == MPFA_BF16, B * Hq, N, (uint32_t*)(w + L.qmax),
                           (unsigned long long*)(w + L.qsum), q_mean, s);
     kc_mean = k_mean;
@@ -278,11 +284,69 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.G = Hq / Hkv;
   p.q_mean = delta_s ? q_mean : nullptr;
   p.k_mean = delta_s ? k_mean : nullptr;
+  p.q_tile_mean = nullptr;
   p.k_f16 = k_f16;
   p.k_gscale = k_gscale;
   p.v_fp8 = v_fp8;
   p.v_scale = v_scale;
   p.delta_s = delta_s;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.out = out;
+  p.out_bf16 = out_dtype == MPFA_BF16;
+  p.lse = lse;
+  p.q_amax = amax;
+  p.n_units = n_units;
+  launch_prefill(p, s);
+  return launch_status();
+}
+
+int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                           const float* k_mean, const uint8_t* k_fp4, const uint8_t* k_sf,
+                           const float* k_gscale, const uint8_t* v_fp8, const float* v_scale,
+                           float softmax_scale, int causal, void* out, int out_dtype, float* lse,
+                           float* q_tile_mean, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if ((st = check_heads(Hq, Hkv, B))) return st;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!q || !k_mean || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out ||
+      !q_tile_mean || !ws)
+    return MPFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_mean) || !aligned16(k_fp4) || !aligned16(k_sf) ||
+      !aligned16(v_fp8) || !aligned16(out) || !aligned16(q_tile_mean) || !aligned16(ws) ||
+      (lse && !aligned16(lse)))
+    return MPFA_ERR_INVALID;
+  if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
+  const PrefillWs L = prefill_layout(B, Hkv, N);
+  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
+  const int n_units = (N + 255) / 256;
+  if ((int64_t)n_units * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int qb = q_dtype == MPFA_BF16;
+  uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
+  uint8_t* k_img = (uint8_t*)ws + L.k_f16;
+  launch_tile_mean(q, qb, B * Hq, N, q_tile_mean, s);
+  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
+  launch_centered_amax(q, qb, B * Hq, N, q_tile_mean, amax, s, /*tile_means=*/true);
+  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_img, s, /*bf16=*/true);
+  PrefillParams p;
+  p.q = q;
+  p.q_bf16 = qb;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.G = Hq / Hkv;
+  p.q_mean = nullptr;
+  p.k_mean = k_mean;
+  p.q_tile_mean = q_tile_mean;
+  p.k_f16 = k_img;
+  p.k_gscale = k_gscale;
+  p.v_fp8 = v_fp8;
+  p.v_scale = v_scale;
+  p.delta_s = nullptr;
   p.scale = softmax_scale;
   p.causal = causal != 0;
   p.out = out;

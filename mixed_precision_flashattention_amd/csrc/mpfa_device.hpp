@@ -156,6 +156,17 @@ __device__ __forceinline__ void expand_fp4x8(uint32_t w, f16x2 s2, uint32_t* out
   out[3] = __builtin_bit_cast(uint32_t, a3 * s2);
 }
 
+// The same eight codes as BF16 (the products are exact there too): pairs of
+// elements 2i (low half) and 2i + 1 (high half) of the word's byte i.
+__device__ __forceinline__ void expand_fp4x8_bf16(uint32_t w, float s, uint32_t* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = e2m1_value((w >> (8 * i)) & 15u) * s;
+    const float hi = e2m1_value((w >> (8 * i + 4)) & 15u) * s;
+    out[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+}
+
 __device__ __forceinline__ f16x2 e4m3_scale_f16x2(uint32_t code) {
   const _Float16 h = (_Float16)e4m3_value_pos(code & 0x7Fu);
   return f16x2{h, h};

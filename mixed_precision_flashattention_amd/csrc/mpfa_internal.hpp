@@ -10,8 +10,9 @@ struct PrefillParams {
   int q_bf16;
   int B, Hq, Hkv, N, G;
   const float* q_mean;  // smoothing only
-  const float* k_mean;  // smoothing only (LSE offset)
-  const uint8_t* k_f16;  // K~ expanded to FP16 by the pre-pass, [B, Hkv, N, 128]
+  const float* k_mean;  // smoothing and per-tile mean mode (LSE offset)
+  const float* q_tile_mean;  // per-tile mean mode: [B, Hq, ceil(N/128), 128]; else NULL
+  const uint8_t* k_f16;  // K~ block images from the pre-pass (BF16 in the per-tile mode)
   const float* k_gscale;
   const uint8_t* v_fp8;
   const float* v_scale;
@@ -65,7 +66,8 @@ void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
                          unsigned long long* sums, float* mean, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
-                          uint32_t* out, hipStream_t st);
+                          uint32_t* out, hipStream_t st, bool tile_means = false);
+void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st);
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
                              hipStream_t st);
@@ -87,7 +89,7 @@ void launch_append_kv_paged(const void* k_new, const void* v_new, int is_bf16, i
 
 // prefill.hip
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
-                     uint8_t* k_f16, hipStream_t st);
+                     uint8_t* k_img, hipStream_t st, bool bf16 = false);
 void launch_prefill(const PrefillParams& p, hipStream_t st);
 
 // decode.hip

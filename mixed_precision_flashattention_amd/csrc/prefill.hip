@@ -137,7 +137,7 @@ __device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, in
 // The K~ operands of head-dim step kc + 1 are read from LDS while the four
 // MFMAs of step kc run (the scheduling barriers keep the reads that early),
 // so the matrix core does not wait on LDS latency.
-template <bool SMOOTH>
+template <bool SMOOTH, bool BF16>
 __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
                                             const uint16_t* dblk, const int (&koff)[4],
                                             const int (&kbase)[4], const i32x4 (&qf)[8],
@@ -167,9 +167,10 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      s[t] = (SMOOTH || kc > 0) ? mfma32_f16(a[kc & 1][t], qf[kc], s[t])
-                                : mfma32_f16(a[kc & 1][t], qf[kc], f32x16{});
+    for (int t = 0; t < 4; ++t) {
+      const f32x16 c = (SMOOTH || kc > 0) ? s[t] : f32x16{};
+      s[t] = BF16 ? mfma32_bf16(a[kc & 1][t], qf[kc], c) : mfma32_f16(a[kc & 1][t], qf[kc], c);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -268,9 +269,13 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
 // vector ALUs of every SIMD are busy at the same time.  Both groups read
 // the same K~ / V / Delta_S blocks from LDS (double-buffered, loaded two
 // steps ahead by all 8 waves).
-template <bool SMOOTH>
+// MODE 0: direct; 1: smoothing by the sequence means with the rank-one
+// Delta_S step; 2: per-tile means, the tile mean folded into a BF16 query
+// operand against BF16 K~ images (no rank-one step).
+template <int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
+  constexpr bool SMOOTH = MODE == 1, TILE = MODE == 2;
   __shared__ __align__(16) uint8_t smem_k[2][kBlk * kRowBytes];  // K~ blocks (Q~ in the prologue)
   __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];      // V blocks
   __shared__ uint16_t smem_delta[2][kBlk];
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int row0 = unit * kUnitRows;
 
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
+  const int n_qtiles = (N + kBlk - 1) / kBlk;  // query tiles of the per-tile means
   const float gK = *p.k_gscale;
   const float sV = *p.v_scale;
   const float gg = gQ * gK;
@@ -304,8 +310,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       float x[16];
       const int64_t off = ((int64_t)bh * N + qrow) * kD + blk * 16;
       load16(p.q, off, p.q_bf16, x);
-      if (SMOOTH) {
-        const float* mu = p.q_mean + (int64_t)bh * kD + blk * 16;
+      if (SMOOTH || TILE) {
+        const float* mu = SMOOTH ? p.q_mean + (int64_t)bh * kD + blk * 16
+                                 : p.q_tile_mean + ((int64_t)bh * n_qtiles + (qrow >> 7)) * kD + blk * 16;
         const float* km = p.k_mean + ((int64_t)b * p.Hkv + hk) * kD + blk * 16;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -316,11 +323,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       uint32_t c[16];
       const uint32_t sc = nvfp4_block(x, gQ, c);
       const float s = e4m3_value_pos(sc);
+      if (TILE) {
+        // bf16(code value x block scale + fp32(Qbar_tile / gQ)), both sums
+        // rounded to nearest (the product is exact in fp32)
+        const float* mu = p.q_tile_mean + ((int64_t)bh * n_qtiles + (qrow >> 7)) * kD + blk * 16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f16x2 v2 = {(_Float16)(e2m1_value(c[2 * j]) * s),
-                          (_Float16)(e2m1_value(c[2 * j + 1]) * s)};
-        packed[j] = __builtin_bit_cast(uint32_t, v2);
+        for (int j = 0; j < 8; ++j) {
+          const float u0 = e2m1_value(c[2 * j]) * s + mu[2 * j] / gQ;
+          const float u1 = e2m1_value(c[2 * j + 1]) * s + mu[2 * j + 1] / gQ;
+          packed[j] = bf16_rne(u0) | (bf16_rne(u1) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f16x2 v2 = {(_Float16)(e2m1_value(c[2 * j]) * s),
+                            (_Float16)(e2m1_value(c[2 * j + 1]) * s)};
+          packed[j] = __builtin_bit_cast(uint32_t, v2);
+        }
       }
     }
     uint4* dst = reinterpret_cast<uint4*>(qstage + r * kRowBytes);
@@ -338,7 +357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int kc = 0; kc < 8; ++kc)
     qf[kc] = *reinterpret_cast<const i32x4*>(qstage + qr * kRowBytes + 16 * ((8 * h + kc) ^ qswz(qr)));
   float lse_off = 0.0f;
-  if (SMOOTH && p.lse) {
+  if ((SMOOTH || TILE) && p.lse) {
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) lse_off += lse_part[qr * 8 + blk];
     lse_off *= p.scale;
@@ -423,7 +442,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   do {                                                                                       \
     if ((J) >= 1 && (J) <= n_own) pv_block(o, smem_v[((J) - 1) & 1], pb, h, col);           \
     if ((J) < n_own) {                                                                       \
-      score_block<SMOOTH>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, kbase, qf, dB, h);  \
+      score_block<SMOOTH, TILE>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, kbase, qf, dB, h); \
     } else {                                                                                 \
       /* defining s on this path too keeps the old scores from being live */                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \
@@ -500,6 +519,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 // the whole key in that slot: it reads the key's 64 code bytes and 8 scale
 // bytes in one piece and writes its 16 chunks, so consecutive threads read
 // consecutive rows and write consecutive 16-byte slots of each chunk column.
+template <bool BF16>
 __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ codes,
                                                   const uint2* __restrict__ sf, int N, int nkb,
                                                   int64_t n_threads, uint4* __restrict__ out) {
@@ -525,10 +545,17 @@ __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ code
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int e = 2 * q4 + half;
-      const f16x2 s2 = e4m3_scale_f16x2((scw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      const uint32_t scode = (scw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
       uint32_t v[8];
-      expand_fp4x8(ww[2 * half], s2, v);
-      expand_fp4x8(ww[2 * half + 1], s2, v + 4);
+      if (BF16) {
+        const float sf = e4m3_value_pos(scode & 0x7Fu);
+        expand_fp4x8_bf16(ww[2 * half], sf, v);
+        expand_fp4x8_bf16(ww[2 * half + 1], sf, v + 4);
+      } else {
+        const f16x2 s2 = e4m3_scale_f16x2(scode);
+        expand_fp4x8(ww[2 * half], s2, v);
+        expand_fp4x8(ww[2 * half + 1], s2, v + 4);
+      }
       dst[(2 * e) * kBlk] = make_uint4(v[0], v[1], v[2], v[3]);
       dst[(2 * e + 1) * kBlk] = make_uint4(v[4], v[5], v[6], v[7]);
     }
@@ -536,20 +563,27 @@ __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ code
 }
 
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
-                     uint8_t* k_f16, hipStream_t st) {
+                     uint8_t* k_img, hipStream_t st, bool bf16) {
   const int nkb = (N + kBlk - 1) / kBlk;
   const int64_t n_threads = bhk * nkb * kBlk;
-  hipLaunchKernelGGL(k_expand_k, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint4*>(k_fp4), reinterpret_cast<const uint2*>(k_sf), N,
-                     nkb, n_threads, reinterpret_cast<uint4*>(k_f16));
+  const dim3 grid((unsigned)((n_threads + 255) / 256));
+  const auto* codes = reinterpret_cast<const uint4*>(k_fp4);
+  const auto* sf = reinterpret_cast<const uint2*>(k_sf);
+  auto* out = reinterpret_cast<uint4*>(k_img);
+  if (bf16)
+    hipLaunchKernelGGL(k_expand_k<true>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out);
+  else
+    hipLaunchKernelGGL(k_expand_k<false>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out);
 }
 
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.n_units * p.B * p.Hq);
-  if (p.delta_s)
-    hipLaunchKernelGGL(k_prefill<true>, dim3(grid), dim3(512), 0, st, p);
+  if (p.q_tile_mean)
+    hipLaunchKernelGGL(k_prefill<2>, dim3(grid), dim3(512), 0, st, p);
+  else if (p.delta_s)
+    hipLaunchKernelGGL(k_prefill<1>, dim3(grid), dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL(k_prefill<false>, dim3(grid), dim3(512), 0, st, p);
+    hipLaunchKernelGGL(k_prefill<0>, dim3(grid), dim3(512), 0, st, p);
 }
 
 }  // namespace mpfa

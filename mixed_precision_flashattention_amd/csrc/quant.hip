@@ -133,24 +133,101 @@ __global__ void k_mean_finalize(const uint32_t* __restrict__ absmax,
   mean[i] = (float)m;
 }
 
+// Channel means of each 128-row tile of a [BH, N, 128] tensor by the rule of
+// the sequence means above (amax M of the channel over the tile's rows, terms
+// rounded to integers at unit 2^(E-30), an exact integer sum, one FP64
+// division by the tile's row count).  One block per (tile, bh); thread
+// (rl, cg) holds rows rl, rl + 16, ... of the tile for channels 8 cg .. +7,
+// so both passes read the rows once.  mean: [BH, ceil(N/128), 128].
+__global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, int is_bf16, int N,
+                                                   float* __restrict__ mean) {
+  __shared__ float fred[16][kD];
+  __shared__ long long ired[16][kD];
+  __shared__ float cmax[kD];
+  const int64_t bh = blockIdx.y;
+  const int t = blockIdx.x;
+  const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  const int r0 = t * kBlk, n = min(N - r0, kBlk);
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + min(rl + 16 * i, n - 1);  // a repeated row is not summed below
+    load8(x, (bh * N + r) * kD + 8 * cg, is_bf16, v[i]);
+  }
+  float m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[j] = fmaxf(m[j], fabsf(v[i][j]));
+    fred[rl][8 * cg + j] = m[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fred[i][threadIdx.x]);
+    cmax[threadIdx.x] = a;
+  }
+  __syncthreads();
+  long long acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float M = cmax[8 * cg + j];
+    int E = 0;
+    if (M != 0.0f) frexpf(M, &E);
+    const double unit_inv = M != 0.0f ? ldexp(1.0, 30 - E) : 0.0;
+    acc[j] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (rl + 16 * i < n) acc[j] += (long long)__builtin_rint((double)v[i][j] * unit_inv);
+    ired[rl][8 * cg + j] = acc[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    long long S = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S += ired[i][threadIdx.x];
+    const float M = cmax[threadIdx.x];
+    float out = 0.0f;
+    if (M != 0.0f) {
+      int E;
+      frexpf(M, &E);
+      out = (float)(((double)S / (double)n) * ldexp(1.0, E - 30));
+    }
+    mean[(bh * gridDim.x + t) * kD + threadIdx.x] = out;
+  }
+}
+
 // max |fp32(x - mean[bh, d])| over a whole [BH, N, 128] tensor (mean may be
 // NULL).  Same grid and thread layout as the channel statistics; each thread
 // keeps one running max, the block reduces it (wave shuffles, then LDS) and
 // issues a single atomic.
+// With tile_means set, mean holds one row of channel means per 128-row tile,
+// [BH, ceil(N/128), 128], and row r is centred by the mean of tile r / 128.
 __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ x, int is_bf16,
                                                        int N, int rows_per_block,
                                                        const float* __restrict__ mean,
+                                                       int tile_means,
                                                        uint32_t* __restrict__ out) {
   __shared__ float red[4];
   const int64_t bh = blockIdx.y;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
   float mu[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) mu[j] = mean ? mean[bh * kD + 8 * cg + j] : 0.0f;
+  for (int j = 0; j < 8; ++j) mu[j] = (mean && !tile_means) ? mean[bh * kD + 8 * cg + j] : 0.0f;
   const int r_begin = blockIdx.x * rows_per_block;
   const int r_end = min(N, r_begin + rows_per_block);
+  const int64_t n_tiles = (N + kBlk - 1) / kBlk;
   float m = 0.0f;
   for (int r = r_begin + rl; r < r_end; r += 128) {
+    if (tile_means) {
+      // r_begin is a multiple of 128, so the rows r - rl .. r - rl + 127 this
+      // step reads (including the clamped repeat of the last row) share a tile
+      const float* mt = mean + (bh * n_tiles + ((r - rl) >> 7)) * kD + 8 * cg;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mu[j] = mt[j];
+    }
     float v[8][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)  // a repeated row does not change the max
@@ -421,11 +498,17 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
 }
 
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
-                          uint32_t* out, hipStream_t st) {
+                          uint32_t* out, hipStream_t st, bool tile_means) {
   const int rows = stat_rows_per_block(BH, N, 128);
   dim3 grid((unsigned)((N + rows - 1) / rows), BH);
-  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean,
+                     (int)tile_means, out);
   hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, out);
+}
+
+void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st) {
+  dim3 grid((unsigned)((N + kBlk - 1) / kBlk), BH);
+  hipLaunchKernelGGL(k_tile_mean, grid, dim3(256), 0, st, x, is_bf16, N, mean);
 }
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,

@@ -132,6 +132,27 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, f, ws_bytes=16) == WS
 
 
+def _prefill_tile(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, k_mean=f.p, k_fp4=f.p, k_sf=f.p,
+             k_gscale=f.p, v_fp8=f.p, v_scale=f.p, scale=0.088, causal=1, out=f.p, out_dtype=1,
+             lse=None, q_tile_mean=f.p, ws=f.p, ws_bytes=256, stream=None)
+    a.update(kw)
+    return lib.mpfa_prefill_tile_mean(*a.values())
+
+
+def test_prefill_tile_mean_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, UNSUP, WS = -1, -2, -3
+    assert _prefill_tile(lib, f, D=64) == UNSUP
+    assert _prefill_tile(lib, f, q_dtype=5) == UNSUP
+    assert _prefill_tile(lib, f, Hq=3) == INVALID
+    assert _prefill_tile(lib, f, k_mean=None) == INVALID  # K must be cached centred
+    assert _prefill_tile(lib, f, q_tile_mean=None) == INVALID
+    assert _prefill_tile(lib, f, q_tile_mean=f.mis) == INVALID
+    assert _prefill_tile(lib, f, scale=-1.0) == INVALID
+    assert _prefill_tile(lib, f, ws_bytes=16) == WS  # the workspace of mpfa_prefill
+
+
 def test_decode_rejects_bad_arguments(lib):
     f = _Fake()
     INVALID, UNSUP, WS = -1, -2, -3
@@ -147,7 +168,9 @@ def test_quantizers_reject_bad_arguments(lib):
     f = _Fake()
     qk = lib.mpfa_quantize_k_nvfp4
     # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, ws_bytes, stream)
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    # centring only (k_mean without delta_s) takes no query tensor
+    assert qk(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, None, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, f.mis, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
     assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
     assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
     assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -2
