@@ -65,7 +65,8 @@ def lib() -> ctypes.CDLL:
             "oracle_fp8_scale": (f32, [f32]),
             "oracle_fp8_quantize": (None, [P, i64, f32, P]),
             "oracle_delta_s": (None, [P, P, i64, i32, P]),
-            "oracle_attn_state": (None, [i32, i32, P, P, P, P, P, i64, i64, i32, f64, i32, P, P, P]),
+            "oracle_attn_state": (None, [i32, i32, P, P, P, P, P, i64, i64, i32, f64, i32, P, P, P,
+                                         P]),
             "oracle_merge_states": (None, [i32, i32, i32, P, P, P, f64, P, P, P]),
             "oracle_e4m3_encode_array": (None, [P, i64, P]),
             "oracle_e2m1_encode_array": (None, [P, i64, P]),
@@ -199,11 +200,15 @@ def delta_s(qmean: np.ndarray, kc: np.ndarray) -> np.ndarray:
     return out
 
 
-def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, block=KV_BLOCK):
+def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, block=KV_BLOCK,
+               ambiguity=False):
     """Blocked online-softmax state of R rows over keys [kv_begin, kv_end).
 
     q [R, D] f64; row_pos [R] int64 (-1: every key visible); k, v [Nk, D] f64;
-    delta [Nk] f64 or None.  Returns (m [R], l [R], acc [R, D]) in FP64."""
+    delta [Nk] f64 or None.  Returns (m [R], l [R], acc [R, D]) in FP64, and
+    with ambiguity=True also amb [R, D]: how far acc may move if the keys
+    whose 448 p sits within 2^-16 of an E4M3 rounding midpoint round the
+    other way (both roundings are correct for a p computed in FP32)."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
@@ -212,13 +217,15 @@ def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, b
     m = np.empty(R)
     l = np.empty(R)
     acc = np.empty((R, D))
+    amb = np.empty((R, D)) if ambiguity else None
     dp = None
     if delta is not None:
         delta = np.ascontiguousarray(delta, dtype=np.float64)
         dp = _p(delta)
     lib().oracle_attn_state(D, R, _p(q), _p(rp), _p(k), _p(v), dp, int(kv_begin), int(kv_end),
-                            int(block), float(scale), int(bool(quant_p)), _p(m), _p(l), _p(acc))
-    return m, l, acc
+                            int(block), float(scale), int(bool(quant_p)), _p(m), _p(l), _p(acc),
+                            _p(amb) if ambiguity else None)
+    return (m, l, acc, amb) if ambiguity else (m, l, acc)
 
 
 def merge_states(m, l, acc, scale):

@@ -272,10 +272,31 @@ void oracle_delta_s(const float* qmean, const float* kc, int64_t T, int D, uint1
  * Outputs the partial state (m, l, acc); m = -inf and l = 0 when the row saw
  * no key.  q is [R][D], k and v are [*][D] indexed by absolute key, delta is
  * indexed by absolute key or NULL.                                          */
+/* The other E4M3 magnitude a value a >= 0 may round to when it lies within
+ * 2^-16 (relative) of the midpoint between two neighbouring magnitudes --
+ * closer than an FP32 computation of p can place it -- else the rounded
+ * value ph itself.                                                          */
+static double e4m3_alternative(double a, double ph) {
+  int lo = 0, hi = 126;
+  double mid;
+  if (a >= g_e4m3_mag[126] || a <= 0.0) return ph;
+  while (hi - lo > 1) {
+    int m = (lo + hi) / 2;
+    if (g_e4m3_mag[m] <= a) lo = m; else hi = m;
+  }
+  mid = 0.5 * (g_e4m3_mag[lo] + g_e4m3_mag[hi]);
+  if (fabs(a - mid) > ldexp(a, -16)) return ph;
+  return ph == g_e4m3_mag[lo] ? g_e4m3_mag[hi] : g_e4m3_mag[lo];
+}
+
+/* out_amb (NULL or [R][D]): alongside acc, the sum over keys whose 448 p is
+ * that close to an E4M3 rounding midpoint of |other rounding - p^| * |v|,
+ * rescaled with acc -- the most a different (equally valid) rounding of
+ * those keys can move acc.  It does not change m, l or acc.                 */
 void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
                        const double* k, const double* v, const double* delta,
                        int64_t kv_begin, int64_t kv_end, int block, double scale, int quant_p,
-                       double* out_m, double* out_l, double* out_acc) {
+                       double* out_m, double* out_l, double* out_acc, double* out_amb) {
   const double lam = scale / log(2.0);
   int r;
   init_tables();
@@ -283,10 +304,13 @@ void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
   for (r = 0; r < R; ++r) {
     double m = -INFINITY, l = 0.0;
     double* acc = out_acc + (int64_t)r * D;
+    double* amb = out_amb ? out_amb + (int64_t)r * D : NULL;
     double* s = (double*)malloc(sizeof(double) * (size_t)block);
     int64_t b0;
     int d;
     for (d = 0; d < D; ++d) acc[d] = 0.0;
+    if (amb)
+      for (d = 0; d < D; ++d) amb[d] = 0.0;
     for (b0 = kv_begin; b0 < kv_end; b0 += block) {
       int64_t b1 = b0 + block < kv_end ? b0 + block : kv_end;
       int64_t last = b1; /* exclusive end of visible keys in this block */
@@ -305,11 +329,18 @@ void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
       alpha = (m == -INFINITY) ? 0.0 : exp2(lam * (m - mn));
       l *= alpha;
       for (d = 0; d < D; ++d) acc[d] *= alpha;
+      if (amb)
+        for (d = 0; d < D; ++d) amb[d] *= alpha;
       for (j = b0; j < last; ++j) {
         double p = exp2(lam * (s[j - b0] - mn));
         double ph = quant_p ? oracle_e4m3_decode(oracle_e4m3_encode(448.0 * p)) : 448.0 * p;
         l += p;
         for (d = 0; d < D; ++d) acc[d] += ph * v[j * D + d];
+        if (amb && quant_p) {
+          double alt = e4m3_alternative(448.0 * p, ph);
+          if (alt != ph)
+            for (d = 0; d < D; ++d) amb[d] += fabs(alt - ph) * fabs(v[j * D + d]);
+        }
       }
       m = mn;
     }

@@ -235,13 +235,16 @@ class Operands:
 
 
 def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=None, out_f64=False,
-                 ops=None):
+                 ops=None, ambiguity=False):
     """Causal (or full) prefill, MpFA §5.1 second stage, for the selected rows.
 
     rows: None (every row) or an int array [R, 3] of (b, q-head, position).
     ops: an Operands already built from the same q, k, v and mode (else built here).
     Returns (O [R, D] fp32, LSE [R] f64, rows) -- O = acc * s_V / (448 l), LSE in
-    natural log with the smoothing row offset scale * (Q_i . Kbar) added back."""
+    natural log with the smoothing row offset scale * (Q_i . Kbar) added back;
+    with ambiguity=True also AMB [R, D], the most O may move when the P^
+    roundings that sit on an E4M3 midpoint (see ``attn_state``) go the other
+    way."""
     q = np.asarray(q, dtype=F32)
     B, Hq, N, D = q.shape
     if ops is None:
@@ -253,6 +256,7 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
     rows = np.asarray(rows, dtype=np.int64)
     O = np.empty((len(rows), D), dtype=F64 if out_f64 else F32)
     LSE = np.empty(len(rows))
+    AMB = np.zeros((len(rows), D))
     for b in range(B):
         for hk in range(q.shape[1] // G):
             kt = vt = None
@@ -264,15 +268,16 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
                     kt, vt = ops.k(b, hk), ops.v(b, hk)
                 pos = rows[sel, 2]
                 row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
-                m, l, acc = attn_state(ops.q(b, h, pos), row_pos, kt, vt, ops.delta(b, h), 0, N, scale,
-                                       ops.quant_p)
+                m, l, acc, amb = attn_state(ops.q(b, h, pos), row_pos, kt, vt, ops.delta(b, h), 0, N,
+                                            scale, ops.quant_p, ambiguity=True)
                 off = None
                 if smooth:
                     off = scale * (q[b, h][pos].astype(F64) @ ops.k_mean[b, hk].astype(F64))
                 o, lse = _finalize(m, l, acc, ops.s_v, scale, off, out_f64)
                 O[sel] = o
                 LSE[sel] = lse
-    return O, LSE, rows
+                AMB[sel] = amb * ops.s_v / (P_SCALE * l[:, None])
+    return (O, LSE, rows, AMB) if ambiguity else (O, LSE, rows)
 
 
 # --------------------------------------------- per-query-tile mean mode --
@@ -327,7 +332,8 @@ def tile_operand(codes, sf, g, tm, tile=Q_TILE):
     return bf16_to_f64(bf16_rne(u)) * float(g)
 
 
-def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=None, out_f64=False):
+def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=None, out_f64=False,
+                           ambiguity=False):
     """Prefill in the per-query-tile mean mode for the selected rows.
 
     K is centred by its sequence mean Kbar and quantized as in smoothing mode
@@ -337,7 +343,8 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
     Qbar_tile . K~_c[j]; the rest is the prefill of ``prefill_rows``.  The
     LSE adds back the row term scale * (Q_i . Kbar), as in smoothing mode.
     identity: no quantizer (the operand is Q_c + Qbar_tile in FP64, K~_c = K_c,
-    P not rounded).  Returns (O, LSE, rows)."""
+    P not rounded).  Returns (O, LSE, rows), plus AMB as in ``prefill_rows``
+    with ambiguity=True."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     v = np.asarray(v, dtype=F32)
@@ -367,6 +374,7 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
     rows = np.asarray(rows, dtype=np.int64)
     O = np.empty((len(rows), D), dtype=F64 if out_f64 else F32)
     LSE = np.empty(len(rows))
+    AMB = np.zeros((len(rows), D))
     for b in range(B):
         for hk in range(Hkv):
             kt = vt = None
@@ -378,13 +386,14 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
                     kt, vt = kdeq(b, hk), vdeq(b, hk)
                 pos = rows[sel, 2]
                 row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
-                m, l, acc = attn_state(np.ascontiguousarray(qop[b, h][pos]), row_pos, kt, vt, None, 0, N,
-                                       scale, quant_p)
+                m, l, acc, amb = attn_state(np.ascontiguousarray(qop[b, h][pos]), row_pos, kt, vt, None,
+                                            0, N, scale, quant_p, ambiguity=True)
                 off = scale * (q[b, h][pos].astype(F64) @ k_mean[b, hk].astype(F64))
                 o, lse = _finalize(m, l, acc, s_v, scale, off, out_f64)
                 O[sel] = o
                 LSE[sel] = lse
-    return O, LSE, rows
+                AMB[sel] = amb * s_v / (P_SCALE * l[:, None])
+    return (O, LSE, rows, AMB) if ambiguity else (O, LSE, rows)
 
 
 def decode_partitions(n_kv: int, num_splits: int, block: int = KV_BLOCK):

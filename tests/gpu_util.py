@@ -25,19 +25,28 @@ def host(t):
     return t.cpu().numpy()
 
 
-def assert_close(name, got, ref, atol=ATOL, rtol=RTOL):
+def assert_close(name, got, ref, atol=ATOL, rtol=RTOL, slack=None):
+    """|got - ref| <= atol + rtol |ref| (+ slack: the oracle's per-element bound
+    on what an equally valid rounding of a P^ value lying on an E4M3 midpoint
+    can change, zero almost everywhere)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite GPU values"
     err = np.abs(got - ref)
-    bad = err > atol + rtol * np.abs(ref)
+    tol = atol + rtol * np.abs(ref)
+    if slack is not None:
+        slack = np.asarray(slack, dtype=np.float64).reshape(got.shape)
+        say(f"  {name}: {int((slack > 0).any(axis=-1).sum())} rows hold a P^ rounding on an E4M3 "
+            f"midpoint (slack up to {slack.max():.2e})")
+        tol = tol + slack
+    bad = err > tol
     rel = err / np.maximum(np.abs(ref), 1e-30)
     say(f"  {name}: max_abs={err.max():.3e} max_rel(|ref|>1e-3)="
         f"{rel[np.abs(ref) > 1e-3].max() if (np.abs(ref) > 1e-3).any() else 0:.3e} "
         f"violations={int(bad.sum())}/{bad.size}")
     if bad.any():
-        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"{name}: {int(bad.sum())} elements out of tolerance; worst at {i}: "
                              f"gpu={got[i]!r} oracle={ref[i]!r}")
 

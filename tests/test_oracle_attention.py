@@ -207,3 +207,25 @@ def test_smoothing_reduces_error_on_strong_outliers(oracle_mod):
         O, _, _ = oracle_mod.prefill_rows(q, k, v, scale, smooth=smooth)
         errs[smooth] = np.linalg.norm(O - Oe) / np.linalg.norm(Oe)
     assert errs[True] < errs[False]
+
+
+def test_ambiguity_bound_marks_p_on_an_e4m3_midpoint(oracle_mod):
+    """448 p = 432 lies halfway between the E4M3 values 416 and 448: the bound
+    is 32 |v| for that key and zero for a key far from a midpoint, and asking
+    for it leaves m, l and acc unchanged."""
+    lam = 0.1 / math.log(2.0)
+    ds = math.log2(432.0 / 448.0) / lam  # 448 * 2^(lam * ds) = 432
+    D = 128
+    q = np.zeros((1, D))
+    q[0, 0] = 1.0
+    k = np.zeros((3, D))
+    k[1, 0] = ds
+    k[2, 0] = math.log2(300.0 / 448.0) / lam  # 448 p = 300: far from a midpoint (288 | 320)
+    v = np.random.default_rng(3).standard_normal((3, D))
+    m, l, acc, amb = oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 3, 0.1, True, ambiguity=True)
+    np.testing.assert_allclose(amb[0], 32.0 * np.abs(v[1]), rtol=0, atol=0)
+    m2, l2, acc2 = oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 3, 0.1, True)
+    assert m[0] == m2[0] and l[0] == l2[0] and np.array_equal(acc, acc2)
+    # without P rounding there is nothing to be ambiguous about
+    _, _, _, amb0 = oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 3, 0.1, False, ambiguity=True)
+    assert not amb0.any()
