@@ -10,7 +10,8 @@ pair) per second of whole step.
 
 Also reported, each timed on its own with HIP events on the launch stream:
 the prefill call alone (the dominant kernel, against the mixed FP4/FP8 MFMA
-roofline), the direct (unsmoothed) prefill, the Qwen3-14B-shaped 32K causal
+roofline), the direct (unsmoothed) prefill, the prefill with per-128-row
+query-tile means (mpfa_prefill_tile_mean), the Qwen3-14B-shaped 32K causal
 prefill (40 query / 8 KV heads) against the same roofline, and the split-KV
 decode of the Llama-3.1-8B-shaped 128K cache (batch 16, 32 splits) as KV
 bytes per second against HBM bandwidth, the same caches as a shuffled pool
@@ -293,13 +294,17 @@ def write_traffic(run_dir, args):
     # dispatches of one call relative to its main kernel: prefill = fill, Q amax
     # pre-pass and its fold, K expansion, attention; decode = fill, Q amax and
     # its fold, split, combine
-    calls = [("prefill", "prefill", "k_prefill<true>", (-4, -3, -2, -1, 0),
+    # prefill_tile = tile means, fill, Q amax and its fold, K expansion, attention
+    calls = [("prefill", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
               f"mpfa_prefill {args.workload}"),
              ("decode", "decode", "k_decode_split<true, false>", (-3, -2, -1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
-        calls.append(("prefill_long", "prefill", "k_prefill<true>", (-4, -3, -2, -1, 0),
+        calls.append(("prefill_long", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
                       f"mpfa_prefill {args.long_workload}"))
+    if os.path.isdir(os.path.join(run_dir, "pmc_prefill_tile_FETCH_SIZE")):
+        calls.append(("prefill_tile", "prefill", "k_prefill<2>", (-5, -4, -3, -2, -1, 0),
+                      f"mpfa_prefill_tile_mean {args.workload}"))
     for op, kind, main_kernel, offsets, name in calls:
         fv, fn = load(op, "FETCH_SIZE")
         wv, wn = load(op, "WRITE_SIZE")
@@ -322,8 +327,9 @@ def write_traffic(run_dir, args):
 
 def profile_only(args, mpfa, synth, dev):
     """Three calls of one operation for rocprofv3 counter passes: the prefill
-    call of the bench workload, the decode call of the decode workload, or a
-    1 GiB device-to-device copy (the calibration of FETCH_SIZE / WRITE_SIZE)."""
+    call of the bench workload (smoothed, or with per-tile query means), the
+    decode call of the decode workload, or a 1 GiB device-to-device copy (the
+    calibration of FETCH_SIZE / WRITE_SIZE)."""
     import torch
     if args.only == "copy":
         a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -340,6 +346,16 @@ def profile_only(args, mpfa, synth, dev):
                          dtype=torch.uint8, device=dev)
         for _ in range(3):
             mpfa.prefill(x["q"], kq, vq, cfg.scale, causal=True, out=out, ws=ws)
+    elif args.only == "prefill_tile":
+        cfg = synth.config(args.workload)
+        x = synth.device_inputs(cfg, dev)
+        kq = mpfa.quantize_k(x["k"])
+        vq = mpfa.quantize_v(x["v"])
+        out = torch.empty(x["q"].shape, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL, cfg.B, cfg.Hq, cfg.Hkv, cfg.N),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            mpfa.prefill_tile_mean(x["q"], kq, vq, cfg.scale, causal=True, out=out, ws=ws)
     else:
         cfg = synth.config(args.decode_workload)
         x = synth.device_inputs(cfg, dev)
@@ -368,7 +384,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "prefill_tile", "decode", "copy"], default=None,
                     help="counter-collection mode: set up, run 3 calls of one operation, exit")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="build profiles/traffic.json from the rocprofv3 counter CSVs in DIR "
@@ -460,6 +476,22 @@ def main():
     log(f"[bench] direct prefill {ms_direct:.3f} ms")
     del kq_direct
 
+    # per-query-tile mean mode: a centred K cache (no Delta_S), the tile means
+    # and the attention in one call
+    kq_tile = mpfa.quantize_k(k)
+    tmean = torch.empty((B, Hq, (N + 127) // 128, D), dtype=torch.float32, device=dev)
+
+    def prefill_tile():
+        mpfa.mpfa_prefill_tile_mean(q, Hkv, kq_tile["k_mean"], kq_tile["k_fp4"], kq_tile["k_sf"],
+                                    kq_tile["k_gscale"], vq["v_fp8"], vq["v_scale"], cfg.scale, True,
+                                    out, None, tmean, ws_p)
+
+    ms_tile = time_calls(prefill_tile, args.steps, 2)
+    ach_tile = flops / (ms_tile * 1e-3) / 1e12
+    log(f"[bench] tile-mean prefill {ms_tile:.3f} ms -> {ach_tile:.1f} TFLOP/s "
+        f"({ach_tile * 1e12 / PEAK_MIXED:.3f} of the FP4/FP8 roofline)")
+    del kq_tile, tmean
+
     result = {
         "metric": "attention TFLOPS (prefill) and KV GB/s (decode) vs MI355X roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -476,6 +508,12 @@ def main():
                      "traffic": measured_traffic("mpfa_prefill llama8b_prefill_16k"),
                      "flops_per_launch": flops, "ms_per_launch": round(ms_prefill, 4)},
         "prefill_ms": round(ms_prefill, 4), "prefill_direct_ms": round(ms_direct, 4),
+        "prefill_tile_mean": {"ms": round(ms_tile, 4),
+                              "roofline": {"bound": "mfma", "achieved": round(ach_tile, 2),
+                                           "peak": round(PEAK_MIXED / 1e12, 1), "unit": "TFLOP/s",
+                                           "frac": round(ach_tile * 1e12 / PEAK_MIXED, 4),
+                                           "traffic": measured_traffic(
+                                               "mpfa_prefill_tile_mean llama8b_prefill_16k")}},
         "stage_one_ms": round(ms_stage1, 4),
         "compensation_overhead": round(ms_prefill / ms_direct - 1.0, 4),
         "env": {"gpu": torch.cuda.get_device_name(0),

@@ -122,6 +122,52 @@ def test_fullsize_prefill_llama8b_128k_lse(mpfa, oracle_mod):
     _prefill_full(mpfa, oracle_mod, "llama8b_prefill_128k_lse")
 
 
+def test_fullsize_prefill_tile_mean_llama8b_16k(mpfa, oracle_mod):
+    """The per-query-tile mean prefill on the 16K benchmark inputs: every tile
+    mean and the centred K cache's mean and global scale exactly, sampled
+    cache rows byte for byte, output and LSE on the sampled rows."""
+    import torch
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("llama8b_prefill_16k")
+    say(f"case: full-size tile-mean prefill {cfg.name} B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} "
+        f"{cfg.dtype} causal (benchmark inputs)")
+    t0 = time.time()
+    x = synth.device_inputs(cfg, "cuda")
+    kq = mpfa.quantize_k(x["k"])
+    vq = mpfa.quantize_v(x["v"])
+    rows = synth.sample_rows(cfg)
+    idx = [torch.from_numpy(rows[:, i]).cuda() for i in range(3)]
+    out, _, _ = mpfa.prefill_tile_mean(x["q"], kq, vq, cfg.scale, causal=True, out_dtype=torch.bfloat16)
+    got_bf16 = _h(out[idx[0], idx[1], idx[2]])
+    del out
+    out, lse, tm = mpfa.prefill_tile_mean(x["q"], kq, vq, cfg.scale, causal=True,
+                                          out_dtype=torch.float32, with_lse=True)
+    got = _h(out[idx[0], idx[1], idx[2]])
+    got_lse = _h(lse[idx[0], idx[1], idx[2]])
+    got_tm = _h(tm)
+    del out, lse, tm
+    torch.cuda.synchronize()
+    say(f"  gpu calls done ({time.time() - t0:.1f} s); copying inputs to the host")
+    qh, kh, vh = _h(x["q"]), _h(x["k"]), _h(x["v"])
+    kref = oracle_mod.quantize_k(kh)
+    assert_bytes_equal("tile means", got_tm.view(np.uint32), oracle_mod.tile_means(qh).view(np.uint32))
+    assert_bytes_equal("k_mean", _h(kq["k_mean"]).view(np.uint32), kref["k_mean"].view(np.uint32))
+    assert_bytes_equal("k_gscale", _h(kq["k_gscale"]).view(np.uint32),
+                       np.asarray([kref["k_gscale"]], dtype=np.float32).view(np.uint32))
+    for hk in sorted({0, cfg.Hkv - 1}):
+        assert_bytes_equal(f"k_fp4[kv={hk}]", _h(kq["k_fp4"][0, hk]), kref["k_fp4"][0, hk])
+        assert_bytes_equal(f"k_sf[kv={hk}]", _h(kq["k_sf"][0, hk]), kref["k_sf"][0, hk])
+    del kq, vq, x
+    torch.cuda.empty_cache()
+    say(f"  oracle attention on {len(rows)} sampled rows ({time.time() - t0:.1f} s)")
+    O, LSE, _, AMB = oracle_mod.prefill_tile_mean_rows(qh, kh, vh, cfg.scale, causal=True, rows=rows,
+                                                       ambiguity=True)
+    say(f"  oracle done ({time.time() - t0:.1f} s)")
+    assert_close("out bf16", got_bf16, O, rtol=1e-2 + BF16_EXTRA, slack=AMB)
+    assert_close("out f32", got, O, slack=AMB)
+    assert_close("lse", got_lse, LSE, atol=LSE_ATOL, rtol=0.0)
+
+
 def test_fullsize_decode_llama8b_128k(mpfa, oracle_mod):
     import torch
     from mixed_precision_flashattention_amd import synth
