@@ -134,7 +134,7 @@ def cpu_baseline(cfg, target_s=12.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     done_rows, done_flops, spent = 0, 0.0, 0.0
     batch = max(threads, 16)
-    while spent < target_s and done_rows < cfg.N:
+    while spent < target_s and done_rows < 16 * cfg.N:
         rows = np.sort(rng.integers(0, cfg.N, batch)).astype(np.int64)
         t0 = time.perf_counter()
         oracle.attn_state(ops.q(0, 0, rows), rows, kt, vt, delta, 0, cfg.N, cfg.scale, True)
@@ -148,8 +148,9 @@ def cpu_baseline(cfg, target_s=12.0):
 
 def accuracy_report(mpfa):
     """Error of the GPU output against FP32 exact attention (the oracle's FP64
-    reference on the unquantized inputs), with and without smoothing, on the
-    small fp32 configuration (1024 tokens, 2/1 heads, 8 outlier channels)."""
+    reference on the unquantized inputs) with smoothing by the sequence means,
+    without smoothing, and with per-128-row query-tile means, on the small fp32
+    configuration (1024 tokens, 2/1 heads, 8 outlier channels)."""
     import oracle
     import torch
     from mixed_precision_flashattention_amd import synth
@@ -159,13 +160,21 @@ def accuracy_report(mpfa):
     qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
     out = {}
     vq = mpfa.quantize_v(vd)
-    for smooth in (True, False):
-        kq = mpfa.quantize_k(kd, q=qd) if smooth else mpfa.quantize_k(kd, smooth=False)
-        o, _ = mpfa.prefill(qd, kq, vq, cfg.scale, causal=True, out_dtype=torch.float32)
+    for mode in ("smooth", "direct", "tile_mean"):
+        if mode == "smooth":
+            kq = mpfa.quantize_k(kd, q=qd)
+            o, _ = mpfa.prefill(qd, kq, vq, cfg.scale, causal=True, out_dtype=torch.float32)
+        elif mode == "direct":
+            kq = mpfa.quantize_k(kd, smooth=False)
+            o, _ = mpfa.prefill(qd, kq, vq, cfg.scale, causal=True, out_dtype=torch.float32)
+        else:
+            kq = mpfa.quantize_k(kd)
+            o, _, _ = mpfa.prefill_tile_mean(qd, kq, vq, cfg.scale, causal=True,
+                                             out_dtype=torch.float32)
         torch.cuda.synchronize()
         g = o.cpu().numpy().reshape(-1, 128).astype(np.float64)
         d = g - ref
-        out["smooth" if smooth else "direct"] = {
+        out[mode] = {
             "max_abs": float(np.abs(d).max()), "mean_abs": float(np.abs(d).mean()),
             "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)),
             "cos": float((g * ref).sum() / (np.linalg.norm(g) * np.linalg.norm(ref)))}
