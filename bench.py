@@ -301,12 +301,12 @@ def write_traffic(run_dir, args):
                       "then python bench.py --write-traffic DIR",
            "calls": {}}
     # dispatches of one call relative to its main kernel: prefill = fill, Q amax
-    # pre-pass and its fold, K expansion, attention; decode = fill, Q amax and
-    # its fold, split, combine
+    # pre-pass and its fold, K expansion, attention; decode = the one-workgroup
+    # Q amax, split, combine
     # prefill_tile = tile means, fill, Q amax and its fold, K expansion, attention
     calls = [("prefill", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
               f"mpfa_prefill {args.workload}"),
-             ("decode", "decode", "k_decode_split<true, false>", (-3, -2, -1, 0, 1),
+             ("decode", "decode", "k_decode_split<true, false>", (-1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
         calls.append(("prefill_long", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),

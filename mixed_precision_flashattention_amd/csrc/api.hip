@@ -386,8 +386,7 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
-  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
+  launch_rows_amax(q, q_dtype == MPFA_BF16, B * Hq, delta_s ? q_mean : nullptr, (float*)amax, s);
   DecodeParams p;
   p.q = q;
   p.q_bf16 = q_dtype == MPFA_BF16;
@@ -408,7 +407,7 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   p.v_scale = v_scale;
   p.delta_s = delta_s;
   p.scale = softmax_scale;
-  p.q_amax = amax;
+  p.q_amax_slots = (const float*)amax;
   p.ws_m = (float*)(w + L.m);
   p.ws_l = (float*)(w + L.l);
   p.ws_acc = (float*)(w + L.acc);
@@ -457,8 +456,7 @@ int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
-  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, 1, delta_s ? q_mean : nullptr, amax, s);
+  launch_rows_amax(q, q_dtype == MPFA_BF16, B * Hq, delta_s ? q_mean : nullptr, (float*)amax, s);
   DecodeParams p;
   p.q = q;
   p.q_bf16 = q_dtype == MPFA_BF16;
@@ -478,7 +476,7 @@ int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
   p.v_scale = v_scale;
   p.delta_s = delta_s;
   p.scale = softmax_scale;
-  p.q_amax = amax;
+  p.q_amax_slots = (const float*)amax;
   p.ws_m = (float*)(w + L.m);
   p.ws_l = (float*)(w + L.l);
   p.ws_acc = (float*)(w + L.acc);

@@ -39,7 +39,7 @@ struct DecodeParams {
   const float* v_scale;
   const uint16_t* delta_s;
   float scale;
-  const uint32_t* q_amax;
+  const float* q_amax_slots;  // partial maxima of |Q_c| (launch_rows_amax)
   float* ws_m;    // [B*Hq, P]
   float* ws_l;    // [B*Hq, P]
   float* ws_acc;  // [B*Hq, P, 128]
@@ -67,6 +67,11 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
                          unsigned long long* sums, float* mean, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
                           uint32_t* out, hipStream_t st, bool tile_means = false);
+// Partial maxima of |x - mean| over the rows of a [rows, 128] tensor, one
+// per slot (kRowsAmaxSlots floats, all written): the decode query amax.
+constexpr int kRowsAmaxSlots = 64;
+void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, float* slots,
+                      hipStream_t st);
 void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st);
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,

@@ -248,6 +248,43 @@ __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ 
   }
 }
 
+// max |fp32(x - mean[r, d])| over the rows of a [rows, 128] tensor (the
+// decode queries: one row per head, mean may be NULL), as kRowsAmaxSlots
+// partial maxima: workgroup i reduces rows i R .. i R + R - 1 (R =
+// ceil(rows / kRowsAmaxSlots)) and stores its maximum in out[i] (0 when it
+// has no rows).  Every slot is written, so nothing needs clearing first, and
+// there is no atomic and no fold kernel: a consumer takes the max of the
+// slots itself (one wave, one load per lane).
+__global__ __launch_bounds__(256) void k_rows_amax(const void* __restrict__ x, int is_bf16,
+                                                  int rows, const float* __restrict__ mean,
+                                                  float* __restrict__ out) {
+  __shared__ float red[4];
+  const int R = (rows + kRowsAmaxSlots - 1) / kRowsAmaxSlots;
+  const int r0 = min(rows, (int)blockIdx.x * R), r1 = min(rows, r0 + R);
+  const int64_t g0 = (int64_t)r0 * (kD / 8), g1 = (int64_t)r1 * (kD / 8);  // groups of 8
+  float m = 0.0f;
+  for (int64_t g = g0 + threadIdx.x; g < g1; g += 4 * 256) {
+    float v[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // a repeated group does not change the max
+      load8(x, min(g + 256 * k, g1 - 1) * 8, is_bf16, v[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t e = min(g + 256 * k, g1 - 1) * 8;  // channel e % 128 of row e / 128
+      float mu[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mu[j] = mean ? mean[e + j] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[k][j] - mu[j]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 // The slots of a reduced amax folded into its first word (one wave).
 __global__ __launch_bounds__(64) void k_amax_fold(uint32_t* __restrict__ out) {
   uint32_t m = out[threadIdx.x * kAmaxSlotWords];
@@ -504,6 +541,12 @@ void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float
   hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean,
                      (int)tile_means, out);
   hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, out);
+}
+
+void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, float* slots,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(k_rows_amax, dim3(kRowsAmaxSlots), dim3(256), 0, st, x, is_bf16, rows, mean,
+                     slots);
 }
 
 void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st) {
