@@ -69,10 +69,18 @@ __global__ __launch_bounds__(256) void k_channel_absmax(const void* __restrict__
   }
 }
 
+// RNE(x * 2^shift) as an integer, for |x * 2^shift| < 2^30 (see above).
+__device__ __forceinline__ long long fixed_point_term(float x, int shift) {
+  return (long long)(int)__builtin_rintf(__builtin_ldexpf(x, shift));
+}
+
 // Per (b, h, d): 64-bit fixed-point sum of x at unit 2^(E-30), where the
-// channel amax M lies in [2^(E-1), 2^E).  Each term is rounded to the
-// nearest integer (half to even) in FP64, where the scaling is exact; the
-// integer sum is exact, so the result does not depend on order.
+// channel amax M lies in [2^(E-1), 2^E).  Each term is x scaled by
+// 2^(30-E) and rounded to the nearest integer (half to even); the integer
+// sum is exact, so the result does not depend on order.  The scaled value
+// has magnitude below 2^30, so the FP32 ldexp is exact wherever the result
+// can round to a nonzero integer, the FP32 round-to-nearest-even gives the
+// same integer as in FP64, and it fits an int32.
 __global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__ x, int is_bf16,
                                                         int N, int rows_per_block,
                                                         const uint32_t* __restrict__ absmax,
@@ -80,13 +88,13 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__
   __shared__ long long red[16][kD];
   const int64_t bh = blockIdx.y;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
-  double unit_inv[8];
+  int shift[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float M = __uint_as_float(absmax[bh * kD + 8 * cg + j]);
     int E = 0;
     if (M != 0.0f) frexpf(M, &E);
-    unit_inv[j] = M != 0.0f ? ldexp(1.0, 30 - E) : 0.0;  // an all-zero channel sums to 0
+    shift[j] = 30 - E;  // an all-zero channel scales zeros: it sums to 0
   }
   const int r_begin = blockIdx.x * rows_per_block;
   const int r_end = min(N, r_begin + rows_per_block);
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__
     for (int k = 0; k < 4; ++k) {
       if (r + 16 * k < r_end) {  // every row counted exactly once
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += (long long)__builtin_rint((double)v[k][j] * unit_inv[j]);
+        for (int j = 0; j < 8; ++j) acc[j] += fixed_point_term(v[k][j], shift[j]);
       }
     }
   }
@@ -176,11 +184,10 @@ __global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, i
     const float M = cmax[8 * cg + j];
     int E = 0;
     if (M != 0.0f) frexpf(M, &E);
-    const double unit_inv = M != 0.0f ? ldexp(1.0, 30 - E) : 0.0;
     acc[j] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (rl + 16 * i < n) acc[j] += (long long)__builtin_rint((double)v[i][j] * unit_inv);
+      if (rl + 16 * i < n) acc[j] += fixed_point_term(v[i][j], 30 - E);
     ired[rl][8 * cg + j] = acc[j];
   }
   __syncthreads();
