@@ -303,7 +303,8 @@ def write_traffic(run_dir, args):
     # dispatches of one call relative to its main kernel: prefill = fill, Q amax
     # pre-pass and its fold, K expansion, attention; decode = the one-workgroup
     # Q amax, split, combine
-    # prefill_tile = tile means, fill, Q amax and its fold, K expansion, attention
+    # prefill_tile = fill, tile means with the tile-centred Q amax, its fold, K
+    # expansion, attention
     calls = [("prefill", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
               f"mpfa_prefill {args.workload}"),
              ("decode", "decode", "k_decode_split<true, false>", (-1, 0, 1),
@@ -312,7 +313,7 @@ def write_traffic(run_dir, args):
         calls.append(("prefill_long", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
                       f"mpfa_prefill {args.long_workload}"))
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_tile_FETCH_SIZE")):
-        calls.append(("prefill_tile", "prefill", "k_prefill<2>", (-5, -4, -3, -2, -1, 0),
+        calls.append(("prefill_tile", "prefill", "k_prefill<2>", (-4, -3, -2, -1, 0),
                       f"mpfa_prefill_tile_mean {args.workload}"))
     for op, kind, main_kernel, offsets, name in calls:
         fv, fn = load(op, "FETCH_SIZE")

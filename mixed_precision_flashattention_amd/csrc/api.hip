@@ -327,9 +327,8 @@ int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, i
   const int qb = q_dtype == MPFA_BF16;
   uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
   uint8_t* k_img = (uint8_t*)ws + L.k_f16;
-  launch_tile_mean(q, qb, B * Hq, N, q_tile_mean, s);
   launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-  launch_centered_amax(q, qb, B * Hq, N, q_tile_mean, amax, s, /*tile_means=*/true);
+  launch_tile_mean(q, qb, B * Hq, N, q_tile_mean, amax, s);
   launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_img, s, /*bf16=*/true);
   PrefillParams p;
   p.q = q;

@@ -66,13 +66,16 @@ void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
                          unsigned long long* sums, float* mean, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
-                          uint32_t* out, hipStream_t st, bool tile_means = false);
+                          uint32_t* out, hipStream_t st);
 // Partial maxima of |x - mean| over the rows of a [rows, 128] tensor, one
 // per slot (kRowsAmaxSlots floats, all written): the decode query amax.
 constexpr int kRowsAmaxSlots = 64;
 void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, float* slots,
                       hipStream_t st);
-void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st);
+// Per-tile channel means; with amax non-NULL (cleared beforehand) also the
+// amax of the tile-centred tensor into amax[0], as launch_centered_amax does.
+void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, uint32_t* amax,
+                      hipStream_t st);
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
                              hipStream_t st);

@@ -147,11 +147,18 @@ __global__ void k_mean_finalize(const uint32_t* __restrict__ absmax,
 // division by the tile's row count).  One block per (tile, bh); thread
 // (rl, cg) holds rows rl, rl + 16, ... of the tile for channels 8 cg .. +7,
 // so both passes read the rows once.  mean: [BH, ceil(N/128), 128].
+// With amax non-NULL the block also takes max |fp32(x - tile mean)| over its
+// rows (the rows are still in registers) and adds it to the slotted amax of
+// the tile-centred tensor (out[slot * kAmaxSlotWords], cleared beforehand,
+// folded afterwards), so no second pass over x is needed for it.
 __global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, int is_bf16, int N,
-                                                   float* __restrict__ mean) {
+                                                   float* __restrict__ mean,
+                                                   uint32_t* __restrict__ amax) {
   __shared__ float fred[16][kD];
   __shared__ long long ired[16][kD];
   __shared__ float cmax[kD];
+  __shared__ float cmean[kD];
+  __shared__ float ared[4];
   const int64_t bh = blockIdx.y;
   const int t = blockIdx.x;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
@@ -203,6 +210,25 @@ __global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, i
       out = (float)(((double)S / (double)n) * ldexp(1.0, E - 30));
     }
     mean[(bh * gridDim.x + t) * kD + threadIdx.x] = out;
+    cmean[threadIdx.x] = out;
+  }
+  if (!amax) return;  // uniform across the block
+  __syncthreads();
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float mu = cmean[8 * cg + j];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i][j] - mu));  // a repeated row adds nothing
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((threadIdx.x & 63) == 0) ared[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int slot = (blockIdx.x + blockIdx.y * gridDim.x) % kAmaxSlots;
+    atomic_max_nonneg(amax + slot * kAmaxSlotWords,
+                      fmaxf(fmaxf(ared[0], ared[1]), fmaxf(ared[2], ared[3])));
   }
 }
 
@@ -210,31 +236,20 @@ __global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, i
 // NULL).  Same grid and thread layout as the channel statistics; each thread
 // keeps one running max, the block reduces it (wave shuffles, then LDS) and
 // issues a single atomic.
-// With tile_means set, mean holds one row of channel means per 128-row tile,
-// [BH, ceil(N/128), 128], and row r is centred by the mean of tile r / 128.
 __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ x, int is_bf16,
                                                        int N, int rows_per_block,
                                                        const float* __restrict__ mean,
-                                                       int tile_means,
                                                        uint32_t* __restrict__ out) {
   __shared__ float red[4];
   const int64_t bh = blockIdx.y;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
   float mu[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) mu[j] = (mean && !tile_means) ? mean[bh * kD + 8 * cg + j] : 0.0f;
+  for (int j = 0; j < 8; ++j) mu[j] = mean ? mean[bh * kD + 8 * cg + j] : 0.0f;
   const int r_begin = blockIdx.x * rows_per_block;
   const int r_end = min(N, r_begin + rows_per_block);
-  const int64_t n_tiles = (N + kBlk - 1) / kBlk;
   float m = 0.0f;
   for (int r = r_begin + rl; r < r_end; r += 128) {
-    if (tile_means) {
-      // r_begin is a multiple of 128, so the rows r - rl .. r - rl + 127 this
-      // step reads (including the clamped repeat of the last row) share a tile
-      const float* mt = mean + (bh * n_tiles + ((r - rl) >> 7)) * kD + 8 * cg;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mu[j] = mt[j];
-    }
     float v[8][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)  // a repeated row does not change the max
@@ -542,11 +557,10 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
 }
 
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
-                          uint32_t* out, hipStream_t st, bool tile_means) {
+                          uint32_t* out, hipStream_t st) {
   const int rows = stat_rows_per_block(BH, N, 128);
   dim3 grid((unsigned)((N + rows - 1) / rows), BH);
-  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean,
-                     (int)tile_means, out);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out);
   hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, out);
 }
 
@@ -556,9 +570,11 @@ void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, f
                      slots);
 }
 
-void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, hipStream_t st) {
+void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, uint32_t* amax,
+                      hipStream_t st) {
   dim3 grid((unsigned)((N + kBlk - 1) / kBlk), BH);
-  hipLaunchKernelGGL(k_tile_mean, grid, dim3(256), 0, st, x, is_bf16, N, mean);
+  hipLaunchKernelGGL(k_tile_mean, grid, dim3(256), 0, st, x, is_bf16, N, mean, amax);
+  if (amax) hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, amax);
 }
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
