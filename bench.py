@@ -117,6 +117,49 @@ def time_calls(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
+def median_call_ms(fn, n=20):
+    """Median of n single calls, each bracketed by its own HIP events on the
+    current stream (after one untimed call)."""
+    import torch
+    fn()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(st)
+        fn()
+        e1.record(st)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def host_env():
+    """Shader clock levels as the driver lists them (the active one marked),
+    the host CPU model and its logical core count."""
+    import glob
+    import platform
+    env = {"cpu_model": platform.processor() or None, "cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    env["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                levels = [ln.strip() for ln in f if ln.strip()]
+        except OSError:
+            continue
+        if levels:
+            env["sclk_levels"] = levels
+            break
+    return env
+
+
 def cpu_baseline(cfg, target_s=12.0):
     """The oracle's blocked attention on sampled rows of one (batch, query
     head) of the workload, operands quantized and dequantized by the oracle
@@ -472,6 +515,7 @@ def main():
     # ---- the dominant kernel, alone --------------------------------------
     stage1()
     ms_prefill = time_calls(prefill_call, args.steps, 2)
+    ms_prefill_median = median_call_ms(prefill_call)
     ms_stage1 = time_calls(stage1, args.steps, 1)
     achieved = flops / (ms_prefill * 1e-3) / 1e12
     log(f"[bench] prefill call {ms_prefill:.3f} ms -> {achieved:.1f} TFLOP/s; stage one {ms_stage1:.3f} ms")
@@ -516,8 +560,10 @@ def main():
                      "achieved": round(achieved, 2), "peak": round(PEAK_MIXED / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MIXED, 4),
                      "traffic": measured_traffic("mpfa_prefill llama8b_prefill_16k"),
-                     "flops_per_launch": flops, "ms_per_launch": round(ms_prefill, 4)},
-        "prefill_ms": round(ms_prefill, 4), "prefill_direct_ms": round(ms_direct, 4),
+                     "flops_per_launch": flops, "ms_per_launch": round(ms_prefill, 4),
+                     "frac_of_fp16_fp8_instruction_peak": round(achieved * 1e12 / PEAK_F16_FP8, 4)},
+        "prefill_ms": round(ms_prefill, 4), "prefill_median_ms": round(ms_prefill_median, 4),
+        "prefill_direct_ms": round(ms_direct, 4),
         "prefill_tile_mean": {"ms": round(ms_tile, 4),
                               "roofline": {"bound": "mfma", "achieved": round(ach_tile, 2),
                                            "peak": round(PEAK_MIXED / 1e12, 1), "unit": "TFLOP/s",
@@ -528,7 +574,7 @@ def main():
         "compensation_overhead": round(ms_prefill / ms_direct - 1.0, 4),
         "env": {"gpu": torch.cuda.get_device_name(0),
                 "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
-                "hip": torch.version.hip, "torch": torch.__version__},
+                "hip": torch.version.hip, "torch": torch.__version__, **host_env()},
     }
     del q, k, v, x, kq, vq, out
     torch.cuda.empty_cache()
@@ -565,6 +611,7 @@ def main():
                              dout, None, dws)
 
         ms_dec = time_calls(decode_call, max(args.steps, 10), 3)
+        ms_dec_median = median_call_ms(decode_call)
         ms_dec_direct = time_calls(lambda: decode_call(False), max(args.steps, 10), 3)
         nbytes = decode_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.N)
         gbs = nbytes / (ms_dec * 1e-3) / 1e9
@@ -578,7 +625,11 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM / 1e9,
                          "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4),
                          "traffic": measured_traffic("mpfa_decode llama8b_decode_128k")},
-            "direct_ms": round(ms_dec_direct, 4), "direct_GBps": round(gbs_d, 1)}
+            "median_ms": round(ms_dec_median, 4),
+            "direct_ms": round(ms_dec_direct, 4), "direct_GBps": round(gbs_d, 1),
+            # attention FLOPs (4 * 128 per (query head, key)), for context only
+            "flops_per_call": 4.0 * D * dcfg.N * dcfg.B * dcfg.Hq,
+            "TFLOPs": round(4.0 * D * dcfg.N * dcfg.B * dcfg.Hq / (ms_dec * 1e-3) / 1e12, 2)}
         # decode-time cache write of one new token per request (centring against
         # the frozen means, NVFP4 K / FP8 V with the frozen scales, Delta_S)
         kn = torch.randn((dcfg.B, dcfg.Hkv, 1, D), device=dev).to(torch.bfloat16)

@@ -39,13 +39,15 @@ __device__ __forceinline__ float query_amax(const float* slots) {
 
 // Everything one 128-key block needs from HBM, per lane: the K codes of its
 // key in each of the 4 score tiles (32 bytes = its head-dim half), their 4
-// E4M3 scales, the group's Delta_S entries of those keys, and 8 x 32 bytes
-// of V^T operands.  Two of these are live: block j+1 is loaded while block
-// j is computed.
+// E4M3 scales, 8 x 32 bytes of V^T operands, and a share of the group's
+// Delta_S rows: keys 8 (lane % 16) .. + 7 of rows lane / 16 and 4 + lane / 16
+// (whole 16-byte pieces of the rows; LDS hands each lane the entries of its
+// own keys).  Two of these are live: block j+1 is loaded while block j is
+// computed.
 struct DecodeBlockRegs {
   uint4 k[4][2];
   uint32_t sc[4];
-  uint32_t dl[4][8];
+  uint4 dl[2];
   i32x8 v[8];
 };
 
@@ -67,6 +69,7 @@ struct DecodeCtx {
   const uint8_t* vbase;
   const uint16_t* dbase;  // Delta_S row of the group's first query head
   int N, G, ntiles32;
+  bool dvec;  // Delta_S rows start 16-byte aligned (contiguous cache: N % 8 == 0)
   // paged cache: this request's block-table row, the pool size and strides
   const int32_t* table;
   int num_pages, Hkv, hk, Hq;
@@ -122,10 +125,30 @@ __device__ __forceinline__ void decode_load(DecodeBlockRegs& r, const DecodeCtx&
     r.k[t][0] = make_uint4(k0v[0], k0v[1], k0v[2], k0v[3]);
     r.k[t][1] = make_uint4(k1v[0], k1v[1], k1v[2], k1v[3]);
     r.sc[t] = ld_stream<uint32_t>(bp.s + (int64_t)key * 8 + 4 * h);
-    if (SMOOTH) {
+  }
+  if (SMOOTH) {
+    // A whole 16-byte piece when the block is full and the rows are aligned
+    // (always in a page); otherwise entry by entry, keys clamped to the end.
+    const bool vec = PAGED || (c.dvec && bp.klast >= kBlk - 1);
+    const int j8 = 8 * (lane & 15);
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        r.dl[t][g] = g < c.G ? ld_stream<uint16_t>(bp.d + (int64_t)g * bp.dstride + key) : 0u;
+    for (int i = 0; i < 2; ++i) {
+      const int g = 4 * i + (lane >> 4);
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if ((i == 0 || c.G > 4) && g < c.G) {
+        const uint16_t* row = bp.d + (int64_t)g * bp.dstride;
+        if (vec) {
+          const i32x4 x = ld_stream<i32x4>(row + j8);
+          w = make_uint4(x[0], x[1], x[2], x[3]);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = ld_stream<uint16_t>(row + min(j8 + u, bp.klast));
+          w = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                         e[6] | (e[7] << 16));
+        }
+      }
+      r.dl[i] = w;
     }
   }
   const int n = lane & 15, kg = lane >> 4;
@@ -142,8 +165,16 @@ struct DecodeState {
 template <bool SMOOTH>
 __device__ __forceinline__ void decode_compute(const DecodeBlockRegs& r, DecodeState& st, int k0,
                                                int p1, int lane, float lam, const i32x4* qa,
-                                               const i32x4& dA, uint8_t* sp, float* salpha) {
+                                               const i32x4& dA, uint8_t* sp, float* salpha,
+                                               uint16_t* sdl, int G) {
   const int h = lane >> 5, col = lane & 31;
+  if (SMOOTH) {
+    // the group's Delta_S rows of this block into LDS, [row][key] (rows past
+    // the group hold zeros from the kernel's start)
+    *reinterpret_cast<uint4*>(sdl + (lane >> 4) * kBlk + 8 * (lane & 15)) = r.dl[0];
+    if (G > 4) *reinterpret_cast<uint4*>(sdl + (4 + (lane >> 4)) * kBlk + 8 * (lane & 15)) = r.dl[1];
+    __syncthreads();
+  }
   // ---- scores S = Q~ K~^T: 4 tiles of 32 keys, lane col = key ------------
   f32x16 s[4];
 #pragma unroll
@@ -154,8 +185,12 @@ __device__ __forceinline__ void decode_compute(const DecodeBlockRegs& r, DecodeS
     expand_fp4x8(w[0], e4m3_scale_f16x2(r.sc[t] & 0xFFu), e);
     const i32x4 kb0 = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
     if (SMOOTH) {
-      const i32x4 dB = {(int)(r.dl[t][0] | (r.dl[t][1] << 16)), (int)(r.dl[t][2] | (r.dl[t][3] << 16)),
-                        (int)(r.dl[t][4] | (r.dl[t][5] << 16)), (int)(r.dl[t][6] | (r.dl[t][7] << 16))};
+      // Delta_S[g][key] in slot g: the B operand of the rank-one step
+      uint32_t dg[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) dg[g] = sdl[g * kBlk + 32 * t + col];
+      const i32x4 dB = {(int)(dg[0] | (dg[1] << 16)), (int)(dg[2] | (dg[3] << 16)),
+                        (int)(dg[4] | (dg[5] << 16)), (int)(dg[6] | (dg[7] << 16))};
       s[t] = mfma32_bf16(dA, dB, f32x16{});
       s[t] = mfma32_f16(qa[0], kb0, s[t]);
     } else {
@@ -236,6 +271,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   __shared__ __align__(16) uint8_t sq[8 * kQStride];
   __shared__ __align__(16) uint8_t sp[8 * kPStride];
   __shared__ float salpha[8];
+  __shared__ __align__(16) uint16_t sdl[8 * kBlk];  // Delta_S rows of the block (smoothing)
 
   const int N = p.N, G = p.G, P = p.P;
   const int part = blockIdx.x % P;
@@ -317,6 +353,11 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   c.N = N;
   c.G = G;
   c.ntiles32 = (N + 31) / 32;
+  c.dvec = (N & 7) == 0;
+  if (SMOOTH) {  // rows past the group stay zero for the whole loop
+    for (int i = lane; i < 8 * kBlk; i += 64) sdl[i] = 0;
+    __syncthreads();
+  }
   if (PAGED) {
     c.kbase = p.k_fp4;
     c.sbase = p.k_sf;
@@ -351,10 +392,10 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeParams p) {
   decode_load<SMOOTH, PAGED>(ra, c, p0, lane);
   for (int k0 = p0; k0 < p1; k0 += 2 * kBlk) {
     if (k0 + kBlk < p1) decode_load<SMOOTH, PAGED>(rb, c, k0 + kBlk, lane);
-    decode_compute<SMOOTH>(ra, st, k0, p1, lane, lam, qa, dA, sp, salpha);
+    decode_compute<SMOOTH>(ra, st, k0, p1, lane, lam, qa, dA, sp, salpha, sdl, G);
     if (k0 + kBlk >= p1) break;
     if (k0 + 2 * kBlk < p1) decode_load<SMOOTH, PAGED>(ra, c, k0 + 2 * kBlk, lane);
-    decode_compute<SMOOTH>(rb, st, k0 + kBlk, p1, lane, lam, qa, dA, sp, salpha);
+    decode_compute<SMOOTH>(rb, st, k0 + kBlk, p1, lane, lam, qa, dA, sp, salpha, sdl, G);
   }
 
   // ---- partition state -------------------------------------------------
