@@ -343,17 +343,17 @@ def write_traffic(run_dir, args):
                       "(op prefill_long: --only prefill --workload qwen14b_prefill_32k); "
                       "then python bench.py --write-traffic DIR",
            "calls": {}}
-    # dispatches of one call relative to its main kernel: prefill = fill, Q amax
-    # pre-pass and its fold, K expansion, attention; decode = the one-workgroup
-    # Q amax, split, combine
+    # dispatches of one call relative to its main kernel: prefill = the Q amax
+    # pass (per-workgroup maxima), K expansion (which folds them), attention;
+    # decode = the query amax, split, combine
     # prefill_tile = fill, tile means with the tile-centred Q amax, its fold, K
     # expansion, attention
-    calls = [("prefill", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
+    calls = [("prefill", "prefill", "k_prefill<1>", (-2, -1, 0),
               f"mpfa_prefill {args.workload}"),
              ("decode", "decode", "k_decode_split<true, false>", (-1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_long_FETCH_SIZE")):
-        calls.append(("prefill_long", "prefill", "k_prefill<1>", (-4, -3, -2, -1, 0),
+        calls.append(("prefill_long", "prefill", "k_prefill<1>", (-2, -1, 0),
                       f"mpfa_prefill {args.long_workload}"))
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_tile_FETCH_SIZE")):
         calls.append(("prefill_tile", "prefill", "k_prefill<2>", (-4, -3, -2, -1, 0),

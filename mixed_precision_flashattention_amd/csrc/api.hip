@@ -271,9 +271,17 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
   uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
-  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-  launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, delta_s ? q_mean : nullptr, amax, s);
-  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_f16, s);
+  // Q_c amax as per-workgroup maxima, folded by the K expansion that follows
+  // (more heads than partial slots: cleared slots, atomics and a fold)
+  const float* qm = delta_s ? q_mean : nullptr;
+  const int n_part = launch_centered_amax_partials(q, q_dtype == MPFA_BF16, B * Hq, N, qm,
+                                                   (float*)amax, s);
+  if (n_part < 0) {
+    launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
+    launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, qm, amax, s);
+  }
+  launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_f16, s, /*bf16=*/false,
+                  n_part > 0 ? (const float*)amax : nullptr, n_part, amax);
   PrefillParams p;
   p.q = q;
   p.q_bf16 = q_dtype == MPFA_BF16;

@@ -67,6 +67,12 @@ void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* ab
                          unsigned long long* sums, float* mean, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
                           uint32_t* out, hipStream_t st);
+// The same amax as per-workgroup maxima in partials[0 .. n) (no clearing, no
+// fold launch; the consumer folds them): returns n <= kAmaxPartials, or -1
+// (nothing launched) when the tensor has more than kAmaxPartials heads.
+constexpr int kAmaxPartials = (int)(kAmaxBytes / 4);
+int launch_centered_amax_partials(const void* x, int is_bf16, int BH, int N, const float* mean,
+                                  float* partials, hipStream_t st);
 // Partial maxima of |x - mean| over the rows of a [rows, 128] tensor, one
 // per slot (kRowsAmaxSlots floats, all written): the decode query amax.
 constexpr int kRowsAmaxSlots = 64;
@@ -96,8 +102,12 @@ void launch_append_kv_paged(const void* k_new, const void* v_new, int is_bf16, i
                             uint8_t* k_sf, uint8_t* v_fp8, uint16_t* delta, hipStream_t st);
 
 // prefill.hip
+// partials non-NULL: also fold n_partials maxima of launch_centered_amax_partials
+// into amax_out[0] (amax_out may alias partials).
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
-                     uint8_t* k_img, hipStream_t st, bool bf16 = false);
+                     uint8_t* k_img, hipStream_t st, bool bf16 = false,
+                     const float* partials = nullptr, int n_partials = 0,
+                     uint32_t* amax_out = nullptr);
 void launch_prefill(const PrefillParams& p, hipStream_t st);
 
 // decode.hip

@@ -519,10 +519,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 // the whole key in that slot: it reads the key's 64 code bytes and 8 scale
 // bytes in one piece and writes its 16 chunks, so consecutive threads read
 // consecutive rows and write consecutive 16-byte slots of each chunk column.
+// With partials non-NULL, block 0 first folds the n_partials per-workgroup
+// maxima of the query amax pass into amax_out[0] (the word the attention
+// kernel reads), so that pass needs neither a cleared buffer nor a fold
+// launch of its own.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ codes,
                                                   const uint2* __restrict__ sf, int N, int nkb,
-                                                  int64_t n_threads, uint4* __restrict__ out) {
+                                                  int64_t n_threads, uint4* __restrict__ out,
+                                                  const float* __restrict__ partials,
+                                                  int n_partials, uint32_t* __restrict__ amax_out) {
+  if (partials && blockIdx.x == 0) {  // uniform across the block
+    __shared__ float red[4];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n_partials; i += 256) m = fmaxf(m, partials[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();  // also orders every read of partials before the store below
+    if (threadIdx.x == 0) amax_out[0] = __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  }
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= n_threads) return;
   const int slot = (int)(g & (kBlk - 1));
@@ -563,7 +579,8 @@ __global__ __launch_bounds__(256) void k_expand_k(const uint4* __restrict__ code
 }
 
 void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int N,
-                     uint8_t* k_img, hipStream_t st, bool bf16) {
+                     uint8_t* k_img, hipStream_t st, bool bf16, const float* partials,
+                     int n_partials, uint32_t* amax_out) {
   const int nkb = (N + kBlk - 1) / kBlk;
   const int64_t n_threads = bhk * nkb * kBlk;
   const dim3 grid((unsigned)((n_threads + 255) / 256));
@@ -571,9 +588,11 @@ void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int
   const auto* sf = reinterpret_cast<const uint2*>(k_sf);
   auto* out = reinterpret_cast<uint4*>(k_img);
   if (bf16)
-    hipLaunchKernelGGL(k_expand_k<true>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out);
+    hipLaunchKernelGGL(k_expand_k<true>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out,
+                       partials, n_partials, amax_out);
   else
-    hipLaunchKernelGGL(k_expand_k<false>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out);
+    hipLaunchKernelGGL(k_expand_k<false>, grid, dim3(256), 0, st, codes, sf, N, nkb, n_threads, out,
+                       partials, n_partials, amax_out);
 }
 
 void launch_prefill(const PrefillParams& p, hipStream_t st) {

@@ -235,11 +235,14 @@ __global__ __launch_bounds__(256) void k_tile_mean(const void* __restrict__ x, i
 // max |fp32(x - mean[bh, d])| over a whole [BH, N, 128] tensor (mean may be
 // NULL).  Same grid and thread layout as the channel statistics; each thread
 // keeps one running max, the block reduces it (wave shuffles, then LDS) and
-// issues a single atomic.
+// issues a single atomic.  With partials non-NULL the block instead stores
+// its maximum in partials[block] (no atomic, nothing to clear beforehand);
+// a later kernel folds them.
 __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ x, int is_bf16,
                                                        int N, int rows_per_block,
                                                        const float* __restrict__ mean,
-                                                       uint32_t* __restrict__ out) {
+                                                       uint32_t* __restrict__ out,
+                                                       float* __restrict__ partials) {
   __shared__ float red[4];
   const int64_t bh = blockIdx.y;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
@@ -264,9 +267,13 @@ __global__ __launch_bounds__(256) void k_centered_amax(const void* __restrict__ 
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int slot = (blockIdx.x + blockIdx.y * gridDim.x) % kAmaxSlots;
-    atomic_max_nonneg(out + slot * kAmaxSlotWords,
-                      fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (partials) {
+      partials[blockIdx.x + blockIdx.y * gridDim.x] = bm;
+    } else {
+      const int slot = (blockIdx.x + blockIdx.y * gridDim.x) % kAmaxSlots;
+      atomic_max_nonneg(out + slot * kAmaxSlotWords, bm);
+    }
   }
 }
 
@@ -560,8 +567,22 @@ void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float
                           uint32_t* out, hipStream_t st) {
   const int rows = stat_rows_per_block(BH, N, 128);
   dim3 grid((unsigned)((N + rows - 1) / rows), BH);
-  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean, out,
+                     (float*)nullptr);
   hipLaunchKernelGGL(k_amax_fold, dim3(1), dim3(kAmaxSlots), 0, st, out);
+}
+
+int launch_centered_amax_partials(const void* x, int is_bf16, int BH, int N, const float* mean,
+                                  float* partials, hipStream_t st) {
+  if (BH > kAmaxPartials) return -1;
+  // at most kAmaxPartials / BH blocks per head, whole multiples of 128 rows
+  const int per_bh = kAmaxPartials / BH;
+  int rows = (N + per_bh - 1) / per_bh;
+  rows = (rows + 127) / 128 * 128;
+  dim3 grid((unsigned)((N + rows - 1) / rows), BH);
+  hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean,
+                     (uint32_t*)nullptr, partials);
+  return (int)(grid.x * grid.y);
 }
 
 void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, float* slots,
