@@ -393,32 +393,53 @@ __global__ __launch_bounds__(512) void k_delta_s(const void* __restrict__ k, int
 }
 
 // FP8 E4M3 V in 32-token tiles, head-dim major inside a tile.  Block: 128
-// threads (one per channel) x one tile; positions past N are written as 0.
-__global__ void k_quantize_v(const void* __restrict__ v, int is_bf16, int N, int n_tiles,
-                             const uint32_t* __restrict__ amax, float* __restrict__ vscale_out,
-                             uint8_t* __restrict__ out) {
+// threads x one tile; positions past N are written as 0.  Thread (tr, cg)
+// reads channels 8 cg .. 8 cg + 7 of tokens 4 tr .. 4 tr + 3 of the tile
+// (16-byte loads of bf16), encodes them and keeps one word per channel (its
+// four tokens' codes); LDS turns the tile around so that thread d then
+// writes channel d's 32 codes in two 16-byte stores.  Channel c's 32-byte
+// LDS row sits in slot 8 (c / 8) + (c + c / 8) % 8, which spreads the word
+// writes of one instruction over the banks.
+__device__ __forceinline__ int v_tile_slot(int c) { return 8 * (c >> 3) + ((c + (c >> 3)) & 7); }
+__global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, int is_bf16, int N,
+                                                    int n_tiles, const uint32_t* __restrict__ amax,
+                                                    float* __restrict__ vscale_out,
+                                                    uint8_t* __restrict__ out) {
+  __shared__ __align__(16) uint32_t rows[kD * 8];  // [slot of channel][token / 4]
   const float A = __uint_as_float(*amax);
   const float s = A > 0.0f ? A / kE4M3Max : 1.0f;
-  const int d = threadIdx.x;
   const int tile = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  if (tile == 0 && bh == 0 && d == 0) *vscale_out = s;
-  uint32_t w[8];
+  if (tile == 0 && bh == 0 && threadIdx.x == 0) *vscale_out = s;
+  const int cg = threadIdx.x & 15, tr = threadIdx.x >> 4;
+  float x[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tile * 32 + 4 * tr + i;
+    if (t < N) {
+      load8(v, (bh * N + t) * kD + 8 * cg, is_bf16, x[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t word = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int t = tile * 32 + j * 4 + b;
-      uint32_t c = 0;
-      if (t < N) c = e4m3_encode(load_elem(v, (bh * N + t) * kD + d, is_bf16) / s);
-      word |= c << (8 * b);
+    for (int i = 0; i < 4; ++i) {
+      const int t = tile * 32 + 4 * tr + i;
+      const uint32_t c = t < N ? e4m3_encode(x[i][j] / s) : 0u;
+      word |= c << (8 * i);
     }
-    w[j] = word;
+    rows[v_tile_slot(8 * cg + j) * 8 + tr] = word;
   }
+  __syncthreads();
+  const int d = threadIdx.x;
+  const uint4* src = reinterpret_cast<const uint4*>(rows + v_tile_slot(d) * 8);
   uint4* dst = reinterpret_cast<uint4*>(out + ((bh * n_tiles + tile) * kD + d) * 32);
-  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  dst[0] = src[0];
+  dst[1] = src[1];
 }
 
 // Decode-time cache write (paper section 6 "Online quantization": the new
