@@ -160,6 +160,29 @@ def host_env():
     return env
 
 
+def measured_peaks():
+    """The device's measured ceilings from the standalone probe built beside
+    the library (mixed_precision_flashattention_amd/mpfa_peaks): MFMA rates of
+    the instructions the kernels use and HBM streaming-read bandwidth.  Run as
+    a child process before this process touches the GPU.  None if the probe
+    is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "mixed_precision_flashattention_amd", "mpfa_peaks")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    if r.returncode != 0:
+        log(f"[bench] peak probe failed ({r.returncode}): {r.stderr.strip()[-200:]}")
+        return None
+    try:
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except (ValueError, IndexError):
+        return None
+
+
 def cpu_baseline(cfg, target_s=12.0):
     """The oracle's blocked attention on sampled rows of one (batch, query
     head) of the workload, operands quantized and dequantized by the oracle
@@ -437,6 +460,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the probe of the measured MFMA and HBM ceilings")
     ap.add_argument("--only", choices=["prefill", "prefill_tile", "decode", "copy"], default=None,
                     help="counter-collection mode: set up, run 3 calls of one operation, exit")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -450,6 +475,13 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    peaks = None
+    if not args.only and not args.no_peaks:
+        peaks = measured_peaks()  # a child process, before this one touches the GPU
+        if peaks:
+            log(f"[bench] measured ceilings: MFMA {peaks.get('mfma_tflops')} TFLOP/s, "
+                f"read {peaks.get('read_GBps')} GB/s")
 
     import torch
     import mixed_precision_flashattention_amd as mpfa
@@ -575,6 +607,9 @@ def main():
         "env": {"gpu": torch.cuda.get_device_name(0),
                 "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
                 "hip": torch.version.hip, "torch": torch.__version__, **host_env()},
+        # measured on this device by the peak probe (context for the published
+        # peaks the roofline fractions use)
+        "measured_peaks": peaks,
     }
     del q, k, v, x, kq, vq, out
     torch.cuda.empty_cache()

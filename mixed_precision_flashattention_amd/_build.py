@@ -29,14 +29,24 @@ def flags() -> list[str]:
     ]
 
 
+PEAKS = os.path.join(PKG, "mpfa_peaks")  # standalone probe of the device's ceilings (bench.py)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libmpfa.so (always recompiles)."""
+    """Compile every source into libmpfa.so, and the peak probe into
+    mpfa_peaks (always recompiles)."""
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *flags(), "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    probe = [hipcc(), *[f for f in flags() if f not in ("-fPIC", "-shared")], "-o", PEAKS + ".tmp",
+             os.path.join(CSRC, "peaks.hip")]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    subprocess.check_call(probe)
+    os.replace(PEAKS + ".tmp", PEAKS)
     return LIB
 
 
