@@ -122,7 +122,9 @@ int main() {
   const int cus = prop.multiProcessorCount;
   printf("{\"device\": \"%s\", \"compute_units\": %d", prop.gcnArchName, cus);
 
-  // ---- MFMA issue rates: 8 waves per CU (two per SIMD), 4 rounds of the grid
+  // ---- MFMA issue rates: 32 waves per CU in 256-thread blocks; one wave per
+  // SIMD is resident at a time (eight 16-register accumulators plus operands),
+  // so the grid runs in eight rounds
   const int blocks = cus * 2 * 4;  // 256-thread blocks = 4 waves each
   float* out = nullptr;
   CHECK(hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)));
