@@ -138,6 +138,16 @@ def test_prefill_gqa2_xcd_mapping_bf16_out(mpfa, oracle_mod):
                    out_bf16=True)
 
 
+@pytest.mark.parametrize("B", [64, 66])
+def test_prefill_query_amax_at_and_past_2048_heads(mpfa, oracle_mod, B):
+    """The prefill call's Q_c amax pass leaves one maximum per workgroup (at
+    most 2048, folded by the K expansion); B * Hq = 2048 query heads is the
+    largest case it covers (one workgroup per head) and 2112 takes the
+    slotted-atomic pass instead.  Short ragged sequences."""
+    from mixed_precision_flashattention_amd import synth
+    _check_prefill(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=B, Hq=32, Hkv=8, N=20))
+
+
 @pytest.mark.parametrize("smooth", [True, False])
 def test_decode_mha(mpfa, oracle_mod, smooth):
     """Hq = Hkv: one real row per score tile."""
