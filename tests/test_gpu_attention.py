@@ -163,6 +163,17 @@ def test_decode_gqa8(mpfa, oracle_mod):
                   synth.config("llama8b_decode_128k", B=1, Hq=16, Hkv=2, N=777, num_splits=2))
 
 
+@pytest.mark.parametrize("Hq,N,splits", [(10, 2048, 4), (12, 1000, 3), (16, 1024, 2)])
+def test_decode_groups_past_four_whole_delta_rows(mpfa, oracle_mod, Hq, N, splits):
+    """Smoothing with GQA groups of 5, 6 and 8 and N a multiple of 8: the
+    group's Delta_S rows of every full block are read as 16-byte pieces, two
+    per lane when the group has more than four rows (1000 = 7 x 128 + 104
+    also ends in a partial block, read entry by entry)."""
+    from mixed_precision_flashattention_amd import synth
+    _check_decode(mpfa, oracle_mod,
+                  synth.config("llama8b_decode_128k", B=2, Hq=Hq, Hkv=2, N=N, num_splits=splits))
+
+
 # ---- degenerate inputs: a global amax or a centered tensor that is exactly 0 --
 def _zero_k(q, k, v):
     return q, np.zeros_like(k), v
