@@ -65,44 +65,60 @@ __device__ __forceinline__ void load16(const void* p, int64_t i, int is_bf16, fl
 // ---------------------------------------------------------------- codecs --
 // E2M1 code of x: nearest of the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6},
 // ties to the even code, saturating at 6, sign bit (bit 3) copied from x so
-// that -0 and negatives rounding to zero keep their sign.  The comparisons
-// against the midpoints encode the tie rule directly (">" where the lower
-// code is even, ">=" where the upper one is).
+// that -0 and negatives rounding to zero keep their sign.  Below 1 the code
+// is rint(2|x|) (0, 1 or 2 = the value 1.0; 0.25 and 0.75 go to the even
+// codes 0 and 2).  From 1 on, the magnitude codes are the fp32 pattern
+// rounded to one mantissa bit: with the mantissa rounded half to even at
+// bit 22, (bits >> 22) - 252 is 2 for 1.0, 3 for 1.5, ... 7 for 6.0 (and
+// above 7 for what saturates).  Rounding the fp32 mantissa to nearest even
+// is the tie rule of the code, because every E2M1 value from 1 on has a
+// one-bit mantissa.
 __device__ __forceinline__ uint32_t e2m1_encode(float x) {
   const float a = fabsf(x);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
+  const uint32_t small = (uint32_t)__builtin_rintf(a * 2.0f);
+  uint32_t u = __float_as_uint(a);
+  u += 0x1FFFFFu + ((u >> 22) & 1u);
+  const uint32_t big = min((u >> 22) - 252u, 7u);
+  const uint32_t c = a < 1.0f ? small : big;
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// Value of an E2M1 code (4 bits).
+// Value of an E2M1 code (4 bits).  The normal and the subnormal forms are
+// both computed and one is selected (no branch); the sign bit is copied, so
+// code 8 gives -0.
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const float v = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-  return (c & 8u) ? -v : v;
+  const float normal = __uint_as_float(((e + 126u) << 23) | (m << 22));
+  const float sub = 0.5f * (float)m;
+  const float v = e ? normal : sub;
+  return __uint_as_float(__float_as_uint(v) | ((c & 8u) << 28));
 }
 
 // E4M3 code of a magnitude a >= 0 (finite): round to nearest, ties to the
-// even code, saturate at 448 (code 0x7E); never the NaN code.
+// even code, saturate at 448 (code 0x7E); never the NaN code.  The normal
+// and the subnormal encodings are both computed and one is selected (no
+// branch); each is used only in its own range.
 __device__ __forceinline__ uint32_t e4m3_encode_mag(float a) {
-  if (a >= 448.0f) return 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9; rint rounds half to even
-    return (uint32_t)__builtin_rintf(a * 512.0f);  // 8 -> code 0x08 = 2^-6
-  }
   uint32_t u = __float_as_uint(a);
   u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits, half to even
-  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+  const uint32_t normal = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+  // below 2^-6: subnormal step 2^-9; rint rounds half to even (8 -> code 0x08 = 2^-6)
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t c = a < 0.015625f ? sub : normal;
+  return a >= 448.0f ? 0x7Eu : c;
 }
 
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return e4m3_encode_mag(fabsf(x)) | ((__float_as_uint(x) >> 24) & 0x80u);
 }
 
-// Value of a non-negative E4M3 code below 0x7F.
+// Value of a non-negative E4M3 code below 0x7F (both forms computed, one
+// selected).
 __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;
+  return e ? normal : sub;
 }
 
 // bf16 bits of a finite fp32, round to nearest even.
@@ -128,9 +144,15 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float* x, float g, uint32_
   const float s = e4m3_value_pos(sc);
   const float sg = s * g;
   const bool zero = (s == 0.0f) || (sg == 0.0f);
+  // a zero scale gives signed zero codes; the division still runs (by 1, its
+  // result unused) so that the block takes no branch per element
+  const float den = zero ? 1.0f : sg;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    codes[j] = zero ? ((__float_as_uint(x[j]) >> 28) & 8u) : e2m1_encode(x[j] / sg);
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t cz = (__float_as_uint(x[j]) >> 28) & 8u;
+    const uint32_t cq = e2m1_encode(x[j] / den);
+    codes[j] = zero ? cz : cq;
+  }
   return sc;
 }
 
