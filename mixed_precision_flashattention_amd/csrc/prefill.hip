@@ -49,10 +49,6 @@ constexpr int kRowBytes = 256;  // one Q~ row in LDS: 128 f16
 // conflict).
 constexpr int kKChunkBytes = kBlk * 16;
 constexpr int kKBlockBytes = kBlk * kRowBytes;
-// Q~ staging rows use chunk c ^ (row & 15): the operand read (16 rows, one
-// chunk column) and the quantizer's writes (8 rows x 8 chunk pairs) are both
-// spread over all 16 chunk slots.
-__device__ __forceinline__ int qswz(int r) { return r & 15; }
 // V in LDS: [4 tiles][2 halves][128 channels][16 bytes]: each lane's two
 // 16-byte reads are then contiguous across lanes (no bank conflicts).
 constexpr int kVTileBytes = kD * 32;
@@ -276,7 +272,7 @@ template <int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
   constexpr bool SMOOTH = MODE == 1, TILE = MODE == 2;
-  __shared__ __align__(16) uint8_t smem_k[2][kBlk * kRowBytes];  // K~ blocks (Q~ in the prologue)
+  __shared__ __align__(16) uint8_t smem_k[2][kBlk * kRowBytes];  // K~ blocks
   __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];      // V blocks
   __shared__ uint16_t smem_delta[2][kBlk];
 
@@ -298,12 +294,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;  // exp2 constant per unit of the MFMA score
 
-  // ---- prologue: NVFP4 of the 256 query rows, expanded to FP16 in LDS ----
-  uint8_t* qstage = smem_k[0];                             // 256 rows x 256 bytes
-  float* lse_part = reinterpret_cast<float*>(smem_v[0]);  // [256 rows][8 blocks]
-  for (int u = tid; u < kUnitRows * 8; u += 512) {
-    const int r = u >> 3, blk = u & 7;
-    const int qrow = row0 + r;
+  const int nblk_all = (N + kBlk - 1) / kBlk;
+  const int64_t kvh = (int64_t)b * p.Hkv + hk;
+  const uint8_t* kimg = p.k_f16 + kvh * nblk_all * kKBlockBytes;
+  const uint32_t lds_k0 = lds_addr(smem_k[0]), lds_k1 = lds_addr(smem_k[1]);
+  // The first K~ block goes out before the queries are quantized, so its
+  // load latency overlaps the prologue.
+  issue_k_block<8>(kimg, lds_k0, wave, lane);
+
+  // ---- prologue: NVFP4 of the queries, expanded to FP16 in registers -----
+  // Each lane holds, as the B operand of the score MFMA (Q~^T), query row
+  // 32*wave + col at head-dim slots 64*h + 8*kc .. +7 for step kc, i.e. the
+  // 16-element blocks 4h .. 4h+3 of its row: it quantizes exactly those (no
+  // LDS staging, no barrier).
+  const int qr = 32 * wave + col;
+  const int qrow = row0 + qr;
+  i32x4 qf[8];
+  float part_sum = 0.0f;  // this lane's half of Q_i . Kbar (the LSE row term)
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    const int blk = 4 * h + bi;
     uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float part = 0.0f;
     if (qrow < N) {
@@ -320,48 +330,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
           x[j] = x[j] - mu[j];
         }
       }
-      uint32_t c[16];
-      const uint32_t sc = nvfp4_block(x, gQ, c);
-      const float s = e4m3_value_pos(sc);
+      uint32_t w[2];
+      const uint32_t sc = nvfp4_block_packed(x, gQ, w);
       if (TILE) {
         // bf16(code value x block scale + fp32(Qbar_tile / gQ)), both sums
         // rounded to nearest (the product is exact in fp32)
+        const float s = e4m3_value_pos(sc);
         const float* mu = p.q_tile_mean + ((int64_t)bh * n_qtiles + (qrow >> 7)) * kD + blk * 16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float u0 = e2m1_value(c[2 * j]) * s + mu[2 * j] / gQ;
-          const float u1 = e2m1_value(c[2 * j + 1]) * s + mu[2 * j + 1] / gQ;
+          const uint32_t byte = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+          const float u0 = e2m1_value(byte & 15u) * s + mu[2 * j] / gQ;
+          const float u1 = e2m1_value(byte >> 4) * s + mu[2 * j + 1] / gQ;
           packed[j] = bf16_rne(u0) | (bf16_rne(u1) << 16);
         }
       } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const f16x2 v2 = {(_Float16)(e2m1_value(c[2 * j]) * s),
-                            (_Float16)(e2m1_value(c[2 * j + 1]) * s)};
-          packed[j] = __builtin_bit_cast(uint32_t, v2);
-        }
+        // code value x block scale in FP16 (exact) by the hardware conversion
+        const f16x2 s2 = e4m3_scale_f16x2(sc);
+        expand_fp4x8(w[0], s2, packed);
+        expand_fp4x8(w[1], s2, packed + 4);
       }
     }
-    uint4* dst = reinterpret_cast<uint4*>(qstage + r * kRowBytes);
-    dst[(2 * blk) ^ qswz(r)] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[(2 * blk + 1) ^ qswz(r)] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    lse_part[r * 8 + blk] = part;
+    qf[2 * bi] = i32x4{(int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]};
+    qf[2 * bi + 1] = i32x4{(int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]};
+    part_sum += part;
   }
-  __syncthreads();
-
-  // B operand of the score MFMA (Q~^T): query row 32*wave + col, head-dim
-  // slots 64*h + 8*kc .. +7 for step kc (the K~ reads use the same slots).
-  const int qr = 32 * wave + col;
-  i32x4 qf[8];
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = *reinterpret_cast<const i32x4*>(qstage + qr * kRowBytes + 16 * ((8 * h + kc) ^ qswz(qr)));
   float lse_off = 0.0f;
-  if ((SMOOTH || TILE) && p.lse) {
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) lse_off += lse_part[qr * 8 + blk];
-    lse_off *= p.scale;
-  }
+  if ((SMOOTH || TILE) && p.lse) lse_off = p.scale * sum_halves(part_sum);
   // Constant B operand of the rank-one step: slots 0..2 of lane half 0 hold
   // 1 / (gQ gK) as the sum of three bf16 parts (exact to fp32 precision);
   // the A operand repeats Delta_S[key] in the same slots.
@@ -377,7 +372,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   const int my_row = row0 + qr;
   const int grow0 = row0 + 128 * grp;  // first row of this wave's group
-  const int nblk_all = (N + kBlk - 1) / kBlk;
   // blocks per group (0 for a group past the end), and the loop length
   const int n_a = p.causal ? min(2 * unit + 1, nblk_all) : nblk_all;
   const int n_b = row0 + 128 < N ? (p.causal ? min(2 * unit + 2, nblk_all) : nblk_all) : 0;
@@ -385,11 +379,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int n_max = max(n_a, n_b);
   const int lim = p.causal ? min(my_row, N - 1) : N - 1;  // last visible key of this row
   const int ntiles32 = (N + 31) / 32;
-  const int64_t kvh = (int64_t)b * p.Hkv + hk;
-  const uint8_t* kimg = p.k_f16 + kvh * nblk_all * kKBlockBytes;
   const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * kVTileBytes;
   const uint16_t* dbase = SMOOTH ? p.delta_s + (int64_t)bh * N : nullptr;
-  const uint32_t lds_k0 = lds_addr(smem_k[0]), lds_k1 = lds_addr(smem_k[1]);
   const uint32_t lds_v0 = lds_addr(smem_v[0]), lds_v1 = lds_addr(smem_v[1]);
 
   // A-row rho of score tile t holds key 64*(t/2) + 32*hp + 16*(t%2) + vp of
@@ -409,8 +400,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  __syncthreads();  // Q~ and the LSE parts are consumed: LDS is free for the blocks
-  issue_k_block<8>(kimg, lds_k0, wave, lane);
   uint32_t dd = 0;
   if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 

@@ -339,14 +339,9 @@ __global__ void k_quantize_k(const void* __restrict__ k, int is_bf16, int64_t n_
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = v[j] - mu[j];
   }
-  uint32_t c[16];
-  const uint32_t sc = nvfp4_block(v, g, c);
-  uint2 packed;
-  packed.x = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) |
-             (c[6] << 24) | (c[7] << 28);
-  packed.y = c[8] | (c[9] << 4) | (c[10] << 8) | (c[11] << 12) | (c[12] << 16) | (c[13] << 20) |
-             (c[14] << 24) | (c[15] << 28);
-  reinterpret_cast<uint2*>(codes)[gi] = packed;
+  uint32_t w[2];
+  const uint32_t sc = nvfp4_block_packed(v, g, w);
+  reinterpret_cast<uint2*>(codes)[gi] = make_uint2(w[0], w[1]);
   sf[gi] = (uint8_t)sc;
 }
 
