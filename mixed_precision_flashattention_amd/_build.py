@@ -30,23 +30,25 @@ def flags() -> list[str]:
 
 
 PEAKS = os.path.join(PKG, "mpfa_peaks")  # standalone probe of the device's ceilings (bench.py)
+FP4_CHECK = os.path.join(PKG, "mpfa_fp4_check")  # hardware FP4 conversion check (tests)
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libmpfa.so, and the peak probe into
-    mpfa_peaks (always recompiles)."""
+    """Compile every source into libmpfa.so, the peak probe into mpfa_peaks
+    and the FP4 conversion check into mpfa_fp4_check (always recompiles)."""
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *flags(), "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
-    probe = [hipcc(), *[f for f in flags() if f not in ("-fPIC", "-shared")], "-o", PEAKS + ".tmp",
-             os.path.join(CSRC, "peaks.hip")]
-    if verbose:
-        print(" ".join(probe), flush=True)
-    subprocess.check_call(probe)
-    os.replace(PEAKS + ".tmp", PEAKS)
+    exe_flags = [f for f in flags() if f not in ("-fPIC", "-shared")] + ["-I", CSRC]
+    for exe, src in ((PEAKS, "peaks.hip"), (FP4_CHECK, "fp4_check.hip")):
+        cmd = [hipcc(), *exe_flags, "-o", exe + ".tmp", os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 

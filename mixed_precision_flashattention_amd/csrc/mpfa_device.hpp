@@ -160,9 +160,10 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float* x, float g, uint32_
 // nibble of byte t, w[0] = elements 0-7, w[1] = 8-15) by the hardware
 // FP32 -> E2M1 conversion (v_cvt_scalef32_pk_fp4_f32 at unit scale).  Its
 // rounding is that of e2m1_encode -- nearest, ties to the even code,
-// saturating at 6, sign kept -- which was checked on gfx950 for every fp32
-// value within 64 ulps of each E2M1 midpoint and grid point (both signs),
-// for +-0, tiny and huge values and a million random ones.  The quotients are
+// saturating at 6, sign kept -- checked on gfx950 for every fp32 value
+// within 64 ulps of each E2M1 midpoint and grid point (both signs), for +-0,
+// tiny and huge values and a million random ones (csrc/fp4_check.hip, run by
+// the GPU tests).  The quotients are
 // the same correctly rounded divisions; a zero scale converts +-0.
 __device__ __forceinline__ uint32_t nvfp4_block_packed(const float* x, float g, uint32_t (&w)[2]) {
   float ab = 0.0f;
