@@ -4,7 +4,11 @@ like the library's encoder (nearest, ties to the even code, saturating at 6,
 sign kept).  The check program built beside the library compares the two on
 every fp32 value within 64 ulps of each E2M1 midpoint and grid point (both
 signs), on +-0, tiny, huge and denormal values and on a million seeded random
-values."""
+values.  The same program checks the quantizers' per-block quotients (one
+correctly rounded reciprocal per block, two FMA residual corrections per
+element) against IEEE division, bit for bit wherever the quotient reaches
+1/8, for divisors from every E4M3 scale times global scales over 2^-120 ..
+2^120 and dividends within 4 ulps of every E2M1 midpoint and grid point."""
 import json
 import os
 import subprocess
@@ -30,3 +34,4 @@ def test_hardware_fp4_conversion_rounds_like_the_encoder():
     assert r.returncode == 0, r.stdout + r.stderr
     res = json.loads(r.stdout.strip().splitlines()[-1])
     assert res["mismatches"] == 0 and res["values"] > 1_000_000
+    assert res["quotient_mismatches"] == 0 and res["quotients"] > 1_000_000
