@@ -148,11 +148,11 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
   launch_fill_u32((uint32_t*)w, (int64_t)(L.total / 4), 0u, s);
   const float* kc_mean = nullptr;
   if (center) {
-    launch_channel_mean(k, kb, B * Hkv, N, (uint32_t*)(w + L.kmax),
-                        (unsigned long long*)(w + L.ksum), k_mean, s);
-    if (smooth && q)
-      launch_channel_mean(q, q_dtype == MPFA_BF16, B * Hq, N, (uint32_t*)(w + L.qmax),
-                          (unsigned long long*)(w + L.qsum), q_mean, s);
+    const ChannelMeanJob jobs[2] = {
+        {k, kb, B * Hkv, (uint32_t*)(w + L.kmax), (unsigned long long*)(w + L.ksum), k_mean},
+        {q, q_dtype == MPFA_BF16, B * Hq, (uint32_t*)(w + L.qmax),
+         (unsigned long long*)(w + L.qsum), q_mean}};
+    launch_channel_means(jobs, (smooth && q) ? 2 : 1, N, s);  // K and Q in the same launches
     kc_mean = k_mean;
   }
   launch_centered_amax(k, kb, B * Hkv, N, kc_mean, amax, s);
@@ -173,8 +173,15 @@ int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)ws;
   const int vb = v_dtype == MPFA_BF16;
-  launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-  launch_centered_amax(v, vb, B * Hkv, N, nullptr, amax, s);
+  // per-workgroup maxima stored plainly into the workspace and folded into
+  // its first word: no clearing launch (the slotted atomics past the limit)
+  const int n_part = launch_centered_amax_partials(v, vb, B * Hkv, N, nullptr, (float*)ws, s);
+  if (n_part > 0) {
+    launch_partials_fold((const float*)ws, n_part, amax, s);
+  } else {
+    launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
+    launch_centered_amax(v, vb, B * Hkv, N, nullptr, amax, s);
+  }
   launch_quantize_v_codes(v, vb, B * Hkv, N, amax, v_scale, v_fp8, s);
   return launch_status();
 }

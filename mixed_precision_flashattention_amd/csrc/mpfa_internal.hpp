@@ -63,8 +63,17 @@ constexpr int kAmaxSlots = 64;
 constexpr int kAmaxSlotWords = 32;
 constexpr size_t kAmaxBytes = (size_t)kAmaxSlots * kAmaxSlotWords * 4;
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
-void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
-                         unsigned long long* sums, float* mean, hipStream_t st);
+// Sequence channel means of one or two [BH, N, 128] tensors (K and Q) in
+// three launches: absmax, fixed-point sums (both into cleared buffers),
+// finalize into mean.
+struct ChannelMeanJob {
+  const void* x;
+  int is_bf16, BH;
+  uint32_t* absmax;
+  unsigned long long* sums;
+  float* mean;
+};
+void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
                           uint32_t* out, hipStream_t st);
 // The same amax as per-workgroup maxima in partials[0 .. n) (no clearing, no
@@ -73,6 +82,8 @@ void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float
 constexpr int kAmaxPartials = (int)(kAmaxBytes / 4);
 int launch_centered_amax_partials(const void* x, int is_bf16, int BH, int N, const float* mean,
                                   float* partials, hipStream_t st);
+// Fold n such maxima into out[0] (one workgroup; out may alias partials).
+void launch_partials_fold(const float* partials, int n, uint32_t* out, hipStream_t st);
 // Partial maxima of |x - mean| over the rows of a [rows, 128] tensor, one
 // per slot (kRowsAmaxSlots floats, all written): the decode query amax.
 constexpr int kRowsAmaxSlots = 64;

@@ -38,14 +38,52 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, int is_bf16, flo
 
 constexpr int kStatBlocks = 2048;  // target number of blocks per statistics pass
 
+// The sequence-mean passes take one or two [BH, N, 128] tensors of the same
+// N (K and Q) in one launch: blocks [0, nblk0) cover tensor 0 and the rest
+// tensor 1, each as gx row blocks (fastest) times BH heads.  Every result is
+// an order-free reduction, so the split of the grid does not change a bit.
+struct StatJobs {
+  const void* x[2];
+  int is_bf16[2], BH[2], rows[2], gx[2];
+  uint32_t* absmax[2];
+  unsigned long long* sums[2];
+  float* mean[2];
+  int nblk0, N;
+};
+struct StatBlock {
+  const void* x;
+  int is_bf16, rows, r_begin;
+  int64_t bh;
+  uint32_t* absmax;
+  unsigned long long* sums;
+};
+__device__ __forceinline__ StatBlock stat_block(const StatJobs& J) {
+  int f = blockIdx.x;
+  const int t = f >= J.nblk0;
+  if (t) f -= J.nblk0;
+  StatBlock b;
+  const int gx = t ? J.gx[1] : J.gx[0];
+  b.x = t ? J.x[1] : J.x[0];
+  b.is_bf16 = t ? J.is_bf16[1] : J.is_bf16[0];
+  b.rows = t ? J.rows[1] : J.rows[0];
+  b.absmax = t ? J.absmax[1] : J.absmax[0];
+  b.sums = t ? J.sums[1] : J.sums[0];
+  b.bh = f / gx;
+  b.r_begin = (f % gx) * b.rows;
+  return b;
+}
+
 // Per (b, h, d): max over tokens of |x|.
-__global__ __launch_bounds__(256) void k_channel_absmax(const void* __restrict__ x, int is_bf16,
-                                                        int N, int rows_per_block,
-                                                        uint32_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_channel_absmax(StatJobs J) {
   __shared__ float red[16][kD];
-  const int64_t bh = blockIdx.y;
+  const StatBlock sb = stat_block(J);
+  const void* x = sb.x;
+  const int is_bf16 = sb.is_bf16, N = J.N;
+  uint32_t* __restrict__ out = sb.absmax;
+  const int64_t bh = sb.bh;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
-  const int r_begin = blockIdx.x * rows_per_block;
+  const int rows_per_block = sb.rows;
+  const int r_begin = sb.r_begin;
   const int r_end = min(N, r_begin + rows_per_block);
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = r_begin + rl; r < r_end; r += 64) {
@@ -81,12 +119,15 @@ __device__ __forceinline__ long long fixed_point_term(float x, int shift) {
 // has magnitude below 2^30, so the FP32 ldexp is exact wherever the result
 // can round to a nonzero integer, the FP32 round-to-nearest-even gives the
 // same integer as in FP64, and it fits an int32.
-__global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__ x, int is_bf16,
-                                                        int N, int rows_per_block,
-                                                        const uint32_t* __restrict__ absmax,
-                                                        unsigned long long* __restrict__ sums) {
+__global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
   __shared__ long long red[16][kD];
-  const int64_t bh = blockIdx.y;
+  const StatBlock sb = stat_block(J);
+  const void* x = sb.x;
+  const int is_bf16 = sb.is_bf16, N = J.N;
+  const uint32_t* __restrict__ absmax = sb.absmax;
+  unsigned long long* __restrict__ sums = sb.sums;
+  const int64_t bh = sb.bh;
+  const int rows_per_block = sb.rows;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
   int shift[8];
 #pragma unroll
@@ -96,7 +137,7 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__
     if (M != 0.0f) frexpf(M, &E);
     shift[j] = 30 - E;  // an all-zero channel scales zeros: it sums to 0
   }
-  const int r_begin = blockIdx.x * rows_per_block;
+  const int r_begin = sb.r_begin;
   const int r_end = min(N, r_begin + rows_per_block);
   long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = r_begin + rl; r < r_end; r += 64) {
@@ -124,11 +165,16 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(const void* __restrict__
 }
 
 // mean = fp32( (double)S / (double)N * 2^(E-30) ), each FP64 op rounded once.
-__global__ void k_mean_finalize(const uint32_t* __restrict__ absmax,
-                                const unsigned long long* __restrict__ sums, int N, int n,
-                                float* __restrict__ mean) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// Thread i < n0 = BH[0] * 128 finalizes tensor 0's channel i, the rest tensor 1's.
+__global__ void k_mean_finalize(StatJobs J, int n0, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const int t = i >= n0;
+  if (t) i -= n0;
+  const uint32_t* __restrict__ absmax = t ? J.absmax[1] : J.absmax[0];
+  const unsigned long long* __restrict__ sums = t ? J.sums[1] : J.sums[0];
+  float* __restrict__ mean = t ? J.mean[1] : J.mean[0];
+  const int N = J.N;
   const float M = __uint_as_float(absmax[i]);
   if (M == 0.0f) {
     mean[i] = 0.0f;
@@ -312,6 +358,20 @@ __global__ __launch_bounds__(256) void k_rows_amax(const void* __restrict__ x, i
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// n per-workgroup maxima (non-negative) folded into out[0] as fp32 bits; one
+// block, every read before the barrier, so out may alias partials.
+__global__ __launch_bounds__(256) void k_partials_fold(const float* partials, int n,
+                                                       uint32_t* out) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partials[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
 }
 
 // The slots of a reduced amax folded into its first word (one wave).
@@ -567,16 +627,28 @@ static inline int stat_rows_per_block(int BH, int N, int align) {
   return (int)(rows < align ? align : rows);
 }
 
-void launch_channel_mean(const void* x, int is_bf16, int BH, int N, uint32_t* absmax,
-                         unsigned long long* sums, float* mean, hipStream_t st) {
-  const int rows = stat_rows_per_block(BH, N, 64);
-  dim3 grid((unsigned)((N + rows - 1) / rows), BH);
-  hipLaunchKernelGGL(k_channel_absmax, grid, dim3(256), 0, st, x, is_bf16, N, rows, absmax);
-  hipLaunchKernelGGL(k_channel_fixsum, grid, dim3(256), 0, st, x, is_bf16, N, rows,
-                     (const uint32_t*)absmax, sums);
-  const int n = BH * kD;
-  hipLaunchKernelGGL(k_mean_finalize, dim3((n + 255) / 256), dim3(256), 0, st,
-                     (const uint32_t*)absmax, (const unsigned long long*)sums, N, n, mean);
+void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStream_t st) {
+  StatJobs J{};
+  J.N = N;
+  int64_t nblk = 0;
+  for (int t = 0; t < 2; ++t) {
+    const ChannelMeanJob& c = jobs[t < n_jobs ? t : 0];
+    J.x[t] = c.x;
+    J.is_bf16[t] = c.is_bf16;
+    J.BH[t] = c.BH;
+    J.rows[t] = stat_rows_per_block(c.BH, N, 64);
+    J.gx[t] = (N + J.rows[t] - 1) / J.rows[t];
+    J.absmax[t] = c.absmax;
+    J.sums[t] = c.sums;
+    J.mean[t] = c.mean;
+    if (t < n_jobs) nblk += (int64_t)J.gx[t] * c.BH;
+  }
+  J.nblk0 = J.gx[0] * J.BH[0];
+  hipLaunchKernelGGL(k_channel_absmax, dim3((unsigned)nblk), dim3(256), 0, st, J);
+  hipLaunchKernelGGL(k_channel_fixsum, dim3((unsigned)nblk), dim3(256), 0, st, J);
+  const int n0 = J.BH[0] * kD;
+  const int n = n0 + (n_jobs > 1 ? J.BH[1] * kD : 0);
+  hipLaunchKernelGGL(k_mean_finalize, dim3((n + 255) / 256), dim3(256), 0, st, J, n0, n);
 }
 
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,
@@ -599,6 +671,10 @@ int launch_centered_amax_partials(const void* x, int is_bf16, int BH, int N, con
   hipLaunchKernelGGL(k_centered_amax, grid, dim3(256), 0, st, x, is_bf16, N, rows, mean,
                      (uint32_t*)nullptr, partials);
   return (int)(grid.x * grid.y);
+}
+
+void launch_partials_fold(const float* partials, int n, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_partials_fold, dim3(1), dim3(256), 0, st, partials, n, out);
 }
 
 void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, float* slots,
