@@ -21,9 +21,9 @@ struct QuantKWs {
 inline QuantKWs quant_k_layout(int B, int Hq, int Hkv) {
   QuantKWs w;
   const size_t nk = (size_t)B * Hkv * kD, nq = (size_t)B * Hq * kD;
-  w.kmax = 0;
-  w.qmax = align_up(w.kmax + nk * 4);
-  w.ksum = align_up(w.qmax + nq * 4);
+  w.kmax = 0;  // channel ranges: two words per channel
+  w.qmax = align_up(w.kmax + nk * 8);
+  w.ksum = align_up(w.qmax + nq * 8);
   w.qsum = align_up(w.ksum + nk * 8);
   w.amax = align_up(w.qsum + nq * 8);
   w.total = align_up(w.amax + kAmaxBytes);
@@ -148,14 +148,18 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
   launch_fill_u32((uint32_t*)w, (int64_t)(L.total / 4), 0u, s);
   const float* kc_mean = nullptr;
   if (center) {
+    // K and Q in the same launches; the K_c amax comes from K's channel
+    // ranges and means, with no pass of its own
     const ChannelMeanJob jobs[2] = {
-        {k, kb, B * Hkv, (uint32_t*)(w + L.kmax), (unsigned long long*)(w + L.ksum), k_mean},
+        {k, kb, B * Hkv, (uint32_t*)(w + L.kmax), (unsigned long long*)(w + L.ksum), k_mean,
+         amax},
         {q, q_dtype == MPFA_BF16, B * Hq, (uint32_t*)(w + L.qmax),
-         (unsigned long long*)(w + L.qsum), q_mean}};
-    launch_channel_means(jobs, (smooth && q) ? 2 : 1, N, s);  // K and Q in the same launches
+         (unsigned long long*)(w + L.qsum), q_mean, nullptr}};
+    launch_channel_means(jobs, (smooth && q) ? 2 : 1, N, s);
     kc_mean = k_mean;
+  } else {
+    launch_centered_amax(k, kb, B * Hkv, N, nullptr, amax, s);
   }
-  launch_centered_amax(k, kb, B * Hkv, N, kc_mean, amax, s);
   launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf, s);
   if (smooth) launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s);
   return launch_status();

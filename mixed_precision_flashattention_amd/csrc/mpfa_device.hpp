@@ -293,4 +293,15 @@ __device__ __forceinline__ void atomic_max_nonneg(uint32_t* p, float v) {
   atomicMax(p, __float_as_uint(v));
 }
 
+// Any non-NaN float as an unsigned key in the same order (sign bit flipped
+// for non-negative values, all bits for negative ones); a cleared word is
+// below every key.
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ordered_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 }  // namespace mpfa

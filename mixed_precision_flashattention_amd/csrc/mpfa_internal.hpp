@@ -64,14 +64,16 @@ constexpr int kAmaxSlotWords = 32;
 constexpr size_t kAmaxBytes = (size_t)kAmaxSlots * kAmaxSlotWords * 4;
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 // Sequence channel means of one or two [BH, N, 128] tensors (K and Q) in
-// three launches: absmax, fixed-point sums (both into cleared buffers),
-// finalize into mean.
+// three launches: channel ranges, fixed-point sums (both into cleared
+// buffers), finalize into mean, and, with extent non-NULL (a cleared word),
+// the centred amax max |fp32(x - mean)| derived from the ranges.
 struct ChannelMeanJob {
   const void* x;
   int is_bf16, BH;
-  uint32_t* absmax;
+  uint32_t* range;  // 2 * BH * 128 words
   unsigned long long* sums;
   float* mean;
+  uint32_t* extent;
 };
 void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStream_t st);
 void launch_centered_amax(const void* x, int is_bf16, int BH, int N, const float* mean,

@@ -45,16 +45,17 @@ constexpr int kStatBlocks = 2048;  // target number of blocks per statistics pas
 struct StatJobs {
   const void* x[2];
   int is_bf16[2], BH[2], rows[2], gx[2];
-  uint32_t* absmax[2];
+  uint32_t* range[2];  // [2][BH * 128]: ordered keys of max x, then of max -x
   unsigned long long* sums[2];
   float* mean[2];
+  uint32_t* extent[2];  // NULL, or max |fp32(x - mean)| over the tensor
   int nblk0, N;
 };
 struct StatBlock {
   const void* x;
   int is_bf16, rows, r_begin;
-  int64_t bh;
-  uint32_t* absmax;
+  int64_t bh, nch;
+  uint32_t* range;
   unsigned long long* sums;
 };
 __device__ __forceinline__ StatBlock stat_block(const StatJobs& J) {
@@ -66,26 +67,34 @@ __device__ __forceinline__ StatBlock stat_block(const StatJobs& J) {
   b.x = t ? J.x[1] : J.x[0];
   b.is_bf16 = t ? J.is_bf16[1] : J.is_bf16[0];
   b.rows = t ? J.rows[1] : J.rows[0];
-  b.absmax = t ? J.absmax[1] : J.absmax[0];
+  b.range = t ? J.range[1] : J.range[0];
+  b.nch = (int64_t)(t ? J.BH[1] : J.BH[0]) * kD;
   b.sums = t ? J.sums[1] : J.sums[0];
   b.bh = f / gx;
   b.r_begin = (f % gx) * b.rows;
   return b;
 }
 
-// Per (b, h, d): max over tokens of |x|.
+// max |x| of channel i from its range: max(max x, max -x)
+__device__ __forceinline__ float range_absmax(const uint32_t* range, int64_t nch, int64_t i) {
+  return fmaxf(ordered_value(range[i]), ordered_value(range[nch + i]));
+}
+
+// Per (b, h, d): max over tokens of x and of -x (the channel's range).
 __global__ __launch_bounds__(256) void k_channel_absmax(StatJobs J) {
-  __shared__ float red[16][kD];
+  __shared__ float red[2][16][kD];
   const StatBlock sb = stat_block(J);
   const void* x = sb.x;
   const int is_bf16 = sb.is_bf16, N = J.N;
-  uint32_t* __restrict__ out = sb.absmax;
+  uint32_t* __restrict__ out = sb.range;
   const int64_t bh = sb.bh;
   const int cg = threadIdx.x & 15, rl = threadIdx.x >> 4;
   const int rows_per_block = sb.rows;
   const int r_begin = sb.r_begin;
   const int r_end = min(N, r_begin + rows_per_block);
-  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float hi[8], lo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) hi[j] = lo[j] = -INFINITY;
   for (int r = r_begin + rl; r < r_end; r += 64) {
     float v[4][8];
 #pragma unroll
@@ -94,16 +103,23 @@ __global__ __launch_bounds__(256) void k_channel_absmax(StatJobs J) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[k][j]));  // repeats are harmless
+      for (int j = 0; j < 8; ++j) {  // repeats are harmless
+        hi[j] = fmaxf(hi[j], v[k][j]);
+        lo[j] = fmaxf(lo[j], -v[k][j]);
+      }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[rl][8 * cg + j] = m[j];
+  for (int j = 0; j < 8; ++j) {
+    red[0][rl][8 * cg + j] = hi[j];
+    red[1][rl][8 * cg + j] = lo[j];
+  }
   __syncthreads();
-  if (threadIdx.x < kD) {
-    float t = 0.0f;
+  if (threadIdx.x < 2 * kD) {
+    const int side = threadIdx.x >> 7, c = threadIdx.x & (kD - 1);
+    float t = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t = fmaxf(t, red[i][threadIdx.x]);
-    atomic_max_nonneg(out + bh * kD + threadIdx.x, t);
+    for (int i = 0; i < 16; ++i) t = fmaxf(t, red[side][i][c]);
+    atomicMax(out + side * sb.nch + bh * kD + c, ordered_key(t));
   }
 }
 
@@ -124,7 +140,7 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
   const StatBlock sb = stat_block(J);
   const void* x = sb.x;
   const int is_bf16 = sb.is_bf16, N = J.N;
-  const uint32_t* __restrict__ absmax = sb.absmax;
+  const uint32_t* __restrict__ range = sb.range;
   unsigned long long* __restrict__ sums = sb.sums;
   const int64_t bh = sb.bh;
   const int rows_per_block = sb.rows;
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
   int shift[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float M = __uint_as_float(absmax[bh * kD + 8 * cg + j]);
+    const float M = range_absmax(range, sb.nch, bh * kD + 8 * cg + j);
     int E = 0;
     if (M != 0.0f) frexpf(M, &E);
     shift[j] = 30 - E;  // an all-zero channel scales zeros: it sums to 0
@@ -165,26 +181,44 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
 }
 
 // mean = fp32( (double)S / (double)N * 2^(E-30) ), each FP64 op rounded once.
-// Thread i < n0 = BH[0] * 128 finalizes tensor 0's channel i, the rest tensor 1's.
-__global__ void k_mean_finalize(StatJobs J, int n0, int n) {
+// Thread i < n0 = BH[0] * 128 finalizes tensor 0's channel i, the rest tensor
+// 1's (n0 is a multiple of 128, so no wave spans both).  With extent[t]
+// non-NULL (a cleared word) it also takes the tensor's centred amax
+// max |fp32(x - mean)| from the ranges: fp32 subtraction is monotone in x
+// and x - m rounds to the negation of m - x, so over a channel it is
+// max(fp32(max x - m), fp32(m + max -x)), the value a pass over x would
+// find; one atomic per wave.
+__global__ __launch_bounds__(256) void k_mean_finalize(StatJobs J, int n0, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  const bool valid = i < n;
   const int t = i >= n0;
   if (t) i -= n0;
-  const uint32_t* __restrict__ absmax = t ? J.absmax[1] : J.absmax[0];
+  const uint32_t* __restrict__ range = t ? J.range[1] : J.range[0];
   const unsigned long long* __restrict__ sums = t ? J.sums[1] : J.sums[0];
   float* __restrict__ mean = t ? J.mean[1] : J.mean[0];
+  uint32_t* extent = t ? J.extent[1] : J.extent[0];
+  const int64_t nch = (int64_t)(t ? J.BH[1] : J.BH[0]) * kD;
   const int N = J.N;
-  const float M = __uint_as_float(absmax[i]);
-  if (M == 0.0f) {
-    mean[i] = 0.0f;
-    return;
+  float e = 0.0f;
+  if (valid) {
+    const float hi = ordered_value(range[i]), lo = ordered_value(range[nch + i]);
+    const float M = fmaxf(hi, lo);
+    float mu = 0.0f;
+    if (M != 0.0f) {
+      int E;
+      frexpf(M, &E);
+      const double s = (double)(long long)sums[i];
+      mu = (float)((s / (double)N) * ldexp(1.0, E - 30));
+    }
+    mean[i] = mu;
+    const float a = fmaxf(hi - mu, mu + lo);
+    e = a > 0.0f ? a : 0.0f;
   }
-  int E;
-  frexpf(M, &E);
-  const double s = (double)(long long)sums[i];
-  const double m = (s / (double)N) * ldexp(1.0, E - 30);
-  mean[i] = (float)m;
+  if (extent) {  // uniform over the wave
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e = fmaxf(e, __shfl_xor(e, o));
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(extent, e);
+  }
 }
 
 // Channel means of each 128-row tile of a [BH, N, 128] tensor by the rule of
@@ -638,9 +672,10 @@ void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStre
     J.BH[t] = c.BH;
     J.rows[t] = stat_rows_per_block(c.BH, N, 64);
     J.gx[t] = (N + J.rows[t] - 1) / J.rows[t];
-    J.absmax[t] = c.absmax;
+    J.range[t] = c.range;
     J.sums[t] = c.sums;
     J.mean[t] = c.mean;
+    J.extent[t] = c.extent;
     if (t < n_jobs) nblk += (int64_t)J.gx[t] * c.BH;
   }
   J.nblk0 = J.gx[0] * J.BH[0];
