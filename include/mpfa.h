@@ -119,12 +119,18 @@ const char* mpfa_status_string(int status);
  *
  * k, q: [B, Hkv, N, 128] and [B, Hq, N, 128] in k_dtype / q_dtype.
  * Hq: number of query heads (needed in smoothing mode; Hq % Hkv == 0).
+ * q_amax: NULL, or (smoothing mode with q non-NULL) OUTPUT, one device float
+ * <- max |fp32(Q - q_mean)| over Q, the Q_c amax that sets mpfa_prefill's
+ * NVFP4 global scale for this Q; it is taken from the channel statistics
+ * this call computes anyway (the maximum and minimum of each channel and
+ * its mean: fp32 subtraction is monotone), so it costs no pass over Q, and
+ * mpfa_prefill given it skips its own.  Ignored in the other modes.
  * ws: mpfa_workspace_bytes(MPFA_OP_QUANTIZE_K, B, q ? Hq : 0, Hkv, N, 128, 1).
  */
 int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
                           const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
                           uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
-                          void* ws, size_t ws_bytes, void* stream);
+                          float* q_amax, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mpfa_quantize_v_fp8 -- FP8 E4M3 V cache (paper section 4.2: V is neither
@@ -224,6 +230,11 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
  * uncentred scores).
  *
  * Smoothing iff delta_s != NULL (then q_mean and k_mean are required).
+ * q_amax: NULL (the call takes max |fp32(Q - q_mean)|, or max |Q| without
+ * smoothing, in a pass over Q), or a device float holding that value for
+ * this Q and q_mean, as mpfa_quantize_k_nvfp4 writes it (smoothing mode):
+ * the results are then identical and the pass is skipped.  A value for
+ * another Q gives another global scale; it is not checked.
  * causal != 0: key j is visible to row i iff j <= i; else every key.
  * out: [B, Hq, N, 128] in out_dtype (MPFA_BF16, the paper's output, or
  * MPFA_F32).  lse: [B, Hq, N] float, or NULL.
@@ -236,8 +247,9 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
 int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
-                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
-                 void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+                 const float* v_scale, const uint16_t* delta_s, const float* q_amax,
+                 float softmax_scale, int causal, void* out, int out_dtype, float* lse, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /*
  * mpfa_prefill_tile_mean -- mpfa_prefill with the queries smoothed per

@@ -56,15 +56,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_status_string.argtypes = [i32]
     L.mpfa_quantize_k_nvfp4.restype = i32
     L.mpfa_quantize_k_nvfp4.argtypes = [P, i32, i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P,
-                                        P, sz, P]
+                                        P, P, sz, P]
     L.mpfa_quantize_v_fp8.restype = i32
     L.mpfa_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, sz, P]
     L.mpfa_append_kv.restype = i32
     L.mpfa_append_kv.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P,
                                  P]
     L.mpfa_prefill.restype = i32
-    L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
-                               P, i32, P, P, sz, P]
+    L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, f32,
+                               i32, P, i32, P, P, sz, P]
     L.mpfa_prefill_tile_mean.restype = i32
     L.mpfa_prefill_tile_mean.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f32, i32,
                                          P, i32, P, P, P, sz, P]
@@ -132,17 +132,18 @@ def _raise(fn: str, status: int):
 
 
 def mpfa_quantize_k_nvfp4(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, Hq=None,
-                          stream=None):
+                          stream=None, q_amax=None):
     """C-ABI call: k [B, Hkv, N, 128]; q [B, Hq, N, 128] or None (then q_mean is
-    an input); direct mode when k_mean, delta_s (and q_mean) are None."""
-    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws)
+    an input); direct mode when k_mean, delta_s (and q_mean) are None.
+    q_amax: optional float32 [1] output, the Q_c amax for mpfa_prefill."""
+    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, q_amax, ws)
     B, Hkv, N, D = k.shape
     if Hq is None:
         Hq = q.shape[1] if q is not None else (q_mean.shape[1] if q_mean is not None else 0)
     st = load_library().mpfa_quantize_k_nvfp4(
         _ptr(k), _dtype_code(k), B, Hkv, N, D, _ptr(q), _dtype_code(q) if q is not None else 0,
         Hq, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf), _ptr(k_gscale), _ptr(delta_s),
-        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _ptr(q_amax), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_quantize_k_nvfp4", st)
 
 
@@ -156,12 +157,14 @@ def mpfa_quantize_v_fp8(v, v_fp8, v_scale, ws, stream=None):
 
 
 def mpfa_prefill(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
-                 softmax_scale, causal, out, lse, ws, stream=None):
-    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse, ws)
+                 softmax_scale, causal, out, lse, ws, stream=None, q_amax=None):
+    """C-ABI call; q_amax: optional float32 [1] input, the Q_c amax that
+    mpfa_quantize_k_nvfp4 wrote for this q (then no pass over q is made)."""
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, q_amax, out, lse, ws)
     B, Hq, N, D = q.shape
     st = load_library().mpfa_prefill(
         _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
-        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s), _ptr(q_amax),
         float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_prefill", st)
@@ -261,7 +264,9 @@ def _workspace(op, B, Hq, Hkv, N, num_splits, device):
 
 def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
     """Allocate and fill the NVFP4 K cache.  Returns a dict with k_fp4, k_sf,
-    k_gscale and, in smoothing mode, k_mean, q_mean and delta_s.  Smoothing
+    k_gscale and, in smoothing mode, k_mean, q_mean and delta_s (and, with q
+    given, q_amax: the Q_c amax that ``prefill`` then takes instead of a pass
+    over the same q).  Smoothing
     with neither q nor q_mean only centres K (k_mean, no delta_s): the cache
     of ``prefill_tile_mean``."""
     import torch
@@ -283,9 +288,12 @@ def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
         out.update(k_mean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev),
                    q_mean=q_mean,
                    delta_s=torch.empty((B, Hq, N), dtype=torch.int16, device=dev))
+        if q is not None:
+            out["q_amax"] = torch.empty(1, dtype=torch.float32, device=dev)
         ws = _workspace(MPFA_OP_QUANTIZE_K, B, Hq if q is not None else 0, Hkv, N, 1, dev)
         mpfa_quantize_k_nvfp4(k, q, q_mean, out["k_mean"], out["k_fp4"], out["k_sf"],
-                              out["k_gscale"], out["delta_s"], ws, Hq=Hq, stream=stream)
+                              out["k_gscale"], out["delta_s"], ws, Hq=Hq, stream=stream,
+                              q_amax=out.get("q_amax"))
     else:
         ws = _workspace(MPFA_OP_QUANTIZE_K, B, 0, Hkv, N, 1, dev)
         mpfa_quantize_k_nvfp4(k, None, None, None, out["k_fp4"], out["k_sf"], out["k_gscale"],
@@ -308,7 +316,8 @@ def quantize_v(v, stream=None):
 def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False, ws=None,
             out=None, lse=None, stream=None):
     """QK4PV8 prefill from the caches returned by quantize_k / quantize_v.
-    Smoothing iff kq holds delta_s.  Returns (out, lse or None)."""
+    Smoothing iff kq holds delta_s.  q must be the q that quantize_k saw when
+    kq holds its q_amax (as for q_mean and delta_s).  Returns (out, lse or None)."""
     import torch
     B, Hq, N, D = q.shape
     Hkv = kq["k_fp4"].shape[1]
@@ -323,7 +332,8 @@ def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=Fals
     mpfa_prefill(q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
                  kq["k_fp4"], kq["k_sf"], kq["k_gscale"], vq["v_fp8"], vq["v_scale"],
                  kq.get("delta_s") if smooth else None, softmax_scale, causal, out,
-                 lse if with_lse else None, ws, stream=stream)
+                 lse if with_lse else None, ws, stream=stream,
+                 q_amax=kq.get("q_amax") if smooth else None)
     return out, (lse if with_lse else None)
 
 

@@ -114,7 +114,7 @@ const char* mpfa_status_string(int status) {
 int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
                           const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
                           uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          float* q_amax, void* ws, size_t ws_bytes, void* stream) {
   int st = check_sizes(B, Hkv, N, D);
   if (st) return st;
   if (!dtype_ok(k_dtype)) return MPFA_ERR_UNSUPPORTED;
@@ -144,6 +144,8 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
+  // the Q_c amax (second slot of the cleared amax block) when it is asked for
+  uint32_t* q_ext = (smooth && q && q_amax) ? amax + kAmaxSlotWords : nullptr;
   const int kb = k_dtype == MPFA_BF16;
   launch_fill_u32((uint32_t*)w, (int64_t)(L.total / 4), 0u, s);
   const float* kc_mean = nullptr;
@@ -154,13 +156,15 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
         {k, kb, B * Hkv, (uint32_t*)(w + L.kmax), (unsigned long long*)(w + L.ksum), k_mean,
          amax},
         {q, q_dtype == MPFA_BF16, B * Hq, (uint32_t*)(w + L.qmax),
-         (unsigned long long*)(w + L.qsum), q_mean, nullptr}};
+         (unsigned long long*)(w + L.qsum), q_mean, q_ext}};
     launch_channel_means(jobs, (smooth && q) ? 2 : 1, N, s);
     kc_mean = k_mean;
   } else {
     launch_centered_amax(k, kb, B * Hkv, N, nullptr, amax, s);
   }
-  launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf, s);
+  // the K quantizer also copies the Q_c amax word out (it runs after the finalize)
+  launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf,
+                          q_ext, q_ext ? q_amax : nullptr, s);
   if (smooth) launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s);
   return launch_status();
 }
@@ -259,8 +263,9 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
 int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
-                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
-                 void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                 const float* v_scale, const uint16_t* delta_s, const float* q_amax,
+                 float softmax_scale, int causal, void* out, int out_dtype, float* lse, void* ws,
+                 size_t ws_bytes, void* stream) {
   int st = check_sizes(B, Hkv, N, D);
   if (st) return st;
   if ((st = check_heads(Hq, Hkv, B))) return st;
@@ -284,12 +289,16 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
   // Q_c amax as per-workgroup maxima, folded by the K expansion that follows
   // (more heads than partial slots: cleared slots, atomics and a fold)
+  // (given by the caller: no pass at all)
   const float* qm = delta_s ? q_mean : nullptr;
-  const int n_part = launch_centered_amax_partials(q, q_dtype == MPFA_BF16, B * Hq, N, qm,
-                                                   (float*)amax, s);
-  if (n_part < 0) {
-    launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
-    launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, qm, amax, s);
+  int n_part = 0;
+  if (!q_amax) {
+    n_part = launch_centered_amax_partials(q, q_dtype == MPFA_BF16, B * Hq, N, qm, (float*)amax,
+                                           s);
+    if (n_part < 0) {
+      launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
+      launch_centered_amax(q, q_dtype == MPFA_BF16, B * Hq, N, qm, amax, s);
+    }
   }
   launch_expand_k(k_fp4, k_sf, (int64_t)B * Hkv, N, k_f16, s, /*bf16=*/false,
                   n_part > 0 ? (const float*)amax : nullptr, n_part, amax);
@@ -314,7 +323,7 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.out = out;
   p.out_bf16 = out_dtype == MPFA_BF16;
   p.lse = lse;
-  p.q_amax = amax;
+  p.q_amax = q_amax ? reinterpret_cast<const uint32_t*>(q_amax) : amax;
   p.n_units = n_units;
   launch_prefill(p, s);
   return launch_status();

@@ -95,9 +95,10 @@ void launch_rows_amax(const void* x, int is_bf16, int rows, const float* mean, f
 // amax of the tile-centred tensor into amax[0], as launch_centered_amax does.
 void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, uint32_t* amax,
                       hipStream_t st);
+// q_amax non-NULL: also copies the word q_ext (a Q_c amax) into *q_amax
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
-                             hipStream_t st);
+                             const uint32_t* q_ext, float* q_amax, hipStream_t st);
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
                     const float* q_mean, uint16_t* delta, hipStream_t st);
 void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,

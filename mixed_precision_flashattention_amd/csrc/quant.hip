@@ -421,10 +421,14 @@ __global__ __launch_bounds__(64) void k_amax_fold(uint32_t* __restrict__ out) {
 __global__ void k_quantize_k(const void* __restrict__ k, int is_bf16, int64_t n_groups, int N,
                              const float* __restrict__ k_mean,
                              const uint32_t* __restrict__ amax, float* __restrict__ gscale_out,
-                             uint8_t* __restrict__ codes, uint8_t* __restrict__ sf) {
+                             uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+                             const uint32_t* __restrict__ q_ext, float* __restrict__ q_amax_out) {
   const float g = nvfp4_global_scale(__uint_as_float(*amax));
   const int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (gi == 0) *gscale_out = g;
+  if (gi == 0) {
+    *gscale_out = g;
+    if (q_amax_out) *q_amax_out = __uint_as_float(*q_ext);  // the Q_c amax, passed on
+  }
   if (gi >= n_groups) return;
   float v[16];
   load16(k, gi * 16, is_bf16, v);
@@ -727,10 +731,10 @@ void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, ui
 
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
-                             hipStream_t st) {
+                             const uint32_t* q_ext, float* q_amax, hipStream_t st) {
   const int64_t n_groups = (int64_t)BH * N * (kD / 16);
   hipLaunchKernelGGL(k_quantize_k, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, st, k,
-                     is_bf16, n_groups, N, k_mean, amax, gscale, codes, sf);
+                     is_bf16, n_groups, N, k_mean, amax, gscale, codes, sf, q_ext, q_amax);
 }
 
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,

@@ -101,7 +101,8 @@ class _Fake:
 
 def _prefill(lib, f, **kw):
     a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
-             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, causal=1,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, q_amax=None, scale=0.088,
+             causal=1,
              out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256, stream=None)
     a.update(kw)
     return lib.mpfa_prefill(*a.values())
@@ -167,15 +168,15 @@ def test_decode_rejects_bad_arguments(lib):
 def test_quantizers_reject_bad_arguments(lib):
     f = _Fake()
     qk = lib.mpfa_quantize_k_nvfp4
-    # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, ws_bytes, stream)
+    # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, q_amax, ws, ws_bytes, stream)
     # centring only (k_mean without delta_s) takes no query tensor
-    assert qk(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, None, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, f.mis, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -2
-    assert qk(f.mis, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 8, None) == -3
+    assert qk(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, None, f.p, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, f.mis, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -2
+    assert qk(f.mis, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 8, None) == -3
     qv = lib.mpfa_quantize_v_fp8
     assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, 256, None) == -2
     assert qv(f.p, 1, 1, 2, 64, 128, None, f.p, f.p, 256, None) == -1

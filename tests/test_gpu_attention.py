@@ -209,3 +209,29 @@ def test_decode_degenerate_inputs(mpfa, oracle_mod, edit):
     out, O = _check_decode(mpfa, oracle_mod, cfg, edit=edit)
     if edit is _zero_v:
         assert not np.any(out), "zero V must give a zero output"
+
+
+def test_prefill_takes_the_first_stage_query_amax(mpfa, oracle_mod):
+    """The Q_c amax written by the first stage (from its channel ranges and
+    means) is max |fp32(Q - q_mean)| exactly, and a prefill given it returns
+    the bytes of one that takes the amax in its own pass."""
+    import torch
+    torch.manual_seed(11)
+    B, Hq, Hkv, N = 2, 8, 2, 777
+    say(f"case: first-stage Q amax, B={B} Hq={Hq} Hkv={Hkv} N={N}")
+    q = (torch.randn(B, Hq, N, 128) * 2.0 + torch.randn(1, 1, 1, 128)).to(torch.bfloat16).cuda()
+    q[1, 3, 100, 7] = 40.0  # one spike sets the amax
+    k = torch.randn(B, Hkv, N, 128).to(torch.bfloat16).cuda()
+    v = torch.randn(B, Hkv, N, 128).to(torch.bfloat16).cuda()
+    kq = mpfa.quantize_k(k, q=q)
+    vq = mpfa.quantize_v(v)
+    torch.cuda.synchronize()
+    want = (q.float() - kq["q_mean"][:, :, None, :]).abs().max()
+    assert kq["q_amax"].item() == want.item()
+    scale = 128 ** -0.5
+    out_a, lse_a = mpfa.prefill(q, kq, vq, scale, causal=True, with_lse=True)
+    kq_no = {key: val for key, val in kq.items() if key != "q_amax"}
+    out_b, lse_b = mpfa.prefill(q, kq_no, vq, scale, causal=True, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(lse_a, lse_b)
