@@ -31,6 +31,7 @@ def _buffers(mpfa, torch, B, Hq, Hkv, N, P, dev):
          "k_mean": torch.empty((B, Hkv, D), dtype=f32, device=dev),
          "q_mean": torch.empty((B, Hq, D), dtype=f32, device=dev),
          "delta_s": torch.empty((B, Hq, N), dtype=torch.int16, device=dev),
+         "q_amax": torch.empty(1, dtype=torch.float32, device=dev),
          "v_fp8": torch.empty((B, Hkv, (N + 31) // 32, D, 32), dtype=u8, device=dev),
          "v_scale": torch.empty(1, dtype=f32, device=dev),
          "out": torch.empty((B, Hq, N, D), dtype=f32, device=dev),
@@ -51,8 +52,8 @@ def test_graph_replays_equal_eager(mpfa):
     from mixed_precision_flashattention_amd import synth
     cfg = synth.config("llama8b_prefill_16k", B=1, Hq=8, Hkv=2, N=777)
     B, Hq, Hkv, N, P = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, 3
-    say(f"case: graph capture of stage one + prefill + decode B{B} Hq{Hq}/Hkv{Hkv} N{N} "
-        f"{P} splits, bf16 inputs")
+    say(f"case: graph capture of stage one (Q_c amax handed on) + prefill + decode "
+        f"B{B} Hq{Hq}/Hkv{Hkv} N{N} {P} splits, bf16 inputs")
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(synth.full(cfg, t)).to(dev).to(torch.bfloat16)
                for t in ("q", "k", "v"))
@@ -61,17 +62,17 @@ def test_graph_replays_equal_eager(mpfa):
 
     def calls():
         mpfa.mpfa_quantize_k_nvfp4(k, q, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"],
-                                   b["k_gscale"], b["delta_s"], b["ws_k"])
+                                   b["k_gscale"], b["delta_s"], b["ws_k"], q_amax=b["q_amax"])
         mpfa.mpfa_quantize_v_fp8(v, b["v_fp8"], b["v_scale"], b["ws_v"])
         mpfa.mpfa_prefill(q, Hkv, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"], b["k_gscale"],
                           b["v_fp8"], b["v_scale"], b["delta_s"], cfg.scale, True, b["out"],
-                          b["lse"], b["ws_p"])
+                          b["lse"], b["ws_p"], q_amax=b["q_amax"])
         mpfa.mpfa_decode(qd, Hkv, N, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"],
                          b["k_gscale"], b["v_fp8"], b["v_scale"], b["delta_s"], cfg.scale, P,
                          b["dout"], b["dlse"], b["ws_d"])
 
-    results = ("k_fp4", "k_sf", "k_gscale", "k_mean", "q_mean", "delta_s", "v_fp8", "v_scale",
-               "out", "lse", "dout", "dlse")
+    results = ("k_fp4", "k_sf", "k_gscale", "k_mean", "q_mean", "delta_s", "q_amax", "v_fp8",
+               "v_scale", "out", "lse", "dout", "dlse")
     calls()
     torch.cuda.synchronize()
     ref = {n: b[n].clone() for n in results}
