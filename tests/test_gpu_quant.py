@@ -148,3 +148,29 @@ def test_quantize_v(mpfa, oracle_mod, N, dtype):
     # positions past N in the last tile are code 0
     full = mpfa.v_tiles_to_rows(tiled, tiled.shape[2] * 32)
     assert (full[:, :, N:, :] == 0).all()
+
+
+def test_delta_s_crafted_rounding_rows(mpfa, oracle_mod):
+    """Delta_S rows built so that an FP32-accumulated dot product (catastrophic
+    cancellation), a single rounding of the FP64 sum straight to bf16 (double
+    rounding at a bf16 tie) or another summation order would each give other
+    bytes; every row also appears negated, so the K mean is exactly zero and
+    K_c = K.  The query mean is frozen (an input)."""
+    import torch
+    D = 128
+    base = np.zeros((8, D), dtype=np.float32)
+    base[0, :3] = [2.0 ** 24, 1.0, -2.0 ** 24]
+    base[1, :3] = [2.0 ** 40, 3.0, -2.0 ** 40]
+    base[2, :3] = [1.0, 2.0 ** -8, 2.0 ** -30]
+    base[3, :3] = [3.0, 2.0 ** -7, 2.0 ** -29]
+    base[4, :3] = [2.0 ** 60, 1.0, -2.0 ** 60]
+    base[5, :3] = [2.0 ** 60, -2.0 ** 60, 1.0]
+    base[6, :3] = [1.0, -1.0, 0.0]
+    base[7, :3] = [-0.75, 2.0 ** -9, -(2.0 ** -33)]
+    k = np.concatenate([base, -base])[None, None]
+    qm = np.zeros((1, 1, D), dtype=np.float32)
+    qm[0, 0, :3] = 1.0
+    say(f"case: crafted Delta_S rounding rows ({k.shape[2]} rows)")
+    _compare_k(mpfa, oracle_mod, k, q_mean=qm, dtype=torch.float32)
+    ref = oracle_mod.quantize_k(k, q_mean=qm)
+    assert ref["delta_s"][0, 0, 0] == 0x3F80 and ref["delta_s"][0, 0, 4] == 0x0000

@@ -155,19 +155,102 @@ def test_fp8_v_matches_torch_conversion(oracle_mod):
 
 
 # ---------------------------------------------------------------- delta_S --
-def test_delta_s_against_fp64_gemv(oracle_mod):
+def _bf16_bits_of_f32(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _exact_then_round(qm, kc):
+    """bf16(fp32(exact sum of the exact FP64 products)), by math.fsum."""
+    exact = np.array([math.fsum(float(a) * float(b) for a, b in zip(qm, row)) for row in kc])
+    return _bf16_bits_of_f32(exact.astype(np.float32)), exact
+
+
+def _fp32_accumulated(qm, kc):
+    """A plausible mistake: the dot product accumulated in FP32."""
+    out = np.empty(len(kc), dtype=np.float32)
+    for j, row in enumerate(kc):
+        acc = np.float32(0.0)
+        for a, b in zip(qm, row):
+            acc = np.float32(acc + np.float32(a) * np.float32(b))
+        out[j] = acc
+    return _bf16_bits_of_f32(out)
+
+
+def _direct_to_bf16(x):
+    """Another plausible mistake: the FP64 sum rounded to bf16 in one step
+    (round to 8 significant bits, ties to even), skipping the fp32 rounding."""
+    out = np.empty(len(x), dtype=np.uint16)
+    for j, v in enumerate(x):
+        if v == 0.0:
+            out[j] = 0x8000 if math.copysign(1.0, v) < 0 else 0
+            continue
+        _, e = math.frexp(v)
+        r = round(math.ldexp(v, 8 - e)) * 2.0 ** (e - 8)  # Python round: ties to even
+        out[j] = _bf16_bits_of_f32(np.float32(r))
+    return out
+
+
+def test_delta_s_bit_exact_against_exact_sum(oracle_mod):
+    """Delta_S = bf16(fp32(sum_d Qbar_d K_c[j, d])) with the sum in FP64 over
+    ascending d (products of two fp32 values are exact in FP64).  On inputs
+    whose partial sums stay inside FP64's 53 bits -- all of these -- that is
+    the exact sum rounded once to fp32 and once to bf16, so the oracle must
+    equal math.fsum's exact sum rounded that way, byte for byte."""
     rng = np.random.default_rng(6)
-    kc = (rng.standard_normal((4000, 128)) * 2).astype(np.float32)
+    kc = (rng.standard_normal((2000, 128)) * 2).astype(np.float32)
     qm = (rng.standard_normal(128) * 0.1).astype(np.float32)
-    mine = oracle_mod.delta_s(qm, kc)
-    exact = kc.astype(np.float64) @ qm.astype(np.float64)
-    ref = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    # numpy's FP64 GEMV sums in another order; after two roundings the bytes agree
-    # except where the FP64 sums straddle a rounding boundary
-    assert np.mean(mine == ref) > 0.999
-    got = oracle_mod.bf16_to_f64(mine)
+    ref, exact = _exact_then_round(qm, kc)
+    assert np.array_equal(oracle_mod.delta_s(qm, kc), ref)
+    got = oracle_mod.bf16_to_f64(ref)
     rel = np.abs(got - exact) / np.maximum(np.abs(exact), 1e-30)
     assert np.all(rel <= 2.0 ** -8)  # the page's bound for BF16 carriage of delta_S (§7.4)
+
+
+def test_delta_s_crafted_rounding_rows(oracle_mod):
+    """Rows on which the two plausible mistakes give other bytes:
+    - catastrophic cancellation: 2^24 + 1 - 2^24 is 0 in FP32 accumulation and
+      1 in FP64 (and likewise 2^40 + 3 - 2^40);
+    - double rounding: 1 + 2^-8 + 2^-30 rounds to fp32 1 + 2^-8, a bf16 tie
+      that goes to the even 1.0, while one rounding straight to bf16 gives
+      1 + 2^-7.
+    The oracle must give the exact-sum bytes on every row, and each mistake
+    must differ from them on the rows built against it."""
+    D = 128
+    qm = np.zeros(D, dtype=np.float32)
+    qm[:3] = 1.0
+    rows = np.zeros((6, D), dtype=np.float32)
+    rows[0, :3] = [2.0 ** 24, 1.0, -2.0 ** 24]            # FP32 accumulation loses the 1
+    rows[1, :3] = [2.0 ** 40, 3.0, -2.0 ** 40]            # likewise the 3
+    rows[2, :3] = [1.0, 2.0 ** -8, 2.0 ** -30]            # double rounding
+    rows[3, :3] = [-1.0, -(2.0 ** -8), -(2.0 ** -30)]     # its mirror
+    rows[4, :3] = [3.0, 2.0 ** -7, 2.0 ** -29]           # the same at 3 (bf16 step 2^-6)
+    rows[5, :3] = [1.0, -1.0, 0.0]                        # exact zero
+    got = oracle_mod.delta_s(qm, rows)
+    ref, exact = _exact_then_round(qm, rows)
+    assert np.array_equal(got, ref)
+    assert got[0] == 0x3F80 and got[1] == 0x4040 and got[2] == 0x3F80 and got[3] == 0xBF80
+    assert got[4] == 0x4040 and got[5] == 0x0000
+    fp32acc = _fp32_accumulated(qm, rows)
+    assert fp32acc[0] != got[0] and fp32acc[1] != got[1]
+    direct = _direct_to_bf16(exact)
+    assert direct[2] != got[2] and direct[3] != got[3] and direct[4] != got[4]
+
+
+def test_delta_s_sums_in_ascending_channel_order(oracle_mod):
+    """Where FP64 itself rounds, the stated order decides: 2^60 + 1 - 2^60
+    summed over ascending d in FP64 is 0 (the exact sum is 1, and summing the
+    other way round, 1 first, keeps it too only if the large terms cancel
+    first).  The oracle follows the ascending-d FP64 rule that the GPU
+    stage one also follows."""
+    D = 128
+    qm = np.zeros(D, dtype=np.float32)
+    qm[:3] = 1.0
+    row = np.zeros((1, D), dtype=np.float32)
+    row[0, :3] = [2.0 ** 60, 1.0, -2.0 ** 60]
+    assert oracle_mod.delta_s(qm, row)[0] == 0x0000
+    row[0, :3] = [2.0 ** 60, -2.0 ** 60, 1.0]
+    assert oracle_mod.delta_s(qm, row)[0] == 0x3F80
 
 
 # ---------------------------------------------------- page closed forms --
