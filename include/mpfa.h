@@ -47,6 +47,15 @@
  *
  * The value represented by a K code is e2m1(code) * e4m3(sf) * k_gscale and
  * by a V code e4m3(code) * v_scale.
+ *
+ * The V cache holds the same bytes as a row-major [B, Hkv, N, 128] FP8 cache
+ * (one byte per element, paper section 6), permuted inside each 32-token
+ * tile: the FP8 matrix instruction of P.V takes, per lane, 32 consecutive
+ * tokens of one channel, which this layout serves with plain 16-byte loads
+ * and no transpose.  Its size is 128 * 32 * ceil(N / 32) bytes per
+ * (batch, KV head): N * 128 rounded up to whole tiles.  Converting to or from
+ * the row layout is a pure byte permutation (byte (t, d) of the row layout is
+ * byte [t / 32][d][t % 32] here).
  */
 #ifndef MPFA_H_
 #define MPFA_H_
@@ -119,18 +128,32 @@ const char* mpfa_status_string(int status);
  *
  * k, q: [B, Hkv, N, 128] and [B, Hq, N, 128] in k_dtype / q_dtype.
  * Hq: number of query heads (needed in smoothing mode; Hq % Hkv == 0).
- * q_amax: NULL, or (smoothing mode with q non-NULL) OUTPUT, one device float
- * <- max |fp32(Q - q_mean)| over Q, the Q_c amax that sets mpfa_prefill's
- * NVFP4 global scale for this Q; it is taken from the channel statistics
- * this call computes anyway (the maximum and minimum of each channel and
- * its mean: fp32 subtraction is monotone), so it costs no pass over Q, and
- * mpfa_prefill given it skips its own.  Ignored in the other modes.
  * ws: mpfa_workspace_bytes(MPFA_OP_QUANTIZE_K, B, q ? Hq : 0, Hkv, N, 128, 1).
  */
 int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
-                          const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
+                          const void* q_or_null, int q_dtype, int Hq, float* q_mean, float* k_mean,
                           uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
-                          float* q_amax, void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_quantize_k_nvfp4_with_q_amax -- mpfa_quantize_k_nvfp4 in smoothing
+ * mode with the query tensor given (q_or_null and delta_s non-NULL; any
+ * other mode returns MPFA_ERR_INVALID), which also writes
+ *   q_amax[0] <- max |fp32(Q - q_mean)| over the whole Q tensor,
+ * the amax that sets the NVFP4 global scale of the in-kernel query
+ * quantization of mpfa_prefill for this Q (paper section 5.1: the first stage
+ * feeds the second).  It is derived from the channel statistics the call
+ * computes anyway (each channel's largest and smallest value and its mean:
+ * fp32 subtraction is monotone, so the value is the one a pass over Q finds),
+ * so it costs no pass over Q.  Hand it to mpfa_prefill_with_q_amax with the
+ * same Q.  q_amax: device float [1], 16-byte aligned.  Other arguments,
+ * workspace and errors as mpfa_quantize_k_nvfp4.
+ */
+int mpfa_quantize_k_nvfp4_with_q_amax(const void* k, int k_dtype, int B, int Hkv, int N, int D,
+                                      const void* q_or_null, int q_dtype, int Hq, float* q_mean,
+                                      float* k_mean, uint8_t* k_fp4, uint8_t* k_sf,
+                                      float* k_gscale, uint16_t* delta_s, float* q_amax, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /*
  * mpfa_quantize_v_fp8 -- FP8 E4M3 V cache (paper section 4.2: V is neither
@@ -230,26 +253,41 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
  * uncentred scores).
  *
  * Smoothing iff delta_s != NULL (then q_mean and k_mean are required).
- * q_amax: NULL (the call takes max |fp32(Q - q_mean)|, or max |Q| without
- * smoothing, in a pass over Q), or a device float holding that value for
- * this Q and q_mean, as mpfa_quantize_k_nvfp4 writes it (smoothing mode):
- * the results are then identical and the pass is skipped.  A value for
- * another Q gives another global scale; it is not checked.
+ * The NVFP4 global scale of Q comes from a pass over Q_c in this call.
  * causal != 0: key j is visible to row i iff j <= i; else every key.
  * out: [B, Hq, N, 128] in out_dtype (MPFA_BF16, the paper's output, or
- * MPFA_F32).  lse: [B, Hq, N] float, or NULL.
+ * MPFA_F32).  lse_or_null: [B, Hq, N] float, or NULL.
  * ws: mpfa_workspace_bytes(MPFA_OP_PREFILL, B, Hq, Hkv, N, 128, 1) bytes
  * (8192 + B * Hkv * ceil(N / 128) * 32768, rounded up to 256): the per-call
  * Q amax and the K cache expanded once per call to exact FP16 operands
- * (code value x block scale, 32 KB per 128-key block, zero past N), which
- * the attention kernel copies into LDS block by block.
+ * (code value x block scale, 32 KB per 128-key block, 256 bytes per key
+ * against the cache's 72, zero past N), which the attention kernel copies
+ * into LDS block by block.  It is caller-owned scratch: nothing in it
+ * outlives the call.
  */
 int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
-                 const float* v_scale, const uint16_t* delta_s, const float* q_amax,
-                 float softmax_scale, int causal, void* out, int out_dtype, float* lse, void* ws,
-                 size_t ws_bytes, void* stream);
+                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
+                 void* out, int out_dtype, float* lse_or_null, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/*
+ * mpfa_prefill_with_q_amax -- mpfa_prefill in smoothing mode that takes the
+ * Q_c amax from the first stage (mpfa_quantize_k_nvfp4_with_q_amax on the
+ * same Q) instead of a pass over Q: identical results, one launch less.
+ * q_amax: device float [1] holding max |fp32(Q - q_mean)| for this Q and
+ * q_mean; a value that belongs to another Q gives another global scale, and
+ * the library cannot detect that (it never reads device memory on the host).
+ * delta_s == NULL or q_amax == NULL returns MPFA_ERR_INVALID.  Other
+ * arguments, workspace and errors as mpfa_prefill.
+ */
+int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                             const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                             const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                             const float* v_scale, const uint16_t* delta_s, const float* q_amax,
+                             float softmax_scale, int causal, void* out, int out_dtype,
+                             float* lse_or_null, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mpfa_prefill_tile_mean -- mpfa_prefill with the queries smoothed per
@@ -263,10 +301,13 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
  *     means (the last tile averages only its rows);
  *   Q_c = fp32(Q_i - q_tile_mean[tile of i]); NVFP4 with global scale
  *     gQ = amax(|Q_c|) / 2688 over the whole call;
- *   query operand of row i, channel d, in units of gQ:
- *     bf16_rne(fp32(code value x block scale + fp32(q_tile_mean / gQ)))
- *   S_ij = operand_i . K~_c[j] (FP32 accumulation) -- the centred product
- *     plus the column term Qbar_tile . K~_c[j];
+ *   Delta_tile[t, j] = bf16(fp32(q_tile_mean[t] . K~_c[j])), K~_c the
+ *     dequantized centred key, the column term of the tile's mean, carried
+ *     in BF16 like Delta_S (section 5.2) and computed in the attention kernel
+ *     one 128-key block ahead by a matrix product of the mean's three exact
+ *     bf16 parts with the K operands (FP32 accumulation);
+ *   S_ij = Q~_c,i . K~_c,j + Delta_tile[tile of i, j], the offset written into
+ *     the score accumulator by the rank-one step of mpfa_prefill;
  * then the online softmax, P.V and epilogue of mpfa_prefill; lse adds back
  * scale * (Q_i . k_mean).
  *

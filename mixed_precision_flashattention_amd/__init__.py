@@ -28,8 +28,9 @@ HEAD_DIM = 128
 V_TILE = 32  # tokens per head-dim-major V tile
 
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
-           "mpfa_quantize_v_fp8", "mpfa_append_kv", "mpfa_append_kv_paged", "mpfa_prefill",
-           "mpfa_decode", "mpfa_decode_paged", "mpfa_prefill_tile_mean")
+           "mpfa_quantize_k_nvfp4_with_q_amax", "mpfa_quantize_v_fp8", "mpfa_append_kv",
+           "mpfa_append_kv_paged", "mpfa_prefill", "mpfa_prefill_with_q_amax", "mpfa_decode",
+           "mpfa_decode_paged", "mpfa_prefill_tile_mean")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -56,15 +57,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_status_string.argtypes = [i32]
     L.mpfa_quantize_k_nvfp4.restype = i32
     L.mpfa_quantize_k_nvfp4.argtypes = [P, i32, i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P,
-                                        P, P, sz, P]
+                                        P, sz, P]
+    L.mpfa_quantize_k_nvfp4_with_q_amax.restype = i32
+    L.mpfa_quantize_k_nvfp4_with_q_amax.argtypes = [P, i32, i32, i32, i32, i32, P, i32, i32, P, P,
+                                                    P, P, P, P, P, P, sz, P]
     L.mpfa_quantize_v_fp8.restype = i32
     L.mpfa_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, sz, P]
     L.mpfa_append_kv.restype = i32
     L.mpfa_append_kv.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P,
                                  P]
     L.mpfa_prefill.restype = i32
-    L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, f32,
-                               i32, P, i32, P, P, sz, P]
+    L.mpfa_prefill.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
+                               P, i32, P, P, sz, P]
+    L.mpfa_prefill_with_q_amax.restype = i32
+    L.mpfa_prefill_with_q_amax.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                           P, f32, i32, P, i32, P, P, sz, P]
     L.mpfa_prefill_tile_mean.restype = i32
     L.mpfa_prefill_tile_mean.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f32, i32,
                                          P, i32, P, P, P, sz, P]
@@ -132,19 +139,31 @@ def _raise(fn: str, status: int):
 
 
 def mpfa_quantize_k_nvfp4(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, Hq=None,
-                          stream=None, q_amax=None):
+                          stream=None):
     """C-ABI call: k [B, Hkv, N, 128]; q [B, Hq, N, 128] or None (then q_mean is
-    an input); direct mode when k_mean, delta_s (and q_mean) are None.
-    q_amax: optional float32 [1] output, the Q_c amax for mpfa_prefill."""
-    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, q_amax, ws)
+    an input); direct mode when k_mean, delta_s (and q_mean) are None."""
+    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws)
     B, Hkv, N, D = k.shape
     if Hq is None:
         Hq = q.shape[1] if q is not None else (q_mean.shape[1] if q_mean is not None else 0)
     st = load_library().mpfa_quantize_k_nvfp4(
         _ptr(k), _dtype_code(k), B, Hkv, N, D, _ptr(q), _dtype_code(q) if q is not None else 0,
         Hq, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf), _ptr(k_gscale), _ptr(delta_s),
-        _ptr(q_amax), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_quantize_k_nvfp4", st)
+
+
+def mpfa_quantize_k_nvfp4_with_q_amax(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s,
+                                      q_amax, ws, stream=None):
+    """C-ABI call: smoothing mode with q given; also writes q_amax (float32 [1]),
+    the Q_c amax that mpfa_prefill_with_q_amax takes for this q."""
+    _check(k, q, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, q_amax, ws)
+    B, Hkv, N, D = k.shape
+    st = load_library().mpfa_quantize_k_nvfp4_with_q_amax(
+        _ptr(k), _dtype_code(k), B, Hkv, N, D, _ptr(q), _dtype_code(q), q.shape[1], _ptr(q_mean),
+        _ptr(k_mean), _ptr(k_fp4), _ptr(k_sf), _ptr(k_gscale), _ptr(delta_s), _ptr(q_amax),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_quantize_k_nvfp4_with_q_amax", st)
 
 
 def mpfa_quantize_v_fp8(v, v_fp8, v_scale, ws, stream=None):
@@ -157,17 +176,29 @@ def mpfa_quantize_v_fp8(v, v_fp8, v_scale, ws, stream=None):
 
 
 def mpfa_prefill(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
-                 softmax_scale, causal, out, lse, ws, stream=None, q_amax=None):
-    """C-ABI call; q_amax: optional float32 [1] input, the Q_c amax that
-    mpfa_quantize_k_nvfp4 wrote for this q (then no pass over q is made)."""
-    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, q_amax, out, lse, ws)
+                 softmax_scale, causal, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse, ws)
     B, Hq, N, D = q.shape
     st = load_library().mpfa_prefill(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_prefill", st)
+
+
+def mpfa_prefill_with_q_amax(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale,
+                             delta_s, q_amax, softmax_scale, causal, out, lse, ws, stream=None):
+    """C-ABI call; q_amax: float32 [1], the Q_c amax that
+    mpfa_quantize_k_nvfp4_with_q_amax wrote for this same q (no pass over q)."""
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, q_amax, out, lse, ws)
+    B, Hq, N, D = q.shape
+    st = load_library().mpfa_prefill_with_q_amax(
         _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
         _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s), _ptr(q_amax),
         float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
-    _raise("mpfa_prefill", st)
+    _raise("mpfa_prefill_with_q_amax", st)
 
 
 def mpfa_prefill_tile_mean(q, Hkv, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, softmax_scale,
@@ -262,13 +293,22 @@ def _workspace(op, B, Hq, Hkv, N, num_splits, device):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def query_identity(q):
+    """What identifies one query tensor's contents for the Q_c amax hand-off,
+    as a small host int64 tensor: its storage address, in-place version
+    counter, device index, dtype code and shape."""
+    import torch
+    return torch.tensor([q.data_ptr(), q._version, q.device.index or 0, _dtype_code(q), *q.shape],
+                        dtype=torch.int64)
+
+
 def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
     """Allocate and fill the NVFP4 K cache.  Returns a dict with k_fp4, k_sf,
     k_gscale and, in smoothing mode, k_mean, q_mean and delta_s (and, with q
     given, q_amax: the Q_c amax that ``prefill`` then takes instead of a pass
-    over the same q).  Smoothing
-    with neither q nor q_mean only centres K (k_mean, no delta_s): the cache
-    of ``prefill_tile_mean``."""
+    over q, with q_amax_of: the identity of that q, which ``prefill`` checks).
+    Smoothing with neither q nor q_mean only centres K (k_mean, no delta_s):
+    the cache of ``prefill_tile_mean``."""
     import torch
     B, Hkv, N, D = k.shape
     dev = k.device
@@ -288,12 +328,16 @@ def quantize_k(k, q=None, q_mean=None, smooth=True, Hq=None, stream=None):
         out.update(k_mean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev),
                    q_mean=q_mean,
                    delta_s=torch.empty((B, Hq, N), dtype=torch.int16, device=dev))
+        ws = _workspace(MPFA_OP_QUANTIZE_K, B, Hq if q is not None else 0, Hkv, N, 1, dev)
         if q is not None:
             out["q_amax"] = torch.empty(1, dtype=torch.float32, device=dev)
-        ws = _workspace(MPFA_OP_QUANTIZE_K, B, Hq if q is not None else 0, Hkv, N, 1, dev)
-        mpfa_quantize_k_nvfp4(k, q, q_mean, out["k_mean"], out["k_fp4"], out["k_sf"],
-                              out["k_gscale"], out["delta_s"], ws, Hq=Hq, stream=stream,
-                              q_amax=out.get("q_amax"))
+            out["q_amax_of"] = query_identity(q)
+            mpfa_quantize_k_nvfp4_with_q_amax(k, q, q_mean, out["k_mean"], out["k_fp4"],
+                                              out["k_sf"], out["k_gscale"], out["delta_s"],
+                                              out["q_amax"], ws, stream=stream)
+        else:
+            mpfa_quantize_k_nvfp4(k, q, q_mean, out["k_mean"], out["k_fp4"], out["k_sf"],
+                                  out["k_gscale"], out["delta_s"], ws, Hq=Hq, stream=stream)
     else:
         ws = _workspace(MPFA_OP_QUANTIZE_K, B, 0, Hkv, N, 1, dev)
         mpfa_quantize_k_nvfp4(k, None, None, None, out["k_fp4"], out["k_sf"], out["k_gscale"],
@@ -316,8 +360,10 @@ def quantize_v(v, stream=None):
 def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False, ws=None,
             out=None, lse=None, stream=None):
     """QK4PV8 prefill from the caches returned by quantize_k / quantize_v.
-    Smoothing iff kq holds delta_s.  q must be the q that quantize_k saw when
-    kq holds its q_amax (as for q_mean and delta_s).  Returns (out, lse or None)."""
+    Smoothing iff kq holds delta_s.  When kq holds the Q_c amax of the q that
+    quantize_k saw, the call takes it (mpfa_prefill_with_q_amax, no pass over
+    q); that q must be this q, unchanged since: any other q raises ValueError
+    (its global scale would be wrong).  Returns (out, lse or None)."""
     import torch
     B, Hq, N, D = q.shape
     Hkv = kq["k_fp4"].shape[1]
@@ -329,11 +375,19 @@ def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=Fals
     if ws is None:
         ws = _workspace(MPFA_OP_PREFILL, B, Hq, Hkv, N, 1, q.device)
     smooth = kq.get("delta_s") is not None
-    mpfa_prefill(q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
-                 kq["k_fp4"], kq["k_sf"], kq["k_gscale"], vq["v_fp8"], vq["v_scale"],
-                 kq.get("delta_s") if smooth else None, softmax_scale, causal, out,
-                 lse if with_lse else None, ws, stream=stream,
-                 q_amax=kq.get("q_amax") if smooth else None)
+    args = (q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
+            kq["k_fp4"], kq["k_sf"], kq["k_gscale"], vq["v_fp8"], vq["v_scale"],
+            kq.get("delta_s") if smooth else None)
+    if smooth and kq.get("q_amax") is not None:
+        ident = kq.get("q_amax_of")
+        if ident is None or not torch.equal(ident, query_identity(q)):
+            raise ValueError("kq['q_amax'] is the Q_c amax of another query tensor (or of this one "
+                             "before an in-place change): quantize_k with this q, or drop q_amax")
+        mpfa_prefill_with_q_amax(*args, kq["q_amax"], softmax_scale, causal, out,
+                                 lse if with_lse else None, ws, stream=stream)
+    else:
+        mpfa_prefill(*args, softmax_scale, causal, out, lse if with_lse else None, ws,
+                     stream=stream)
     return out, (lse if with_lse else None)
 
 

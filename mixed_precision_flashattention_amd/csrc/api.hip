@@ -111,10 +111,15 @@ const char* mpfa_status_string(int status) {
   }
 }
 
-int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
-                          const void* q, int q_dtype, int Hq, float* q_mean, float* k_mean,
-                          uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
-                          float* q_amax, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Stage one for K; q_amax (smoothing mode with q only) receives the Q_c amax.
+int quantize_k_impl(const void* k, int k_dtype, int B, int Hkv, int N, int D, const void* q,
+                    int q_dtype, int Hq, float* q_mean, float* k_mean, uint8_t* k_fp4,
+                    uint8_t* k_sf, float* k_gscale, uint16_t* delta_s, float* q_amax, void* ws,
+                    size_t ws_bytes, void* stream) {
   int st = check_sizes(B, Hkv, N, D);
   if (st) return st;
   if (!dtype_ok(k_dtype)) return MPFA_ERR_UNSUPPORTED;
@@ -167,6 +172,29 @@ int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int
                           q_ext, q_ext ? q_amax : nullptr, s);
   if (smooth) launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpfa_quantize_k_nvfp4(const void* k, int k_dtype, int B, int Hkv, int N, int D,
+                          const void* q_or_null, int q_dtype, int Hq, float* q_mean, float* k_mean,
+                          uint8_t* k_fp4, uint8_t* k_sf, float* k_gscale, uint16_t* delta_s,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return quantize_k_impl(k, k_dtype, B, Hkv, N, D, q_or_null, q_dtype, Hq, q_mean, k_mean, k_fp4,
+                         k_sf, k_gscale, delta_s, nullptr, ws, ws_bytes, stream);
+}
+
+int mpfa_quantize_k_nvfp4_with_q_amax(const void* k, int k_dtype, int B, int Hkv, int N, int D,
+                                      const void* q_or_null, int q_dtype, int Hq, float* q_mean,
+                                      float* k_mean, uint8_t* k_fp4, uint8_t* k_sf,
+                                      float* k_gscale, uint16_t* delta_s, float* q_amax, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  // the Q_c amax exists only where Q is centred by its own means
+  if (!q_or_null || !delta_s || !k_mean || !q_amax || !aligned16(q_amax)) return MPFA_ERR_INVALID;
+  return quantize_k_impl(k, k_dtype, B, Hkv, N, D, q_or_null, q_dtype, Hq, q_mean, k_mean, k_fp4,
+                         k_sf, k_gscale, delta_s, q_amax, ws, ws_bytes, stream);
 }
 
 int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp8,
@@ -260,7 +288,12 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
   return launch_status();
 }
 
-int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+}  // extern "C"
+
+namespace {
+
+// The prefill call; q_amax NULL: the Q_c amax comes from a pass over Q here.
+int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
                  const float* v_scale, const uint16_t* delta_s, const float* q_amax,
@@ -327,6 +360,34 @@ int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.n_units = n_units;
   launch_prefill(p, s);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpfa_prefill(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                 const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                 const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                 const float* v_scale, const uint16_t* delta_s, float softmax_scale, int causal,
+                 void* out, int out_dtype, float* lse_or_null, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                      v_scale, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream);
+}
+
+int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                             const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                             const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                             const float* v_scale, const uint16_t* delta_s, const float* q_amax,
+                             float softmax_scale, int causal, void* out, int out_dtype,
+                             float* lse_or_null, void* ws, size_t ws_bytes, void* stream) {
+  // the first stage derives the amax of the centred Q only
+  if (!delta_s || !q_amax || !aligned16(q_amax)) return MPFA_ERR_INVALID;
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                      v_scale, delta_s, q_amax, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream);
 }
 
 int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,

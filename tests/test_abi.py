@@ -40,6 +40,51 @@ def test_header_declares_the_four_entry_points():
         assert name in fns
 
 
+# The boundary's four calls and two helpers, argument for argument (types and
+# order) as the scope table of the build states them.
+CONTRACT = {
+    "mpfa_workspace_bytes": ("size_t", "int op, int B, int Hq, int Hkv, int N, int D, int num_splits"),
+    "mpfa_status_string": ("const char*", "int status"),
+    "mpfa_quantize_k_nvfp4": (
+        "int", "const void* k, int k_dtype, int B, int Hkv, int N, int D, const void* q_or_null, "
+        "int q_dtype, int Hq, float* q_mean, float* k_mean, uint8_t* k_fp4, uint8_t* k_sf, "
+        "float* k_gscale, uint16_t* delta_s, void* ws, size_t ws_bytes, void* stream"),
+    "mpfa_quantize_v_fp8": (
+        "int", "const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp8, "
+        "float* v_scale, void* ws, size_t ws_bytes, void* stream"),
+    "mpfa_prefill": (
+        "int", "const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D, "
+        "const float* q_mean, const float* k_mean, const uint8_t* k_fp4, const uint8_t* k_sf, "
+        "const float* k_gscale, const uint8_t* v_fp8, const float* v_scale, "
+        "const uint16_t* delta_s, float softmax_scale, int causal, void* out, int out_dtype, "
+        "float* lse_or_null, void* ws, size_t ws_bytes, void* stream"),
+    # "the same operand list" as the prefill, with N_kv and num_splits
+    "mpfa_decode": (
+        "int", "const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D, "
+        "const float* q_mean, const float* k_mean, const uint8_t* k_fp4, const uint8_t* k_sf, "
+        "const float* k_gscale, const uint8_t* v_fp8, const float* v_scale, "
+        "const uint16_t* delta_s, float softmax_scale, int num_splits, void* out, int out_dtype, "
+        "float* lse, void* ws, size_t ws_bytes, void* stream"),
+}
+
+
+def _declaration(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"([\w\s\*]+?)\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    ret = " ".join(m.group(1).split()).replace(" *", "*")
+    args = ", ".join(" ".join(a.split()).replace(" *", "*") for a in m.group(2).split(","))
+    return ret.split("\n")[-1].strip(), args
+
+
+@pytest.mark.parametrize("name", sorted(CONTRACT))
+def test_boundary_prototypes_verbatim(name):
+    ret, args = _declaration(name)
+    want_ret, want_args = CONTRACT[name]
+    assert ret.endswith(want_ret), (name, ret)
+    assert args == want_args, (name, args)
+
+
 def test_library_exports_every_declared_symbol(lib):
     import mixed_precision_flashattention_amd as mpfa
     out = subprocess.run(["nm", "-D", "--defined-only", mpfa.LIB_PATH], capture_output=True,
@@ -101,11 +146,28 @@ class _Fake:
 
 def _prefill(lib, f, **kw):
     a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
-             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, q_amax=None, scale=0.088,
-             causal=1,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, causal=1,
              out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256, stream=None)
     a.update(kw)
     return lib.mpfa_prefill(*a.values())
+
+
+def _prefill_qa(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, q_amax=f.p, scale=0.088,
+             causal=1, out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256, stream=None)
+    a.update(kw)
+    return lib.mpfa_prefill_with_q_amax(*a.values())
+
+
+def test_prefill_with_q_amax_rejects_bad_arguments(lib):
+    f = _Fake()
+    INVALID, WS = -1, -3
+    assert _prefill_qa(lib, f, q_amax=None) == INVALID
+    assert _prefill_qa(lib, f, q_amax=f.mis) == INVALID
+    assert _prefill_qa(lib, f, delta_s=None) == INVALID  # direct mode has no first-stage amax
+    assert _prefill_qa(lib, f, delta_s=None, q_mean=None, k_mean=None) == INVALID
+    assert _prefill_qa(lib, f, ws_bytes=16) == WS  # otherwise validated as mpfa_prefill
 
 
 def _decode(lib, f, **kw):
@@ -168,15 +230,22 @@ def test_decode_rejects_bad_arguments(lib):
 def test_quantizers_reject_bad_arguments(lib):
     f = _Fake()
     qk = lib.mpfa_quantize_k_nvfp4
-    # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, q_amax, ws, ws_bytes, stream)
+    # (k, k_dtype, B, Hkv, N, D, q, q_dtype, Hq, q_mean, k_mean, k_fp4, k_sf, k_gscale, delta_s, ws, ws_bytes, stream)
     # centring only (k_mean without delta_s) takes no query tensor
-    assert qk(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, None, f.p, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, f.mis, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -2
-    assert qk(f.mis, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 1 << 20, None) == -1
-    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, None, f.p, 8, None) == -3
+    assert qk(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, None, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, f.mis, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 4, None, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 3, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 3, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -2
+    assert qk(f.mis, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qk(f.p, 1, 1, 2, 64, 128, None, 0, 0, None, None, f.p, f.p, f.p, None, f.p, 8, None) == -3
+    qa = lib.mpfa_quantize_k_nvfp4_with_q_amax
+    # (... delta_s, q_amax, ws, ws_bytes, stream): smoothing with q only, q_amax required
+    assert qa(f.p, 1, 1, 2, 64, 128, None, 0, 4, f.p, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 1 << 20, None) == -1
+    assert qa(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, f.p, f.p, f.p, f.p, f.p, None, f.p, f.p, 1 << 20, None) == -1
+    assert qa(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, f.p, f.p, f.p, f.p, f.p, f.p, None, f.p, 1 << 20, None) == -1
+    assert qa(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, f.p, f.p, f.p, f.p, f.p, f.p, f.mis, f.p, 1 << 20, None) == -1
+    assert qa(f.p, 1, 1, 2, 64, 128, f.p, 1, 4, f.p, f.p, f.p, f.p, f.p, f.p, f.p, f.p, 8, None) == -3
     qv = lib.mpfa_quantize_v_fp8
     assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, 256, None) == -2
     assert qv(f.p, 1, 1, 2, 64, 128, None, f.p, f.p, 256, None) == -1

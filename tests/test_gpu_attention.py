@@ -230,8 +230,16 @@ def test_prefill_takes_the_first_stage_query_amax(mpfa, oracle_mod):
     assert kq["q_amax"].item() == want.item()
     scale = 128 ** -0.5
     out_a, lse_a = mpfa.prefill(q, kq, vq, scale, causal=True, with_lse=True)
-    kq_no = {key: val for key, val in kq.items() if key != "q_amax"}
+    kq_no = {key: val for key, val in kq.items() if key not in ("q_amax", "q_amax_of")}
     out_b, lse_b = mpfa.prefill(q, kq_no, vq, scale, causal=True, with_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b)
     assert torch.equal(lse_a, lse_b)
+    # the hand-off is tied to the q it was computed from: another q (or the
+    # same q changed in place) is refused instead of getting a wrong scale
+    q2 = q.clone()
+    with pytest.raises(ValueError):
+        mpfa.prefill(q2, kq, vq, scale, causal=True)
+    q.mul_(2.0)
+    with pytest.raises(ValueError):
+        mpfa.prefill(q, kq, vq, scale, causal=True)

@@ -61,12 +61,13 @@ def test_graph_replays_equal_eager(mpfa):
     b = _buffers(mpfa, torch, B, Hq, Hkv, N, P, dev)
 
     def calls():
-        mpfa.mpfa_quantize_k_nvfp4(k, q, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"],
-                                   b["k_gscale"], b["delta_s"], b["ws_k"], q_amax=b["q_amax"])
+        mpfa.mpfa_quantize_k_nvfp4_with_q_amax(k, q, b["q_mean"], b["k_mean"], b["k_fp4"],
+                                               b["k_sf"], b["k_gscale"], b["delta_s"], b["q_amax"],
+                                               b["ws_k"])
         mpfa.mpfa_quantize_v_fp8(v, b["v_fp8"], b["v_scale"], b["ws_v"])
-        mpfa.mpfa_prefill(q, Hkv, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"], b["k_gscale"],
-                          b["v_fp8"], b["v_scale"], b["delta_s"], cfg.scale, True, b["out"],
-                          b["lse"], b["ws_p"], q_amax=b["q_amax"])
+        mpfa.mpfa_prefill_with_q_amax(q, Hkv, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"],
+                                      b["k_gscale"], b["v_fp8"], b["v_scale"], b["delta_s"],
+                                      b["q_amax"], cfg.scale, True, b["out"], b["lse"], b["ws_p"])
         mpfa.mpfa_decode(qd, Hkv, N, b["q_mean"], b["k_mean"], b["k_fp4"], b["k_sf"],
                          b["k_gscale"], b["v_fp8"], b["v_scale"], b["delta_s"], cfg.scale, P,
                          b["dout"], b["dlse"], b["ws_d"])
