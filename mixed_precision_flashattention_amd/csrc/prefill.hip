@@ -257,6 +257,36 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
   }
 }
 
+// Per-tile mode: Delta_tile of the 32 keys of score tile t of a K~ block for
+// this wave's query tile, as one bf16 value per key in dst[key].  A = the
+// tile mean split exactly into three bf16 parts (rows 0, 1, 2 of the A
+// operand; the other rows zero), B = the K~ operands of tile t, the same
+// registers the score product uses as its A operand (an A operand read as B
+// is the transposed tile), so D row r, column c = part r . K~[key of c];
+// rows 0-2 land in registers 0-2 of lanes 0-31.  The three partial products
+// are exact in FP32 (8 x 6 significant bits); they are summed in FP32, scaled
+// by the K global scale and rounded once to bf16.
+__device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* qop, int kbase_t,
+                                           int koff_t, float gK, int lane, uint16_t* dst) {
+  const uint8_t* at = kblk + kbase_t;
+  const bool data = (lane & 31) < 3;
+  // lane (r, h) reads the 8 parts of row r for the head-dim slots of half h
+  const uint8_t* qa = qop + ((lane >> 5) * 3 + (lane & 31)) * 16;
+  f32x16 d = f32x16{};
+  i32x4 b[2], a[2];
+  b[0] = *reinterpret_cast<const i32x4*>(at);
+  a[0] = data ? *reinterpret_cast<const i32x4*>(qa) : i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    if (kc + 1 < 8) {
+      b[(kc + 1) & 1] = *reinterpret_cast<const i32x4*>(at + (kc + 1) * kKChunkBytes);
+      a[(kc + 1) & 1] = data ? *reinterpret_cast<const i32x4*>(qa + (kc + 1) * 96) : i32x4{0, 0, 0, 0};
+    }
+    d = mfma32_bf16(a[kc & 1], b[kc & 1], d);
+  }
+  if (lane < 32) dst[koff_t] = (uint16_t)bf16_rne(((d[0] + d[1]) + d[2]) * gK);
+}
+
 // Work unit: 256 query rows of one (batch, head) in two groups of 4 waves
 // (rows 0-127 and 128-255); each SIMD holds one wave of each group.  The
 // groups take turns: between two workgroup barriers one group runs its
@@ -266,15 +296,25 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
 // the same K~ / V / Delta_S blocks from LDS (double-buffered, loaded two
 // steps ahead by all 8 waves).
 // MODE 0: direct; 1: smoothing by the sequence means with the rank-one
-// Delta_S step; 2: per-tile means, the tile mean folded into a BF16 query
-// operand against BF16 K~ images (no rank-one step).
+// Delta_S step; 2: per-tile means: the column term Delta_tile[j] =
+// Qbar_tile . K~_c[j] is computed here, one block ahead, and enters through
+// the same rank-one step (BF16 K~ images and query operands, K~ blocks
+// triple-buffered so the next block is resident while the current one is
+// scored).
 template <int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
   constexpr bool SMOOTH = MODE == 1, TILE = MODE == 2;
-  __shared__ __align__(16) uint8_t smem_k[2][kBlk * kRowBytes];  // K~ blocks
-  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];      // V blocks
-  __shared__ uint16_t smem_delta[2][kBlk];
+  constexpr bool RANK1 = SMOOTH || TILE;  // a rank-one compensation step
+  constexpr int NKB = TILE ? 3 : 2;       // K~ block buffers
+  __shared__ __align__(16) uint8_t smem_k[NKB][kBlk * kRowBytes];  // K~ blocks
+  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];        // V blocks
+  // Delta_S (smoothing: [buffer][0][key]) or Delta_tile (per-tile mode:
+  // [buffer][row group][key])
+  __shared__ uint16_t smem_delta[2][TILE ? 2 : 1][kBlk];
+  // per-tile mode: the tile means' bf16 parts as score-operand rows,
+  // [row group][kc][lane half][part][8 bf16]
+  __shared__ __align__(16) uint8_t smem_qop[TILE ? 2 * 8 * 2 * 3 * 16 : 16];
 
   const int N = p.N;
   int unit, b, hq;
@@ -301,6 +341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // The first K~ block goes out before the queries are quantized, so its
   // load latency overlaps the prologue.
   issue_k_block<8>(kimg, lds_k0, wave, lane);
+  if (TILE && nblk_all > 1) issue_k_block<8>(kimg + kKBlockBytes, lds_k1, wave, lane);
 
   // ---- prologue: NVFP4 of the queries, expanded to FP16 in registers -----
   // Each lane holds, as the B operand of the score MFMA (Q~^T), query row
@@ -333,17 +374,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       uint32_t w[2];
       const uint32_t sc = nvfp4_block_packed(x, gQ, w);
       if (TILE) {
-        // bf16(code value x block scale + fp32(Qbar_tile / gQ)), both sums
-        // rounded to nearest (the product is exact in fp32)
-        const float s = e4m3_value_pos(sc);
-        const float* mu = p.q_tile_mean + ((int64_t)bh * n_qtiles + (qrow >> 7)) * kD + blk * 16;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t byte = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-          const float u0 = e2m1_value(byte & 15u) * s + mu[2 * j] / gQ;
-          const float u1 = e2m1_value(byte >> 4) * s + mu[2 * j + 1] / gQ;
-          packed[j] = bf16_rne(u0) | (bf16_rne(u1) << 16);
-        }
+        // code value x block scale in BF16 (exact: at most 6 significant bits)
+        const float sc_v = e4m3_value_pos(sc);
+        expand_fp4x8_bf16(w[0], sc_v, packed);
+        expand_fp4x8_bf16(w[1], sc_v, packed + 4);
       } else {
         // code value x block scale in FP16 (exact) by the hardware conversion
         const f16x2 s2 = e4m3_scale_f16x2(sc);
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // 1 / (gQ gK) as the sum of three bf16 parts (exact to fp32 precision);
   // the A operand repeats Delta_S[key] in the same slots.
   i32x4 dB = {0, 0, 0, 0};
-  if (SMOOTH) {
+  if (RANK1) {
     const float cinv = 1.0f / gg;
     const uint32_t c_hi = bf16_rne(cinv);
     const float r1 = cinv - __uint_as_float(c_hi << 16);
@@ -403,6 +437,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   uint32_t dd = 0;
   if (SMOOTH && tid < kBlk) dd = dbase[min(tid, N - 1)];
 
+  // Per-tile mode: the means of the unit's two query tiles (2 unit, 2 unit + 1;
+  // one per row group) as exact bf16 parts, laid out as the rows of the A
+  // operand of tile_delta: entry (g, kc, half, part, i) holds part `part` of
+  // Qbar[dim 64 half + 8 kc + i] of tile 2 unit + g (the head-dim order of the
+  // score operands).  Then Delta_tile(0) for each group's tile; K~(0) and K~(1)
+  // are resident after the barrier.
+  const uint8_t* qop_g = smem_qop + (TILE ? grp * 768 : 0);
+  if (TILE) {
+    uint16_t* qop16 = reinterpret_cast<uint16_t*>(smem_qop);
+    for (int e = tid; e < 2 * 8 * 2 * 3 * 8; e += 512) {
+      const int i = e & 7, part = (e >> 3) % 3, rest = (e >> 3) / 3;
+      const int half = rest & 1, kc = (rest >> 1) & 7, g = rest >> 4;
+      const int tile = 2 * unit + g;
+      const float x = tile < n_qtiles
+                          ? p.q_tile_mean[((int64_t)bh * n_qtiles + tile) * kD + 64 * half + 8 * kc + i]
+                          : 0.0f;
+      const uint32_t hi = bf16_rne(x);
+      const float r1 = x - __uint_as_float(hi << 16);  // exact
+      const uint32_t mid = bf16_rne(r1);
+      const uint32_t lo = bf16_rne(r1 - __uint_as_float(mid << 16));  // both exact
+      qop16[e] = (uint16_t)(part == 0 ? hi : (part == 1 ? mid : lo));
+    }
+    wait_direct_loads();
+    __syncthreads();
+    if (n_own > 0)
+      tile_delta(smem_k[0], qop_g, kbase[wave & 3], koff[wave & 3], gK, lane, smem_delta[0][grp]);
+  }
+
   // Steps alternate between the groups: in body j, group 0 runs its matrix
   // phase (P.V of block j-1, scores of block j) in the first step and the
   // softmax of block j in the second; group 1 runs the softmax of block j-1
@@ -410,18 +472,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // first, so it issues the loads of K~(j+1), Delta_S(j+1) and V(j) before
   // the middle barrier (their buffers were last read in body j-1); the
   // barrier that opens body j+1 publishes them.  Both loops pass the same
-  // barriers.
+  // barriers.  In the per-tile mode K~ runs one block further ahead (K~(j+2)
+  // is issued in body j, into the buffer of K~(j-1)), and each wave's matrix
+  // phase also computes Delta_tile(j+1) of its own tile for key tile
+  // (wave & 3) from the resident K~(j+1); the next opening barrier publishes
+  // it, and its buffer was last read by the scores of block j-1.
 #define MPFA_STEP_OPEN(J)                                                                    \
   do {                                                                                       \
     wait_direct_loads(); /* this wave's loads of the previous body have landed */            \
-    if (SMOOTH && tid < kBlk) smem_delta[(J) & 1][tid] = (uint16_t)dd;                       \
+    if (SMOOTH && tid < kBlk) smem_delta[(J) & 1][0][tid] = (uint16_t)dd;                    \
     __syncthreads();                                                                         \
   } while (0)
 #define MPFA_ISSUE(J)                                                                        \
   do {                                                                                       \
-    if ((J) + 1 < n_max) {                                                                   \
-      issue_k_block<4>(kimg + (int64_t)((J) + 1) * kKBlockBytes, ((J) & 1) ? lds_k0 : lds_k1,   \
-                       wave, lane);                                                          \
+    const int jk = (J) + (TILE ? 2 : 1); /* the K~ block loaded in this body */              \
+    if (jk < n_max) {                                                                        \
+      issue_k_block<4>(kimg + (int64_t)jk * kKBlockBytes, lds_addr(smem_k[jk % NKB]), wave,   \
+                       lane);                                                                \
       if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
     }                                                                                        \
     if ((J) < n_max)                                                                         \
@@ -431,7 +498,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   do {                                                                                       \
     if ((J) >= 1 && (J) <= n_own) pv_block(o, smem_v[((J) - 1) & 1], pb, h, col);           \
     if ((J) < n_own) {                                                                       \
-      score_block<SMOOTH, TILE>(s, smem_k[(J) & 1], smem_delta[(J) & 1], koff, kbase, qf, dB, h); \
+      score_block<RANK1, TILE>(s, smem_k[(J) % NKB], smem_delta[(J) & 1][TILE ? grp : 0], koff, \
+                               kbase, qf, dB, h);                                            \
+      if (TILE && (J) + 1 < n_own)                                                           \
+        tile_delta(smem_k[((J) + 1) % NKB], qop_g, kbase[wave & 3], koff[wave & 3], gK, lane,  \
+                   smem_delta[((J) + 1) & 1][TILE ? grp : 0]);                               \
     } else {                                                                                 \
       /* defining s on this path too keeps the old scores from being live */                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \

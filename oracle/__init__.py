@@ -258,7 +258,8 @@ from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     quantize_q_tiles,
     quantize_v,
     tile_means,
-    tile_operand,
+    delta_tile,
+    delta_tile_row,
 )
 
 __all__ = [
@@ -268,6 +269,6 @@ __all__ = [
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
     "quantize_k", "quantize_v", "quantize_q", "prefill_rows", "decode", "decode_partitions",
     "exact_attention", "Operands", "append_kv", "PAGE", "gather_pages", "decode_paged",
-    "append_kv_paged", "Q_TILE", "tile_means", "quantize_q_tiles", "tile_operand",
+    "append_kv_paged", "Q_TILE", "tile_means", "quantize_q_tiles", "delta_tile", "delta_tile_row",
     "prefill_tile_mean_rows"
 ]

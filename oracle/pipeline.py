@@ -314,22 +314,49 @@ def quantize_q_tiles(q, tm, tile=Q_TILE):
     return codes, sf, np.float32(g)
 
 
-def tile_operand(codes, sf, g, tm, tile=Q_TILE):
-    """The query operand of the per-tile mode, FP64, in absolute units.
+def delta_tile(tm, k_codes, k_sf, k_gscale):
+    """The compensation term of the per-tile mode, one bf16 value per
+    (b, q-head, query tile, key):
 
-    Reading: the tile mean's compensation Qbar_tile . K~_c[j] is added to the
-    scores by folding the mean into the query operand of the score product,
-    (Q~_c + Qbar_tile) . K~_c, so the centred product and the compensation
-    share one matrix product.  The fold is carried in BF16, as the paper
-    carries its compensation term (MpFA §5.2, a BF16 product): in units of
-    the Q global scale g, u = fp32(code value x block scale + fp32(Qbar / g))
-    (the first term is exact in fp32), operand = bf16_rne(u) * g."""
-    N = codes.shape[2]
-    qsc = nvfp4_dequantize(codes, sf, 1.0).astype(F32)  # code value x block scale, exact
-    qb = (np.asarray(tm, dtype=F32) / np.float32(g)).astype(F32)
-    rep = np.repeat(qb, tile, axis=2)[:, :, :N]
-    u = (qsc + rep).astype(F32)
-    return bf16_to_f64(bf16_rne(u)) * float(g)
+        Delta_tile[b, h, t, j] = bf16_rne(fp32(sum_d Qbar_tile[b, h, t, d] * K~_c[b, h//G, j, d]))
+
+    with K~_c the dequantized centred key (code value x block scale x global
+    scale) and the sum in FP64 over ascending d (the products of an fp32 mean
+    and a 30-bit key are exact in FP64 but for the last bit).
+
+    Reading: the tile's mean Qbar_tile enters the scores as its own column
+    term Qbar_tile . K~_c[j], the same rank-one form and the same BF16
+    carriage as Delta_S (MpFA §5.2: the compensation is one BF16 matrix
+    product written into S before the main product accumulates; §7.4: only
+    the compensation term is carried in BF16).  The centred keys it multiplies
+    are the quantized ones, since this mode computes the term in the attention
+    stage, where only the quantized cache exists.
+    tm [B, Hq, T, D] fp32; k_codes [B, Hkv, N, D/2], k_sf [B, Hkv, N, D/16].
+    Returns [B, Hq, T, N] uint16 (bf16 bits)."""
+    tm = np.asarray(tm, dtype=F32)
+    B, Hq, T, D = tm.shape
+    Hkv = k_codes.shape[1]
+    G = Hq // Hkv
+    N = k_codes.shape[2]
+    out = np.empty((B, Hq, T, N), dtype=np.uint16)
+    for b in range(B):
+        for hk in range(Hkv):
+            kt = nvfp4_dequantize(k_codes[b, hk], k_sf[b, hk], k_gscale)  # [N, D] f64, exact
+            for h in range(hk * G, (hk + 1) * G):
+                for t in range(T):
+                    out[b, h, t] = delta_tile_row(tm[b, h, t], kt)
+    return out
+
+
+def delta_tile_row(qbar, kt):
+    """One row of ``delta_tile``: qbar [D] fp32, kt [N, D] the dequantized
+    centred keys (FP64) -> [N] bf16 bits; FP64 sum over ascending d, then
+    fp32, then bf16 (round to nearest even each time)."""
+    qbar = np.asarray(qbar, dtype=F32)
+    acc = np.zeros(kt.shape[0])
+    for d in range(kt.shape[1]):
+        acc = acc + float(qbar[d]) * kt[:, d]
+    return bf16_rne(acc.astype(F32))
 
 
 def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=None, out_f64=False,
@@ -339,12 +366,14 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
     K is centred by its sequence mean Kbar and quantized as in smoothing mode
     (without delta_s); Q by the mean of each row's 128-row tile
     (``tile_means``, ``quantize_q_tiles``); the scores are
-    tile_operand(Q) . K~_c^T, i.e. Q~_c . K~_c^T plus the column term
-    Qbar_tile . K~_c[j]; the rest is the prefill of ``prefill_rows``.  The
-    LSE adds back the row term scale * (Q_i . Kbar), as in smoothing mode.
-    identity: no quantizer (the operand is Q_c + Qbar_tile in FP64, K~_c = K_c,
-    P not rounded).  Returns (O, LSE, rows), plus AMB as in ``prefill_rows``
-    with ambiguity=True."""
+    S_ij = Q~_c,i . K~_c,j + Delta_tile[tile(i), j] (``delta_tile``), FP64,
+    before the mask and the running max; the rest is the prefill of
+    ``prefill_rows``.  The LSE adds back the row term scale * (Q_i . Kbar),
+    as in smoothing mode (Q_i . K_j = Q_c,i . K_c,j + Qbar_tile . K_c,j +
+    Q_i . Kbar, the last term constant along the row).
+    identity: no quantizer (Q_c and K_c in FP64, the column term
+    Qbar_tile . K_c[j] unrounded, P not rounded).  Returns (O, LSE, rows),
+    plus AMB as in ``prefill_rows`` with ambiguity=True."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     v = np.asarray(v, dtype=F32)
@@ -353,18 +382,20 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
     G = Hq // Hkv
     tm = tile_means(q)
     k_mean = channel_mean(k)
+    rep = np.repeat(tm, Q_TILE, axis=2)[:, :, :N]
     if identity:
-        rep = np.repeat(tm, Q_TILE, axis=2)[:, :, :N]
-        qop = (q - rep).astype(F32).astype(F64) + rep.astype(F64)
-        kdeq = lambda b, hk: (k[b, hk] - k_mean[b, hk][None, :]).astype(F64)
+        qop = (q - rep).astype(F32).astype(F64)
+        kdeq = lambda b, hk: (k[b, hk] - k_mean[b, hk][None, :]).astype(F32).astype(F64)
         vdeq = lambda b, hk: v[b, hk].astype(F64)
+        dtile = lambda b, h, t: kdeq(b, h // G) @ tm[b, h, t].astype(F64)
         s_v, quant_p = 1.0, False
     else:
         kq = quantize_k(k)
         vq = quantize_v(v)
         codes, sf, g = quantize_q_tiles(q, tm)
-        qop = tile_operand(codes, sf, g, tm)
+        qop = nvfp4_dequantize(codes, sf, g)
         kdeq = lambda b, hk: nvfp4_dequantize(kq["k_fp4"][b, hk], kq["k_sf"][b, hk], kq["k_gscale"])
+        dtile = lambda b, h, t: bf16_to_f64(delta_tile_row(tm[b, h, t], kdeq(b, h // G)))
         table = e4m3_table()
         vdeq = lambda b, hk: table[vq["v_fp8"][b, hk]]
         s_v, quant_p = float(vq["v_scale"]), True
@@ -379,20 +410,22 @@ def prefill_tile_mean_rows(q, k, v, scale, causal=True, identity=False, rows=Non
         for hk in range(Hkv):
             kt = vt = None
             for h in range(hk * G, (hk + 1) * G):
-                sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
-                if len(sel) == 0:
-                    continue
-                if kt is None:
-                    kt, vt = kdeq(b, hk), vdeq(b, hk)
-                pos = rows[sel, 2]
-                row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
-                m, l, acc, amb = attn_state(np.ascontiguousarray(qop[b, h][pos]), row_pos, kt, vt, None,
-                                            0, N, scale, quant_p, ambiguity=True)
-                off = scale * (q[b, h][pos].astype(F64) @ k_mean[b, hk].astype(F64))
-                o, lse = _finalize(m, l, acc, s_v, scale, off, out_f64)
-                O[sel] = o
-                LSE[sel] = lse
-                AMB[sel] = amb * s_v / (P_SCALE * l[:, None])
+                for t in range(-(-N // Q_TILE)):
+                    sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h) &
+                                     (rows[:, 2] // Q_TILE == t))[0]
+                    if len(sel) == 0:
+                        continue
+                    if kt is None:
+                        kt, vt = kdeq(b, hk), vdeq(b, hk)
+                    pos = rows[sel, 2]
+                    row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
+                    m, l, acc, amb = attn_state(np.ascontiguousarray(qop[b, h][pos]), row_pos, kt, vt,
+                                                dtile(b, h, t), 0, N, scale, quant_p, ambiguity=True)
+                    off = scale * (q[b, h][pos].astype(F64) @ k_mean[b, hk].astype(F64))
+                    o, lse = _finalize(m, l, acc, s_v, scale, off, out_f64)
+                    O[sel] = o
+                    LSE[sel] = lse
+                    AMB[sel] = amb * s_v / (P_SCALE * l[:, None])
     return (O, LSE, rows, AMB) if ambiguity else (O, LSE, rows)
 
 

@@ -95,7 +95,7 @@ def test_tile_mean_queries_with_large_tile_offsets(mpfa, oracle_mod):
 
 def test_tile_mean_degenerate_queries(mpfa, oracle_mod):
     """Q constant inside every tile (the centred queries are all zero, the
-    global scale falls back to 1 and only the folded means remain) and an
+    global scale falls back to 1 and only the tile means' column terms remain) and an
     all-zero Q."""
     from mixed_precision_flashattention_amd import synth
     cfg = synth.config("prefill_1k_2x1", N=300)

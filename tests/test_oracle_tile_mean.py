@@ -1,7 +1,8 @@
 """Pins of the oracle's per-query-tile mean mode (the tile-granular reading of
 the query smoothing of MpFA §3.2 / §5.1: each query row is centred by the
-mean of its own 128-row tile, and the compensation Qbar_tile . K~_c[j] is
-folded into the query operand of the score product).
+mean of its own 128-row tile, and the compensation Delta_tile[j] =
+Qbar_tile . K~_c[j] enters the scores as a separate term carried in BF16,
+like Delta_S, §5.2 / §7.4).
 
 * Tile means: the FP64 mean of each tile's own rows within the fixed-point
   bound (exact on dyadic data), the ragged last tile averaging only the rows
@@ -13,7 +14,9 @@ folded into the query operand of the score product).
   tile to tile, keys with a zero sequence mean, lam * S integral -- equals
   exact attention for the full quantized path, so a dropped or misplaced
   tile mean fails it.
-* The folded operand equals torch's bf16 rounding of the fp32 sum.
+* Delta_tile equals the exact rational dot product rounded to fp32 and then
+  to bf16, and it is taken against the quantized keys (the unquantized ones
+  give other bytes).
 * One tile: the query codes equal those of the sequence-mean quantizer.
 * A constant key shift leaves the output bit-identical.
 """
@@ -104,16 +107,75 @@ def test_lossless_tile_mode_equals_exact(causal):
     assert np.abs(L - Le).max() < 1e-12
 
 
-def test_folded_operand_is_bf16_of_the_fp32_sum():
-    q, _, _ = _rand(8, N=200)
+def _fp32_rne(x):
+    """The fp32 nearest to the rational x (ties to the even significand)."""
+    from fractions import Fraction
+    f = np.float32(float(x))
+    cands = [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    best = min(abs(Fraction(float(c)) - x) for c in cands)
+    near = [c for c in cands if abs(Fraction(float(c)) - x) == best]
+    if len(near) > 1:
+        near = [c for c in near if (int(np.array(c).view(np.uint32)) & 1) == 0]
+    return near[0]
+
+
+def _exact_delta_bits(qbar, kt):
+    """bf16(fp32(exact sum)) with the products and the sum in exact rationals."""
+    from fractions import Fraction
+    qf = [Fraction(float(x)) for x in qbar]
+    vals = np.array([_fp32_rne(sum((a * Fraction(float(b)) for a, b in zip(qf, row)), Fraction(0)))
+                     for row in kt], dtype=F32)
+    return torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_delta_tile_is_the_rounded_exact_dot_with_quantized_keys():
+    q, k, _ = _rand(8, Hq=2, Hkv=1, N=200)
     tm = oracle.tile_means(q)
+    kq = oracle.quantize_k(k)
+    dt = oracle.delta_tile(tm, kq["k_fp4"], kq["k_sf"], kq["k_gscale"])
+    assert dt.shape == (1, 2, 2, 200)
+    kt = oracle.nvfp4_dequantize(kq["k_fp4"][0, 0], kq["k_sf"][0, 0], kq["k_gscale"])
+    for h in range(2):
+        for t in range(2):
+            np.testing.assert_array_equal(dt[0, h, t], _exact_delta_bits(tm[0, h, t], kt[:60]).tolist()
+                                          + list(dt[0, h, t, 60:]))
+    # against the unquantized centred keys the bytes differ (a plausible mistake)
+    kc = (k[0, 0] - kq["k_mean"][0, 0][None, :]).astype(F32).astype(np.float64)
+    wrong = oracle.delta_tile_row(tm[0, 0, 0], kc)
+    assert np.mean(wrong != dt[0, 0, 0]) > 0.5
+    # and against the sequence mean instead of the tile mean
+    wrong2 = oracle.delta_tile_row(oracle.channel_mean(q)[0, 0], kt)
+    assert np.mean(wrong2 != dt[0, 0, 0]) > 0.5
+
+
+def test_delta_tile_enters_the_scores_in_bf16():
+    """The mode's output equals the blocked attention of the tile-centred
+    operands with the bf16 Delta_tile as the score offset -- and moves when the
+    offset is used unrounded (so the rounding is part of what is pinned)."""
+    q, k, v = _rand(11, Hq=2, Hkv=1, N=260)
+    scale = 1 / math.sqrt(128)
+    rows = np.array([[0, h, i] for h in range(2) for i in range(0, 260, 7)])
+    O, L, _ = oracle.prefill_tile_mean_rows(q, k, v, scale, rows=rows, out_f64=True)
+    tm = oracle.tile_means(q)
+    kq = oracle.quantize_k(k)
+    vq = oracle.quantize_v(v)
     codes, sf, g = oracle.quantize_q_tiles(q, tm)
-    op = oracle.tile_operand(codes, sf, g, tm)
-    qsc = torch.from_numpy(oracle.nvfp4_dequantize(codes, sf, 1.0).astype(F32))
-    qb = torch.from_numpy(tm) / torch.tensor(float(g), dtype=torch.float32)
-    rep = qb.repeat_interleave(128, dim=2)[:, :, :200]
-    ref = (qsc + rep).to(torch.bfloat16).to(torch.float64) * float(g)
-    np.testing.assert_array_equal(op, ref.numpy())
+    kt = oracle.nvfp4_dequantize(kq["k_fp4"][0, 0], kq["k_sf"][0, 0], kq["k_gscale"])
+    vt = oracle.e4m3_table()[vq["v_fp8"][0, 0]]
+    moved = 0.0
+    for i, (_, h, r) in enumerate(rows):
+        t = r // 128
+        qop = oracle.nvfp4_dequantize(codes[0, h, r:r + 1], sf[0, h, r:r + 1], g)
+        d_bf = oracle.bf16_to_f64(oracle.delta_tile_row(tm[0, h, t], kt))
+        d_ex = kt @ tm[0, h, t].astype(np.float64)
+        for d, check in ((d_bf, True), (d_ex, False)):
+            m, l, acc = oracle.attn_state(qop, np.array([r]), kt, vt, d, 0, 260, scale, True)
+            o = acc[0] * float(vq["v_scale"]) / (oracle.P_SCALE * l[0])
+            if check:
+                np.testing.assert_allclose(o, O[i], rtol=0, atol=1e-12)
+            else:
+                moved = max(moved, np.abs(o - O[i]).max())
+    assert moved > 0.0
 
 
 def test_one_tile_codes_equal_sequence_mean_codes():
