@@ -65,8 +65,8 @@ def lib() -> ctypes.CDLL:
             "oracle_fp8_scale": (f32, [f32]),
             "oracle_fp8_quantize": (None, [P, i64, f32, P]),
             "oracle_delta_s": (None, [P, P, i64, i32, P]),
-            "oracle_attn_state": (None, [i32, i32, P, P, P, P, P, i64, i64, i32, f64, i32, P, P, P,
-                                         P]),
+            "oracle_attn_state": (None, [i32, i32, P, P, P, P, P, i64, i64, i32, f64, i32, f64, P,
+                                         P, P, P]),
             "oracle_merge_states": (None, [i32, i32, i32, P, P, P, f64, P, P, P]),
             "oracle_e4m3_encode_array": (None, [P, i64, P]),
             "oracle_e2m1_encode_array": (None, [P, i64, P]),
@@ -200,15 +200,23 @@ def delta_s(qmean: np.ndarray, kc: np.ndarray) -> np.ndarray:
     return out
 
 
+P_FORMATS = {"none": 0, "e4m3": 1, "bf16": 2}
+AMB_REL = 2.0 ** -16  # how close to a rounding midpoint an FP32 exp2 cannot decide
+
+
 def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, block=KV_BLOCK,
-               ambiguity=False):
+               ambiguity=False, p_format=None, amb_rel=AMB_REL):
     """Blocked online-softmax state of R rows over keys [kv_begin, kv_end).
 
     q [R, D] f64; row_pos [R] int64 (-1: every key visible); k, v [Nk, D] f64;
-    delta [Nk] f64 or None.  Returns (m [R], l [R], acc [R, D]) in FP64, and
-    with ambiguity=True also amb [R, D]: how far acc may move if the keys
-    whose 448 p sits within 2^-16 of an E4M3 rounding midpoint round the
-    other way (both roundings are correct for a p computed in FP32)."""
+    delta [Nk] f64 or None.  P is rounded as p_format says ("e4m3": the
+    method's FP8 P with its fixed scale 448; "bf16": bf16 of 448 p, the BF16
+    P.V assignment; "none": not rounded); by default quant_p picks "e4m3" or
+    "none".  Returns (m [R], l [R], acc [R, D]) in FP64, and with
+    ambiguity=True also amb [R, D]: how far acc may move if the keys whose
+    448 p sits within amb_rel (relative) of a rounding midpoint round the
+    other way (both roundings are correct for a p computed in FP32, or with
+    the relative error amb_rel)."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
@@ -222,8 +230,9 @@ def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, b
     if delta is not None:
         delta = np.ascontiguousarray(delta, dtype=np.float64)
         dp = _p(delta)
+    fmt = P_FORMATS[p_format] if p_format is not None else (1 if quant_p else 0)
     lib().oracle_attn_state(D, R, _p(q), _p(rp), _p(k), _p(v), dp, int(kv_begin), int(kv_end),
-                            int(block), float(scale), int(bool(quant_p)), _p(m), _p(l), _p(acc),
+                            int(block), float(scale), fmt, float(amb_rel), _p(m), _p(l), _p(acc),
                             _p(amb) if ambiguity else None)
     return (m, l, acc, amb) if ambiguity else (m, l, acc)
 
@@ -257,6 +266,7 @@ from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     quantize_q,
     quantize_q_tiles,
     quantize_v,
+    quantize_v_bf16,
     tile_means,
     delta_tile,
     delta_tile_row,
@@ -265,9 +275,9 @@ from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
 __all__ = [
     "build", "lib", "KV_BLOCK", "P_SCALE",
     "e2m1_decode", "e4m3_decode", "e2m1_table", "e4m3_table", "e2m1_encode", "e4m3_encode",
-    "bf16_rne", "bf16_to_f64", "channel_mean", "amax", "nvfp4_global_scale", "nvfp4_quantize",
+    "bf16_rne", "bf16_to_f64", "P_FORMATS", "AMB_REL", "channel_mean", "amax", "nvfp4_global_scale", "nvfp4_quantize",
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
-    "quantize_k", "quantize_v", "quantize_q", "prefill_rows", "decode", "decode_partitions",
+    "quantize_k", "quantize_v", "quantize_v_bf16", "quantize_q", "prefill_rows", "decode", "decode_partitions",
     "exact_attention", "Operands", "append_kv", "PAGE", "gather_pages", "decode_paged",
     "append_kv_paged", "Q_TILE", "tile_means", "quantize_q_tiles", "delta_tile", "delta_tile_row",
     "prefill_tile_mean_rows"

@@ -273,10 +273,10 @@ void oracle_delta_s(const float* qmean, const float* kc, int64_t T, int D, uint1
  * no key.  q is [R][D], k and v are [*][D] indexed by absolute key, delta is
  * indexed by absolute key or NULL.                                          */
 /* The other E4M3 magnitude a value a >= 0 may round to when it lies within
- * 2^-16 (relative) of the midpoint between two neighbouring magnitudes --
- * closer than an FP32 computation of p can place it -- else the rounded
- * value ph itself.                                                          */
-static double e4m3_alternative(double a, double ph) {
+ * `rel` (relative) of the midpoint between two neighbouring magnitudes --
+ * closer than the kernel's own computation of p can place it -- else the
+ * rounded value ph itself.                                                  */
+static double e4m3_alternative(double a, double ph, double rel) {
   int lo = 0, hi = 126;
   double mid;
   if (a >= g_e4m3_mag[126] || a <= 0.0) return ph;
@@ -285,18 +285,49 @@ static double e4m3_alternative(double a, double ph) {
     if (g_e4m3_mag[m] <= a) lo = m; else hi = m;
   }
   mid = 0.5 * (g_e4m3_mag[lo] + g_e4m3_mag[hi]);
-  if (fabs(a - mid) > ldexp(a, -16)) return ph;
+  if (fabs(a - mid) > rel * a) return ph;
   return ph == g_e4m3_mag[lo] ? g_e4m3_mag[hi] : g_e4m3_mag[lo];
 }
 
+/* Nearest bf16 value (8 significant bits) to a >= 0, ties to the even
+ * significand, from the FP64 value directly (one rounding).  Normal bf16
+ * range only: the P values it rounds (448 p) are 0 or above 2^-120 wherever
+ * they can matter.                                                          */
+static double bf16_round_pos(double a) {
+  int e;
+  if (a <= 0.0) return 0.0;
+  frexp(a, &e);
+  return ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);
+}
+
+/* The other bf16 neighbour of a >= 0 when a lies within `rel` of the midpoint
+ * between its two bf16 neighbours, else ph.                                 */
+static double bf16_alternative(double a, double ph, double rel) {
+  int e;
+  double lo, hi, mid;
+  if (a <= 0.0) return ph;
+  frexp(a, &e);
+  lo = ldexp(floor(ldexp(a, 8 - e)), e - 8);
+  hi = lo + ldexp(1.0, e - 8);
+  mid = 0.5 * (lo + hi);
+  if (fabs(a - mid) > rel * a) return ph;
+  return ph == lo ? hi : lo;
+}
+
 /* out_amb (NULL or [R][D]): alongside acc, the sum over keys whose 448 p is
- * that close to an E4M3 rounding midpoint of |other rounding - p^| * |v|,
- * rescaled with acc -- the most a different (equally valid) rounding of
- * those keys can move acc.  It does not change m, l or acc.                 */
+ * that close to a rounding midpoint of its P format of
+ * |other rounding - p^| * |v|, rescaled with acc -- the most a different
+ * (equally valid) rounding of those keys can move acc.  It does not change
+ * m, l or acc.
+ * p_format: 0 = P not rounded (p^ = 448 p), 1 = E4M3 of 448 p (the method's
+ * FP8 P), 2 = bf16 of 448 p (the BF16 P.V precision assignment).
+ * amb_rel: the relative distance to a midpoint below which both roundings
+ * count as valid (2^-16 for an FP32 exp2; wider for an approximate one).    */
 void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
                        const double* k, const double* v, const double* delta,
-                       int64_t kv_begin, int64_t kv_end, int block, double scale, int quant_p,
-                       double* out_m, double* out_l, double* out_acc, double* out_amb) {
+                       int64_t kv_begin, int64_t kv_end, int block, double scale, int p_format,
+                       double amb_rel, double* out_m, double* out_l, double* out_acc,
+                       double* out_amb) {
   const double lam = scale / log(2.0);
   int r;
   init_tables();
@@ -333,14 +364,18 @@ void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
         for (d = 0; d < D; ++d) amb[d] *= alpha;
       for (j = b0; j < last; ++j) {
         double p = exp2(lam * (s[j - b0] - mn));
-        double ph = quant_p ? oracle_e4m3_decode(oracle_e4m3_encode(448.0 * p)) : 448.0 * p;
+        double ph = 448.0 * p, alt = ph;
+        if (p_format == 1) {
+          ph = oracle_e4m3_decode(oracle_e4m3_encode(448.0 * p));
+          alt = e4m3_alternative(448.0 * p, ph, amb_rel);
+        } else if (p_format == 2) {
+          ph = bf16_round_pos(448.0 * p);
+          alt = bf16_alternative(448.0 * p, ph, amb_rel);
+        }
         l += p;
         for (d = 0; d < D; ++d) acc[d] += ph * v[j * D + d];
-        if (amb && quant_p) {
-          double alt = e4m3_alternative(448.0 * p, ph);
-          if (alt != ph)
-            for (d = 0; d < D; ++d) amb[d] += fabs(alt - ph) * fabs(v[j * D + d]);
-        }
+        if (amb && alt != ph)
+          for (d = 0; d < D; ++d) amb[d] += fabs(alt - ph) * fabs(v[j * D + d]);
       }
       m = mn;
     }

@@ -69,6 +69,13 @@ def quantize_v(v):
     return {"v_fp8": fp8_quantize(v, s), "v_scale": np.float32(s)}
 
 
+def quantize_v_bf16(v):
+    """V rounded to bf16 (nearest even), the V operand of the BF16 P.V
+    precision assignment (MpFA §3.1, Fig. 3(a): NVFP4 Q.K^T with BF16 P.V).
+    Returns bf16 bits [..., D] (uint16)."""
+    return bf16_rne(np.asarray(v, dtype=F32))
+
+
 def quantize_q(q, q_mean=None):
     """NVFP4 of Q_c = fp32(Q - Qbar) (direct mode: Q_c = Q), global scale from the
     amax of the whole Q_c tensor of the call.  Returns (codes, scales, g)."""
@@ -141,7 +148,10 @@ class Operands:
     k_mean (smooth) and the per-head accessors q(b, h, pos), k(b, hk),
     v(b, hk), delta(b, h) (None in direct mode)."""
 
-    def __init__(self, q, k, v, scale, smooth, identity, q_mean=None):
+    def __init__(self, q, k, v, scale, smooth, identity, q_mean=None, pv="fp8"):
+        """pv: the P.V precision: "fp8" (the method: E4M3 P with the fixed
+        scale 448, FP8 V with a per-tensor scale) or "bf16" (P rounded to
+        bf16, V in bf16: the NVFP4 + BF16 assignment of MpFA §3.1)."""
         q = np.asarray(q, dtype=F32)
         k = np.asarray(k, dtype=F32)
         v = np.asarray(v, dtype=F32)
@@ -154,6 +164,8 @@ class Operands:
         self._q, self._k, self._v = q, k, v
         self.k_mean = None
         self._delta = None
+        self.pv = pv
+        self.p_format = "none" if identity else ("bf16" if pv == "bf16" else "e4m3")
         if identity:
             if smooth:
                 self.k_mean = channel_mean(k)
@@ -170,10 +182,14 @@ class Operands:
         else:
             kq = quantize_k(k, smooth=False)
             qcodes, qsf, gq = quantize_q(q, None)
-        vq = quantize_v(v)
+        if pv == "bf16":
+            vq = {"v_bf16": quantize_v_bf16(v)}
+            self.s_v = 1.0
+        else:
+            vq = quantize_v(v)
+            self.s_v = float(vq["v_scale"])
         self.kq, self.vq = kq, vq
         self.q_codes, self.q_sf, self.q_gscale = qcodes, qsf, gq
-        self.s_v = float(vq["v_scale"])
         self.quant_p = True
         self._table = e4m3_table()
 
@@ -204,6 +220,7 @@ class Operands:
             self.q_codes, self.q_sf, self.q_gscale = quantize_q(q, None)
         self.s_v = float(self.vq["v_scale"])
         self.quant_p = True
+        self.pv, self.p_format = "fp8", "e4m3"
         self._table = e4m3_table()
         return self
 
@@ -222,6 +239,8 @@ class Operands:
     def v(self, b, hk):
         if self.identity:
             return self._v[b, hk].astype(F64)
+        if self.pv == "bf16":
+            return bf16_to_f64(self.vq["v_bf16"][b, hk])
         return self._table[self.vq["v_fp8"][b, hk]]
 
     def delta(self, b, h):
@@ -235,8 +254,12 @@ class Operands:
 
 
 def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=None, out_f64=False,
-                 ops=None, ambiguity=False):
+                 ops=None, ambiguity=False, pv="fp8", amb_rel=None):
     """Causal (or full) prefill, MpFA §5.1 second stage, for the selected rows.
+
+    pv="bf16" gives the NVFP4 + BF16 precision assignment (P and V in bf16,
+    MpFA §3.1) instead of the method's FP8 P.V.  amb_rel: the width of the
+    rounding-ambiguity window of AMB (default: an FP32 exp2's, 2^-16).
 
     rows: None (every row) or an int array [R, 3] of (b, q-head, position).
     ops: an Operands already built from the same q, k, v and mode (else built here).
@@ -248,8 +271,9 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
     q = np.asarray(q, dtype=F32)
     B, Hq, N, D = q.shape
     if ops is None:
-        ops = Operands(q, k, v, scale, smooth, identity)
+        ops = Operands(q, k, v, scale, smooth, identity, pv=pv)
     G = ops.G
+    amb_kw = {} if amb_rel is None else {"amb_rel": amb_rel}
     if rows is None:
         bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
         rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
@@ -269,7 +293,8 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
                 pos = rows[sel, 2]
                 row_pos = pos if causal else np.full(len(sel), -1, dtype=np.int64)
                 m, l, acc, amb = attn_state(ops.q(b, h, pos), row_pos, kt, vt, ops.delta(b, h), 0, N,
-                                            scale, ops.quant_p, ambiguity=True)
+                                            scale, ops.quant_p, ambiguity=True,
+                                            p_format=ops.p_format, **amb_kw)
                 off = None
                 if smooth:
                     off = scale * (q[b, h][pos].astype(F64) @ ops.k_mean[b, hk].astype(F64))

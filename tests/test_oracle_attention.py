@@ -7,6 +7,7 @@ Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels on Blackwell GPUs":
 import math
 
 import numpy as np
+import torch
 import pytest
 
 
@@ -93,10 +94,15 @@ LOSSLESS_SCALE = LAM * math.log(2.0)
 
 
 @pytest.mark.parametrize("causal", [True, False])
-def test_lossless_prefill_equals_exact(oracle_mod, causal):
+@pytest.mark.parametrize("pv", ["fp8", "bf16"])
+def test_lossless_prefill_equals_exact(oracle_mod, causal, pv):
+    """Operands on the grids and lam * S integral: p = 2^-n is exact in E4M3
+    and in bf16 (448 p too: 448 = 7 * 2^6), and V on the E4M3 grid is on the
+    bf16 grid, so both P.V precision assignments equal exact attention."""
     rng = np.random.default_rng(12)
     q, k, v = _lossless_inputs(rng, 1, 2, 1, 384)
-    O, L, rows = oracle_mod.prefill_rows(q, k, v, LOSSLESS_SCALE, causal=causal, smooth=False, out_f64=True)
+    O, L, rows = oracle_mod.prefill_rows(q, k, v, LOSSLESS_SCALE, causal=causal, smooth=False,
+                                         out_f64=True, pv=pv)
     Oe, Le = oracle_mod.exact_attention(q, k, v, LOSSLESS_SCALE, causal=causal, rows=rows)
     assert np.abs(O - Oe).max() < 1e-12 * max(1.0, np.abs(Oe).max())
     assert np.abs(L - Le).max() < 1e-12
@@ -229,3 +235,59 @@ def test_ambiguity_bound_marks_p_on_an_e4m3_midpoint(oracle_mod):
     # without P rounding there is nothing to be ambiguous about
     _, _, _, amb0 = oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 3, 0.1, False, ambiguity=True)
     assert not amb0.any()
+
+
+def _two_key_row(oracle_mod, target, p_format, lam_scale=0.1):
+    """One query, two keys: key 0 at the row max (448 p = 448), key 1 placed so
+    that 448 p = target; V = unit vectors, so acc holds each key's rounded
+    448 p in its own channel."""
+    lam = lam_scale / math.log(2.0)
+    D = 128
+    q = np.zeros((1, D))
+    q[0, 0] = 1.0
+    k = np.zeros((2, D))
+    k[1, 0] = math.log2(target / 448.0) / lam
+    v = np.zeros((2, D))
+    v[0, 0] = 1.0
+    v[1, 1] = 1.0
+    return oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 2, lam_scale, True, ambiguity=True,
+                                 p_format=p_format)
+
+
+def test_bf16_p_is_one_rounding_of_448p(oracle_mod):
+    """The BF16 P.V assignment rounds 448 p to the nearest bf16 (8 significant
+    bits, ties to the even significand): values well inside a bf16 interval
+    round like torch's conversion, an exact tie goes to the even neighbour,
+    and E4M3 would round the same values differently."""
+    for target in (300.4, 301.7, 123.45, 3.3, 0.0123):
+        _, _, acc, amb = _two_key_row(oracle_mod, target, "bf16")
+        want = torch.tensor(target, dtype=torch.float32).to(torch.bfloat16).double().item()
+        assert abs(acc[0, 1] - want) <= 1e-9 * want, (target, acc[0, 1], want)
+        assert not amb.any()
+        _, _, acc8, _ = _two_key_row(oracle_mod, target, "e4m3")
+        assert acc8[0, 1] != acc[0, 1]
+    # 301 lies halfway between 300 (even significand) and 302
+    _, _, acc, amb = _two_key_row(oracle_mod, 301.0, "bf16")
+    assert acc[0, 1] == 300.0 and acc[0, 0] == 448.0
+    assert amb[0, 1] == 2.0 and amb[0, 0] == 0.0
+
+
+def test_ambiguity_window_widens_with_the_exp2_error(oracle_mod):
+    """A P value 1e-4 (relative) away from an E4M3 midpoint is unambiguous for
+    an FP32 exp2 (window 2^-16) and ambiguous for an exp2 with 2^-12 relative
+    error."""
+    target = 432.0 * (1 + 1e-4)
+    _, _, _, amb = _two_key_row(oracle_mod, target, "e4m3")
+    assert not amb.any()
+    lam_scale = 0.1
+    lam = lam_scale / math.log(2.0)
+    D = 128
+    q = np.zeros((1, D))
+    q[0, 0] = 1.0
+    k = np.zeros((2, D))
+    k[1, 0] = math.log2(target / 448.0) / lam
+    v = np.zeros((2, D))
+    v[1, 1] = 1.0
+    _, _, _, amb2 = oracle_mod.attn_state(q, np.array([-1]), k, v, None, 0, 2, lam_scale, True,
+                                          ambiguity=True, amb_rel=2.0 ** -12)
+    assert amb2[0, 1] == 32.0
