@@ -628,6 +628,21 @@ def main():
     ms_no_rank_one = float(np.median(ms_pair["no_rank_one"]))
     log(f"[bench] same centred cache: with the rank-one step {ms_smooth_own:.3f} ms, without "
         f"{ms_no_rank_one:.3f} ms ({ms_smooth_own / ms_no_rank_one - 1:+.2%})")
+    # precision / placement variants (MpFA page section 3.1 Fig. 3(a), 7.4,
+    # 5.1) on the same caches, each taking its query amax in its own pass like
+    # the smoothing call they are compared with
+    vq16 = mpfa.pack_v_bf16(v)
+    ms_var = {}
+    for name in ("elementwise", "poly_exp2", "pv_bf16"):
+        def var_call(name=name):
+            mpfa.prefill_variant(name, q, kq, vq16 if name == "pv_bf16" else vq, cfg.scale,
+                                 causal=True, out=out, ws=ws_p)
+        ms_var[name] = time_calls(var_call, max(3, args.steps // 2), 1)
+        log(f"[bench] variant {name}: {ms_var[name]:.3f} ms ({ms_var[name] / ms_smooth_own - 1:+.2%} "
+            f"against the rank-one smoothing call)")
+    del vq16
+    torch.cuda.empty_cache()
+
     # the unsmoothed (direct) prefill on its own uncentred cache
     kq_direct = mpfa.quantize_k(k, smooth=False)
 
@@ -681,6 +696,14 @@ def main():
             "with_rank_one_ms": round(ms_smooth_own, 4), "without_ms": round(ms_no_rank_one, 4),
             "overhead": round(ms_smooth_own / ms_no_rank_one - 1.0, 4),
             "samples_ms": {k_: [round(t, 4) for t in v_] for k_, v_ in ms_pair.items()}},
+        "variants": {
+            "reference": "the smoothing call with its own query-amax pass "
+                         "(compensation.with_rank_one_ms); same caches",
+            **{name: {"ms": round(t, 4), "vs_rank_one_smoothing": round(t / ms_smooth_own - 1.0, 4)}
+               for name, t in ms_var.items()},
+            "what": {"elementwise": "Delta_S added per score on the VALU (MpFA 7.4 placement)",
+                     "poly_exp2": "one exp2 in four by a fitted cubic (MpFA 5.1 split)",
+                     "pv_bf16": "P and V in bf16, P.V on bf16 MFMA (MpFA 3.1 NVFP4+BF16)"}},
         "prefill_direct_ms": round(ms_direct, 4),
         "prefill_tile_mean": {"ms": round(ms_tile, 4),
                               "roofline": {"bound": "mfma", "achieved": round(ach_tile, 2),

@@ -290,6 +290,66 @@ int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv,
                              float* lse_or_null, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Precision and placement variants of the smoothing-mode prefill (paper
+ * section 3.1, Fig. 3(a): NVFP4 + FP8 against NVFP4 + BF16; section 7.4
+ * "Compensation placement": the rank-one MMA against an element-wise add;
+ * section 5.1: part of the exponentials by a polynomial on the FMA units).
+ * They exist to measure those choices on gfx950; each computes what its
+ * description says and is checked against the oracle like mpfa_prefill.
+ * Arguments, workspace and errors are those of mpfa_prefill unless stated.
+ *
+ * mpfa_prefill_elementwise -- Delta_S * 1/(gQ gK) added to every score on the
+ * vector ALUs at the start of the softmax of each block (before the mask and
+ * the running max), instead of the rank-one matrix step; the scores are the
+ * same up to FP32 rounding.  delta_s == NULL returns MPFA_ERR_INVALID.
+ */
+int mpfa_prefill_elementwise(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                             const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                             const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                             const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                             int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_prefill_poly_exp2 -- mpfa_prefill with one exponential in four
+ * computed as 2^rint(x) * c(x - rint(x)), c a cubic fitted to 2^f on
+ * [-1/2, 1/2] (largest relative error 7.5e-5), instead of the hardware exp2;
+ * P is then that much less accurate before its E4M3 rounding.  Smoothing or
+ * direct as mpfa_prefill.
+ */
+int mpfa_prefill_poly_exp2(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                           const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                           const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                           const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                           int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_pack_v_bf16 -- the bf16 V cache of mpfa_prefill_pv_bf16: V rounded to
+ * bf16 (nearest even) in tiles of 32 tokens, [B, Hkv, ceil(N/32), 4, 128, 8]
+ * uint16: token t, channel d at [t / 32][(t % 32) / 8][d][t % 8] (8 tokens of
+ * one channel per 16 bytes, the operand of a bf16 matrix instruction); zero
+ * past N.  v: [B, Hkv, N, 128] in v_dtype.  No workspace.
+ */
+int mpfa_pack_v_bf16(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint16_t* v_bf16,
+                     void* stream);
+
+/*
+ * mpfa_prefill_pv_bf16 -- the NVFP4 + BF16 precision assignment: Q.K^T as in
+ * mpfa_prefill, P rounded to bf16 (of 448 p, round to nearest even) instead
+ * of E4M3, and P.V on bf16 matrix instructions over the bf16 V cache of
+ * mpfa_pack_v_bf16 (v_bf16 replaces v_fp8 and v_scale); l sums the
+ * unrounded p as in mpfa_prefill; out_i = acc / (448 l).  Smoothing or direct
+ * as mpfa_prefill.
+ */
+int mpfa_prefill_pv_bf16(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                         const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                         const uint8_t* k_sf, const float* k_gscale, const uint16_t* v_bf16,
+                         const uint16_t* delta_s, float softmax_scale, int causal, void* out,
+                         int out_dtype, float* lse_or_null, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
  * mpfa_prefill_tile_mean -- mpfa_prefill with the queries smoothed per
  * 128-row query tile instead of per sequence (the query smoothing of paper
  * sections 3.2 and 5.1 at the granularity of the attention stage's query

@@ -30,7 +30,8 @@ V_TILE = 32  # tokens per head-dim-major V tile
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
            "mpfa_quantize_k_nvfp4_with_q_amax", "mpfa_quantize_v_fp8", "mpfa_append_kv",
            "mpfa_append_kv_paged", "mpfa_prefill", "mpfa_prefill_with_q_amax", "mpfa_decode",
-           "mpfa_decode_paged", "mpfa_prefill_tile_mean")
+           "mpfa_decode_paged", "mpfa_prefill_tile_mean", "mpfa_prefill_elementwise",
+           "mpfa_prefill_poly_exp2", "mpfa_pack_v_bf16", "mpfa_prefill_pv_bf16")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -72,6 +73,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_prefill_with_q_amax.restype = i32
     L.mpfa_prefill_with_q_amax.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                            P, f32, i32, P, i32, P, P, sz, P]
+    for name in ("mpfa_prefill_elementwise", "mpfa_prefill_poly_exp2"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32,
+                                     i32, P, i32, P, P, sz, P]
+    L.mpfa_prefill_pv_bf16.restype = i32
+    L.mpfa_prefill_pv_bf16.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, f32, i32,
+                                       P, i32, P, P, sz, P]
+    L.mpfa_pack_v_bf16.restype = i32
+    L.mpfa_pack_v_bf16.argtypes = [P, i32, i32, i32, i32, i32, P, P]
     L.mpfa_prefill_tile_mean.restype = i32
     L.mpfa_prefill_tile_mean.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f32, i32,
                                          P, i32, P, P, P, sz, P]
@@ -199,6 +209,48 @@ def mpfa_prefill_with_q_amax(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp
         float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_prefill_with_q_amax", st)
+
+
+def _prefill_variant(fn, q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
+                     softmax_scale, causal, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse, ws)
+    B, Hq, N, D = q.shape
+    st = getattr(load_library(), fn)(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise(fn, st)
+
+
+def mpfa_prefill_elementwise(*args, **kw):
+    """C-ABI call, the arguments of mpfa_prefill (smoothing mode)."""
+    _prefill_variant("mpfa_prefill_elementwise", *args, **kw)
+
+
+def mpfa_prefill_poly_exp2(*args, **kw):
+    """C-ABI call, the arguments of mpfa_prefill."""
+    _prefill_variant("mpfa_prefill_poly_exp2", *args, **kw)
+
+
+def mpfa_pack_v_bf16(v, v_bf16, stream=None):
+    _check(v, v_bf16)
+    B, Hkv, N, D = v.shape
+    st = load_library().mpfa_pack_v_bf16(_ptr(v), _dtype_code(v), B, Hkv, N, D, _ptr(v_bf16),
+                                         _stream(stream))
+    _raise("mpfa_pack_v_bf16", st)
+
+
+def mpfa_prefill_pv_bf16(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_bf16, delta_s,
+                         softmax_scale, causal, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_bf16, delta_s, out, lse, ws)
+    B, Hq, N, D = q.shape
+    st = load_library().mpfa_prefill_pv_bf16(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_bf16), _ptr(delta_s), float(softmax_scale),
+        int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_prefill_pv_bf16", st)
 
 
 def mpfa_prefill_tile_mean(q, Hkv, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, softmax_scale,
@@ -388,6 +440,48 @@ def prefill(q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=Fals
     else:
         mpfa_prefill(*args, softmax_scale, causal, out, lse if with_lse else None, ws,
                      stream=stream)
+    return out, (lse if with_lse else None)
+
+
+def pack_v_bf16(v, stream=None):
+    """Allocate and fill the bf16 V cache of the bf16 P.V variant."""
+    import torch
+    B, Hkv, N, D = v.shape
+    out = torch.empty((B, Hkv, (N + V_TILE - 1) // V_TILE, 4, D, 8), dtype=torch.int16,
+                      device=v.device)
+    mpfa_pack_v_bf16(v, out, stream=stream)
+    return {"v_bf16": out}
+
+
+def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False,
+                    ws=None, out=None, lse=None, stream=None):
+    """One of the prefill's precision / placement variants on the caches of
+    quantize_k (smoothing iff kq holds delta_s): "elementwise" (Delta_S added
+    per score on the vector ALUs; smoothing only), "poly_exp2" (one exponential
+    in four by a cubic), "pv_bf16" (vq from pack_v_bf16: bf16 P and V).  The
+    query amax is taken in the call's own pass.  Returns (out, lse or None)."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = kq["k_fp4"].shape[1]
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(MPFA_OP_PREFILL, B, Hq, Hkv, N, 1, q.device)
+    smooth = kq.get("delta_s") is not None
+    common = (q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
+              kq["k_fp4"], kq["k_sf"], kq["k_gscale"])
+    tail = (softmax_scale, causal, out, lse if with_lse else None, ws)
+    if variant == "pv_bf16":
+        mpfa_prefill_pv_bf16(*common, vq["v_bf16"], kq.get("delta_s") if smooth else None, *tail,
+                             stream=stream)
+    elif variant in ("elementwise", "poly_exp2"):
+        _prefill_variant(f"mpfa_prefill_{variant}", *common, vq["v_fp8"], vq["v_scale"],
+                         kq.get("delta_s") if smooth else None, *tail, stream=stream)
+    else:
+        raise ValueError(f"unknown variant {variant!r}")
     return out, (lse if with_lse else None)
 
 

@@ -293,20 +293,25 @@ int mpfa_append_kv_paged(const void* k_new, const void* v_new, int kv_dtype, int
 namespace {
 
 // The prefill call; q_amax NULL: the Q_c amax comes from a pass over Q here.
+// variant: the attention kernel's precision / placement variant (0 = the
+// method); variant 3 reads V from v_bf16 instead of v_fp8 and v_scale.
 int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
                  const float* v_scale, const uint16_t* delta_s, const float* q_amax,
                  float softmax_scale, int causal, void* out, int out_dtype, float* lse, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 size_t ws_bytes, void* stream, int variant = 0,
+                 const uint16_t* v_bf16 = nullptr) {
   int st = check_sizes(B, Hkv, N, D);
   if (st) return st;
   if ((st = check_heads(Hq, Hkv, B))) return st;
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
-  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out || !ws)
-    return MPFA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_fp8) ||
-      !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
+  const bool v16 = variant == kVarPvBf16;
+  if (!q || !k_fp4 || !k_sf || !k_gscale || !out || !ws) return MPFA_ERR_INVALID;
+  if (v16 ? !v_bf16 : (!v_fp8 || !v_scale)) return MPFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) ||
+      !aligned16(v16 ? (const void*)v_bf16 : (const void*)v_fp8) || !aligned16(out) ||
+      !aligned16(ws) || (lse && !aligned16(lse)))
     return MPFA_ERR_INVALID;
   if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
                   !aligned16(delta_s)))
@@ -358,6 +363,8 @@ int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.lse = lse;
   p.q_amax = q_amax ? reinterpret_cast<const uint32_t*>(q_amax) : amax;
   p.n_units = n_units;
+  p.variant = variant;
+  p.v_bf16 = v16 ? v_bf16 : nullptr;
   launch_prefill(p, s);
   return launch_status();
 }
@@ -388,6 +395,50 @@ int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv,
   return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
                       v_scale, delta_s, q_amax, softmax_scale, causal, out, out_dtype,
                       lse_or_null, ws, ws_bytes, stream);
+}
+
+int mpfa_prefill_elementwise(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                             const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                             const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                             const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                             int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!delta_s) return MPFA_ERR_INVALID;  // a placement of the compensation needs one
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                      v_scale, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream, kVarElementwise);
+}
+
+int mpfa_prefill_poly_exp2(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                           const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                           const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                           const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                           int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                      v_scale, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream, kVarPolyExp2);
+}
+
+int mpfa_prefill_pv_bf16(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                         const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                         const uint8_t* k_sf, const float* k_gscale, const uint16_t* v_bf16,
+                         const uint16_t* delta_s, float softmax_scale, int causal, void* out,
+                         int out_dtype, float* lse_or_null, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, nullptr,
+                      nullptr, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream, kVarPvBf16, v_bf16);
+}
+
+int mpfa_pack_v_bf16(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint16_t* v_bf16,
+                     void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if (!dtype_ok(v_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!v || !v_bf16 || !aligned16(v) || !aligned16(v_bf16)) return MPFA_ERR_INVALID;
+  launch_pack_v_bf16(v, v_dtype == MPFA_BF16, B * Hkv, N, v_bf16, (hipStream_t)stream);
+  return launch_status();
 }
 
 int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
@@ -442,6 +493,8 @@ int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, i
   p.lse = lse;
   p.q_amax = amax;
   p.n_units = n_units;
+  p.variant = 0;
+  p.v_bf16 = nullptr;
   launch_prefill(p, s);
   return launch_status();
 }

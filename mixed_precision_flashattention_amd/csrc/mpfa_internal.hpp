@@ -5,6 +5,11 @@
 
 namespace mpfa {
 
+// Precision / placement variants of the prefill attention kernel
+// (PrefillParams::variant): the library's kernel, element-wise compensation,
+// polynomial exp2 for one exponential in four, bf16 P.V.
+constexpr int kVarNone = 0, kVarElementwise = 1, kVarPolyExp2 = 2, kVarPvBf16 = 3;
+
 struct PrefillParams {
   const void* q;
   int q_bf16;
@@ -24,6 +29,11 @@ struct PrefillParams {
   float* lse;
   const uint32_t* q_amax;  // amax of Q_c, computed by the pre-pass
   int n_units;             // 256-row query units per (batch, head)
+  // precision / placement variant of the attention kernel (0: the library's
+  // kernel; 1: element-wise compensation; 2: polynomial exp2 for one
+  // exponential in four; 3: bf16 P.V over v_bf16)
+  int variant;
+  const uint16_t* v_bf16;  // variant 3: the bf16 V cache (tiled), else NULL
 };
 
 struct DecodeParams {
@@ -123,6 +133,9 @@ void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int
                      const float* partials = nullptr, int n_partials = 0,
                      uint32_t* amax_out = nullptr);
 void launch_prefill(const PrefillParams& p, hipStream_t st);
+// bf16 V cache of the bf16 P.V variant: [BH, ceil(N/32), 4, 128, 8] bf16
+// (token t, channel d at [t/32][(t%32)/8][d][t%8]), zero past N.
+void launch_pack_v_bf16(const void* v, int is_bf16, int BH, int N, uint16_t* out, hipStream_t st);
 
 // decode.hip
 void launch_decode(const DecodeParams& p, hipStream_t st);

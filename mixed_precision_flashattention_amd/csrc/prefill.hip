@@ -53,6 +53,9 @@ constexpr int kKBlockBytes = kBlk * kRowBytes;
 // 16-byte reads are then contiguous across lanes (no bank conflicts).
 constexpr int kVTileBytes = kD * 32;
 constexpr int kVBlockBytes = 4 * kVTileBytes;
+// bf16 V (the bf16 P.V variant): 32-token tiles of 8 KB, 32 KB per block.
+constexpr int kVBf16TileBytes = kD * 32 * 2;
+constexpr int kVBf16BlockBytes = 4 * kVBf16TileBytes;
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
 // lds_addr + 16 i (lds_addr wave-uniform).  Written as inline assembly so the
@@ -100,6 +103,22 @@ __device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32
     const int tt = min(k0 / 32 + t, ntiles32 - 1);
     lds_load16(vbase + (int64_t)tt * kVTileBytes + (ch0 + lane) * 32 + half * 16,
                dst + t * kVTileBytes + half * (kD * 16) + ch0 * 16);
+  }
+}
+
+// The same for a bf16 V block (32 KB: 4 tiles of 8 KB, 1 KB pieces), wave w
+// moving pieces 32/NW w .. 32/NW (w+1) - 1; tiles past the cache are clamped
+// to its last tile (their keys are masked).
+template <int NW>
+__device__ __forceinline__ void issue_v_block_bf16(const uint8_t* vbase, int ntiles32, int k0,
+                                                   uint32_t dst, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int piece = (32 / NW) * w + i;
+    const int t = piece >> 3, part = piece & 7;
+    const int tt = min(k0 / 32 + t, ntiles32 - 1);
+    lds_load16(vbase + (int64_t)tt * kVBf16TileBytes + part * 1024 + 16 * lane,
+               dst + t * kVBf16TileBytes + part * 1024);
   }
 }
 
@@ -171,6 +190,78 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
   }
 }
 
+// Precision / placement variants of the smoothing-mode kernel (the paper's
+// section 3.1 and 7.4 comparisons, built as separate kernels; the library's
+// calls use kVarNone):
+//   kVarElementwise: Delta_S * 1/(gQ gK) added to each score on the VALU at
+//     the start of the softmax, instead of the rank-one matrix step;
+//   kVarPolyExp2: one exponential in four evaluated by a cubic on the FMA
+//     path instead of the hardware exp2 (the split the paper's B200 kernel
+//     uses to relieve its transcendental unit);
+//   kVarPvBf16: P rounded to bf16 and V from a bf16 cache, P.V on bf16 MFMA
+//     (the NVFP4 + BF16 precision assignment).
+// P of one block as the B operands of the P.V products: E4M3, 32 keys per
+// 32x32x64 operand (64 bytes per lane), or bf16 for the bf16 variant, 8 keys
+// per 32x32x16 operand (128 bytes per lane): w[t][u] holds keys 8u .. 8u + 7
+// of the lane's 16 keys of score tile t.
+template <int VAR>
+struct PRegs {
+  i32x8 w[2];
+};
+template <>
+struct PRegs<kVarPvBf16> {
+  i32x4 w[4][2];
+};
+
+// 2^x for the FMA path of kVarPolyExp2: x = r + f with r = rint(x), f in
+// [-1/2, 1/2]; 2^f by a cubic whose coefficients are a minimax fit of the
+// relative error on that interval (Lawson-weighted least squares on 20001
+// points; largest relative error 7.5e-5 evaluated in fp32 Horner form), then
+// scaled by 2^r.  Arguments below -126 are clamped (the result underflows to
+// zero in every P format anyway).
+__device__ __forceinline__ float poly_exp2(float x) {
+  constexpr float c0 = 0x1.fff694p-1f, c1 = 0x1.62f31ap-1f, c2 = 0x1.f0ddccp-3f, c3 = 0x1.c3f6a6p-5f;
+  x = fmaxf(x, -126.0f);
+  const float r = __builtin_rintf(x);
+  const float f = x - r;
+  const float p = fmaf(fmaf(fmaf(c3, f, c2), f, c1), f, c0);
+  return __builtin_ldexpf(p, (int)r);
+}
+
+// Two fp32 -> two bf16 (round to nearest even) in one word, low half first.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// bf16 V in LDS (kVarPvBf16): [4 tiles of 32 keys][4 groups of 8 keys]
+// [128 channels][8 keys] bf16 -- the same bytes as the bf16 V cache's tiles,
+// so a block is one contiguous 32 KB copy; a lane's operand is the 8 keys of
+// one channel (16 bytes), consecutive lanes read consecutive 16-byte slots.
+__device__ __forceinline__ i32x4 v_operand_bf16(const uint8_t* vblk, int i, int h, int col) {
+  const int ku = i >> 2, dt = i & 3, t = ku >> 1, u = ku & 1;
+  return *reinterpret_cast<const i32x4*>(vblk + (2 * (t >> 1) + h) * kVBf16TileBytes +
+                                         (2 * (t & 1) + u) * (kD * 16) + (32 * dt + col) * 16);
+}
+// O^T += V^T P^T for one block on bf16 MFMA (32 MFMAs: 8 key steps of 16 x 4
+// head-dim tiles); the V operand of MFMA i + 1 is read while MFMA i runs.  The
+// k slots of a step are keys 8u .. 8u + 7 of tile t in lane half 0 and the
+// same offsets 32 keys on in lane half 1, matching the P operand's keys.
+__device__ __forceinline__ void pv_block_bf16(f32x16 (&o)[4], const uint8_t* vblk,
+                                              const PRegs<kVarPvBf16>& pb, int h, int col) {
+  i32x4 va[2];
+  va[0] = v_operand_bf16(vblk, 0, h, col);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i + 1 < 32) va[(i + 1) & 1] = v_operand_bf16(vblk, i + 1, h, col);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ku = i >> 2;
+    o[i & 3] = mfma32_bf16(va[i & 1], pb.w[ku >> 1][ku & 1], o[i & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // O^T += V^T P^T for one block on the FP8 MFMA (8 MFMAs: key half c, head-dim
 // tile dt); the V operand of MFMA i + 1 is read while MFMA i runs.
 __device__ __forceinline__ i32x8 v_operand(const uint8_t* vblk, int i, int h, int col) {
@@ -180,16 +271,21 @@ __device__ __forceinline__ i32x8 v_operand(const uint8_t* vblk, int i, int h, in
   const i32x4 hi = *reinterpret_cast<const i32x4*>(vt + kD * 16);
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-__device__ __forceinline__ void pv_block(f32x16 (&o)[4], const uint8_t* vblk, const i32x8 (&pb)[2],
+template <int VAR>
+__device__ __forceinline__ void pv_block(f32x16 (&o)[4], const uint8_t* vblk, const PRegs<VAR>& pr,
                                          int h, int col) {
-  i32x8 va[2];
-  va[0] = v_operand(vblk, 0, h, col);
+  if constexpr (VAR == kVarPvBf16) {
+    pv_block_bf16(o, vblk, pr, h, col);
+  } else {
+    i32x8 va[2];
+    va[0] = v_operand(vblk, 0, h, col);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i + 1 < 8) va[(i + 1) & 1] = v_operand(vblk, i + 1, h, col);
-    __builtin_amdgcn_sched_barrier(0);
-    o[i & 3] = mfma32_fp8(va[i & 1], pb[i >> 2], o[i & 3]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8) va[(i + 1) & 1] = v_operand(vblk, i + 1, h, col);
+      __builtin_amdgcn_sched_barrier(0);
+      o[i & 3] = mfma32_fp8(va[i & 1], pr.w[i >> 2], o[i & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -206,10 +302,29 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // Mask, online softmax and E4M3 rounding of P for one block; rescales the
-// output accumulators when a row max moved.
-__device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i32x8 (&pb)[2],
+// output accumulators when a row max moved.  kVarElementwise first adds
+// Delta_S * cinv to every score (dblk: the block's Delta_S entries), the
+// other variants change the exponential or P's format.
+template <int VAR>
+__device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], PRegs<VAR>& pr,
                                               float& m_run, float& l_run, float lam, bool mask,
-                                              int k0, int lim, int h) {
+                                              int k0, int lim, int h, const uint16_t* dblk,
+                                              float cinv) {
+  if constexpr (VAR == kVarElementwise) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // the lane's 16 consecutive keys of tile t: 32 bytes
+      const i32x4* dp = reinterpret_cast<const i32x4*>(dblk + 64 * (t >> 1) + 32 * h + 16 * (t & 1));
+      const i32x4 d0 = dp[0], d1 = dp[1];
+      const uint32_t dw[8] = {(uint32_t)d0[0], (uint32_t)d0[1], (uint32_t)d0[2], (uint32_t)d0[3],
+                              (uint32_t)d1[0], (uint32_t)d1[1], (uint32_t)d1[2], (uint32_t)d1[3]};
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float dv = __uint_as_float((v & 1) ? (dw[v >> 1] & 0xFFFF0000u) : (dw[v >> 1] << 16));
+        s[t][v] = fmaf(dv, cinv, s[t][v]);
+      }
+    }
+  }
   if (mask) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -239,15 +354,22 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], i3
       const float e0 = fast_exp2(fmaf(s[t][v0], lam, nb));
       const float e1 = fast_exp2(fmaf(s[t][v0 + 1], lam, nb));
       const float e2 = fast_exp2(fmaf(s[t][v0 + 2], lam, nb));
-      const float e3 = fast_exp2(fmaf(s[t][v0 + 3], lam, nb));
+      const float e3 = VAR == kVarPolyExp2 ? poly_exp2(fmaf(s[t][v0 + 3], lam, nb))
+                                           : fast_exp2(fmaf(s[t][v0 + 3], lam, nb));
       const float part = (e0 + e1) + (e2 + e3);
       lsum = (c == 0 && k == 0) ? part : lsum + part;
-      // The low half is written first and the high half second, so the
-      // register's old content does not matter; a value that dies here lets
-      // the compiler convert in place (a constant 0 costs a move per word).
-      uint32_t wd = cvt_fp8x2<false>(e0, e1, __float_as_uint(part));
-      wd = cvt_fp8x2<true>(e2, e3, wd);
-      pb[c][k] = (int)wd;
+      if constexpr (VAR == kVarPvBf16) {
+        const int u = (k & 3) >> 1, wi = 2 * (k & 1);
+        pr.w[t][u][wi] = (int)cvt_bf16x2(e0, e1);
+        pr.w[t][u][wi + 1] = (int)cvt_bf16x2(e2, e3);
+      } else {
+        // The low half is written first and the high half second, so the
+        // register's old content does not matter; a value that dies here lets
+        // the compiler convert in place (a constant 0 costs a move per word).
+        uint32_t wd = cvt_fp8x2<false>(e0, e1, __float_as_uint(part));
+        wd = cvt_fp8x2<true>(e2, e3, wd);
+        pr.w[c][k] = (int)wd;
+      }
     }
   }
   l_run = fmaf(alpha, l_run, lsum);
@@ -301,17 +423,20 @@ __device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* q
 // the same rank-one step (BF16 K~ images and query operands, K~ blocks
 // triple-buffered so the next block is resident while the current one is
 // scored).
-template <int MODE>
+template <int MODE, int VAR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
   constexpr bool SMOOTH = MODE == 1, TILE = MODE == 2;
-  constexpr bool RANK1 = SMOOTH || TILE;  // a rank-one compensation step
+  // a rank-one compensation step (the element-wise variant adds Delta_S in
+  // the softmax instead)
+  constexpr bool RANK1 = (SMOOTH && VAR != kVarElementwise) || TILE;
+  constexpr bool PV16 = VAR == kVarPvBf16;
   constexpr int NKB = TILE ? 3 : 2;       // K~ block buffers
   __shared__ __align__(16) uint8_t smem_k[NKB][kBlk * kRowBytes];  // K~ blocks
-  __shared__ __align__(16) uint8_t smem_v[2][kVBlockBytes];        // V blocks
+  __shared__ __align__(16) uint8_t smem_v[2][PV16 ? kVBf16BlockBytes : kVBlockBytes];  // V blocks
   // Delta_S (smoothing: [buffer][0][key]) or Delta_tile (per-tile mode:
   // [buffer][row group][key])
-  __shared__ uint16_t smem_delta[2][TILE ? 2 : 1][kBlk];
+  __shared__ __align__(16) uint16_t smem_delta[2][TILE ? 2 : 1][kBlk];
   // per-tile mode: the tile means' bf16 parts as score-operand rows,
   // [row group][kc][lane half][part][8 bf16]
   __shared__ __align__(16) uint8_t smem_qop[TILE ? 2 * 8 * 2 * 3 * 16 : 16];
@@ -330,7 +455,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
   const int n_qtiles = (N + kBlk - 1) / kBlk;  // query tiles of the per-tile means
   const float gK = *p.k_gscale;
-  const float sV = *p.v_scale;
+  const float sV = PV16 ? 1.0f : *p.v_scale;  // a bf16 V cache is unscaled
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;  // exp2 constant per unit of the MFMA score
 
@@ -394,9 +519,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // Constant B operand of the rank-one step: slots 0..2 of lane half 0 hold
   // 1 / (gQ gK) as the sum of three bf16 parts (exact to fp32 precision);
   // the A operand repeats Delta_S[key] in the same slots.
+  const float cinv = 1.0f / gg;  // score units per unit of Delta
   i32x4 dB = {0, 0, 0, 0};
   if (RANK1) {
-    const float cinv = 1.0f / gg;
     const uint32_t c_hi = bf16_rne(cinv);
     const float r1 = cinv - __uint_as_float(c_hi << 16);
     const uint32_t c_mid = bf16_rne(r1);
@@ -413,7 +538,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int n_max = max(n_a, n_b);
   const int lim = p.causal ? min(my_row, N - 1) : N - 1;  // last visible key of this row
   const int ntiles32 = (N + 31) / 32;
-  const uint8_t* vbase = p.v_fp8 + kvh * ntiles32 * kVTileBytes;
+  const uint8_t* vbase = PV16 ? reinterpret_cast<const uint8_t*>(p.v_bf16) + kvh * ntiles32 * kVBf16TileBytes
+                              : p.v_fp8 + kvh * ntiles32 * kVTileBytes;
   const uint16_t* dbase = SMOOTH ? p.delta_s + (int64_t)bh * N : nullptr;
   const uint32_t lds_v0 = lds_addr(smem_v[0]), lds_v1 = lds_addr(smem_v[1]);
 
@@ -430,7 +556,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 o[4], s[4];
-  i32x8 pb[2];
+  PRegs<VAR> pb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
@@ -491,12 +617,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
                        lane);                                                                \
       if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
     }                                                                                        \
-    if ((J) < n_max)                                                                         \
-      issue_v_block<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, lane); \
+    if ((J) < n_max) {                                                                       \
+      if (PV16)                                                                              \
+        issue_v_block_bf16<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, \
+                              lane);                                                         \
+      else                                                                                   \
+        issue_v_block<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, lane); \
+    }                                                                                        \
   } while (0)
 #define MPFA_MATRIX(J)                                                                       \
   do {                                                                                       \
-    if ((J) >= 1 && (J) <= n_own) pv_block(o, smem_v[((J) - 1) & 1], pb, h, col);           \
+    if ((J) >= 1 && (J) <= n_own) pv_block<VAR>(o, smem_v[((J) - 1) & 1], pb, h, col);      \
     if ((J) < n_own) {                                                                       \
       score_block<RANK1, TILE>(s, smem_k[(J) % NKB], smem_delta[(J) & 1][TILE ? grp : 0], koff, \
                                kbase, qf, dB, h);                                            \
@@ -513,10 +644,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     if ((J) >= 0 && (J) < n_own) {                                                           \
       const int k0 = (J) * kBlk;                                                             \
       const bool mask = (p.causal && k0 + kBlk > grow0) || (k0 + kBlk > N);                 \
-      softmax_block(s, o, pb, m_run, l_run, lam, mask, k0, lim, h);                          \
+      softmax_block<VAR>(s, o, pb, m_run, l_run, lam, mask, k0, lim, h,                      \
+                         &smem_delta[(J) & 1][0][0], cinv);                                  \
     } else {                                                                                 \
-      pb[0] = i32x8{}; /* as for s: keeps old P from being live */                           \
-      pb[1] = i32x8{};                                                                       \
+      pb = PRegs<VAR>{}; /* as for s: keeps old P from being live */                         \
     }                                                                                        \
   } while (0)
   if (grp == 0) {
@@ -655,14 +786,58 @@ void launch_expand_k(const uint8_t* k_fp4, const uint8_t* k_sf, int64_t bhk, int
                        partials, n_partials, amax_out);
 }
 
+// bf16 V cache of the bf16 P.V variant (layout in mpfa_internal.hpp): thread g
+// writes the 16 bytes of (tile, group of 8 tokens, channel d): the bf16 (round
+// to nearest even) of those 8 tokens' element d, zero past N; consecutive
+// threads take consecutive channels, so the reads of each token are coalesced.
+__global__ __launch_bounds__(256) void k_pack_v_bf16(const void* __restrict__ v, int is_bf16, int N,
+                                                     int ntiles, int64_t n_threads,
+                                                     uint4* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n_threads) return;
+  const int d = (int)(g & (kD - 1));
+  const int64_t r = g >> 7;  // (bh * ntiles + tile) * 4 + group
+  const int grp = (int)(r & 3);
+  const int64_t tb = r >> 2;
+  const int64_t bh = tb / ntiles;
+  const int t0 = (int)(tb - bh * ntiles) * 32 + grp * 8;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ta = t0 + 2 * i, tb2 = ta + 1;
+    const float a = ta < N ? load_elem(v, (bh * N + ta) * kD + d, is_bf16) : 0.0f;
+    const float b = tb2 < N ? load_elem(v, (bh * N + tb2) * kD + d, is_bf16) : 0.0f;
+    w[i] = bf16_rne(a) | (bf16_rne(b) << 16);
+  }
+  out[g] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+void launch_pack_v_bf16(const void* v, int is_bf16, int BH, int N, uint16_t* out, hipStream_t st) {
+  const int ntiles = (N + 31) / 32;
+  const int64_t n_threads = (int64_t)BH * ntiles * 4 * kD;
+  hipLaunchKernelGGL(k_pack_v_bf16, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st, v,
+                     is_bf16, N, ntiles, n_threads, reinterpret_cast<uint4*>(out));
+}
+
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.n_units * p.B * p.Hq);
-  if (p.q_tile_mean)
-    hipLaunchKernelGGL(k_prefill<2>, dim3(grid), dim3(512), 0, st, p);
-  else if (p.delta_s)
-    hipLaunchKernelGGL(k_prefill<1>, dim3(grid), dim3(512), 0, st, p);
-  else
-    hipLaunchKernelGGL(k_prefill<0>, dim3(grid), dim3(512), 0, st, p);
+  const dim3 g(grid), b(512);
+  if (p.q_tile_mean) {
+    hipLaunchKernelGGL((k_prefill<2, kVarNone>), g, b, 0, st, p);
+  } else if (p.delta_s) {
+    switch (p.variant) {
+      case kVarElementwise: hipLaunchKernelGGL((k_prefill<1, kVarElementwise>), g, b, 0, st, p); break;
+      case kVarPolyExp2: hipLaunchKernelGGL((k_prefill<1, kVarPolyExp2>), g, b, 0, st, p); break;
+      case kVarPvBf16: hipLaunchKernelGGL((k_prefill<1, kVarPvBf16>), g, b, 0, st, p); break;
+      default: hipLaunchKernelGGL((k_prefill<1, kVarNone>), g, b, 0, st, p); break;
+    }
+  } else {
+    switch (p.variant) {
+      case kVarPolyExp2: hipLaunchKernelGGL((k_prefill<0, kVarPolyExp2>), g, b, 0, st, p); break;
+      case kVarPvBf16: hipLaunchKernelGGL((k_prefill<0, kVarPvBf16>), g, b, 0, st, p); break;
+      default: hipLaunchKernelGGL((k_prefill<0, kVarNone>), g, b, 0, st, p); break;
+    }
+  }
 }
 
 }  // namespace mpfa

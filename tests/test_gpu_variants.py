@@ -1,0 +1,148 @@
+"""GPU parity of the prefill's precision and placement variants (MpFA page
+section 3.1, Fig. 3(a): NVFP4 + BF16 P.V; section 7.4 "Compensation
+placement": an element-wise add instead of the rank-one MMA; section 5.1: a
+polynomial for part of the exponentials) against the oracle:
+
+* element-wise compensation: the same scores as the smoothing oracle
+  (S = Q~ K~^T + Delta_S before the mask and the max);
+* polynomial exp2: the smoothing and direct oracles, with the oracle's
+  rounding-ambiguity window widened to the polynomial's relative error
+  (2^-13 > 7.5e-5), since a P value that close to an E4M3 midpoint may round
+  either way;
+* bf16 P.V: the oracle with P rounded to bf16 (of 448 p) and V in bf16; the
+  bf16 V cache byte for byte.
+
+Output within |gpu - oracle| <= 2e-3 + 1e-2 |oracle| (+ the ambiguity slack),
+LSE within 2e-3, on every row of small cases and on sampled rows of the 32K
+benchmark inputs."""
+import time
+
+import numpy as np
+import pytest
+
+from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+POLY_AMB_REL = 2.0 ** -13
+
+
+@pytest.fixture(scope="module")
+def mpfa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_precision_flashattention_amd as m
+    m.load_library()
+    return m
+
+
+def _caches(mpfa, variant, qd, kd, vd, smooth):
+    kq = mpfa.quantize_k(kd, q=qd) if smooth else mpfa.quantize_k(kd, smooth=False)
+    vq = mpfa.pack_v_bf16(vd) if variant == "pv_bf16" else mpfa.quantize_v(vd)
+    return kq, vq
+
+
+def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
+    import torch
+    from mixed_precision_flashattention_amd import synth
+    in_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (synth.full(cfg, t) for t in ("q", "k", "v"))
+    say(f"case: prefill variant {variant} B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} {cfg.dtype} "
+        f"smooth={smooth} causal={causal}")
+    qd, kd, vd = dev(q, in_dtype), dev(k, in_dtype), dev(v, in_dtype)
+    kq, vq = _caches(mpfa, variant, qd, kd, vd, smooth)
+    out, lse = mpfa.prefill_variant(variant, qd, kq, vq, cfg.scale, causal=causal,
+                                    out_dtype=torch.float32, with_lse=True)
+    torch.cuda.synchronize()
+    pv = "bf16" if variant == "pv_bf16" else "fp8"
+    amb_rel = POLY_AMB_REL if variant == "poly_exp2" else None
+    if variant == "pv_bf16":
+        ref = oracle_mod.quantize_v_bf16(v)
+        tiles = host(vq["v_bf16"])  # [B, Hkv, T, 4, 128, 8]
+        B, Hkv, T = tiles.shape[:3]
+        rows = tiles.transpose(0, 1, 2, 3, 5, 4).reshape(B, Hkv, T * 32, 128)
+        assert_bytes_equal("v_bf16", rows[:, :, :cfg.N], ref)
+        assert not rows[:, :, cfg.N:].any(), "the bf16 V cache is zero past N"
+    O, LSE, _, AMB = oracle_mod.prefill_rows(q, k, v, cfg.scale, causal=causal, smooth=smooth,
+                                             ambiguity=True, pv=pv, amb_rel=amb_rel)
+    assert_close("out", host(out).reshape(-1, 128), O, slack=AMB)
+    assert_close("lse", host(lse).reshape(-1), LSE, atol=LSE_ATOL, rtol=0.0)
+    return host(out)
+
+
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+def test_variant_small_config(mpfa, oracle_mod, variant):
+    from mixed_precision_flashattention_amd import synth
+    _check(mpfa, oracle_mod, synth.config("prefill_1k_2x1"), variant)
+
+
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+@pytest.mark.parametrize("N", [1, 129, 300])
+def test_variant_gqa5_spikes_ragged(mpfa, oracle_mod, variant, N):
+    from mixed_precision_flashattention_amd import synth
+    _check(mpfa, oracle_mod, synth.config("qwen14b_prefill_32k", B=2, Hq=10, Hkv=2, N=N), variant)
+
+
+@pytest.mark.parametrize("variant", ["poly_exp2", "pv_bf16"])
+def test_variant_direct_mode(mpfa, oracle_mod, variant):
+    from mixed_precision_flashattention_amd import synth
+    _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=4, Hkv=2, N=333), variant,
+           smooth=False)
+
+
+@pytest.mark.parametrize("variant", ["elementwise", "pv_bf16"])
+def test_variant_non_causal(mpfa, oracle_mod, variant):
+    from mixed_precision_flashattention_amd import synth
+    _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=2, Hkv=1, N=260), variant,
+           causal=False)
+
+
+def test_elementwise_matches_the_rank_one_kernel(mpfa):
+    """The two placements compute the same scores; their outputs agree far
+    inside the oracle tolerance."""
+    import torch
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("llama8b_prefill_16k", B=1, Hq=8, Hkv=2, N=1000)
+    q, k, v = (dev(synth.full(cfg, t), torch.bfloat16) for t in ("q", "k", "v"))
+    say("case: element-wise against rank-one compensation, N1000")
+    kq, vq = mpfa.quantize_k(k, q=q), mpfa.quantize_v(v)
+    a, _ = mpfa.prefill(q, kq, vq, cfg.scale, out_dtype=torch.float32)
+    b, _ = mpfa.prefill_variant("elementwise", q, kq, vq, cfg.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("elementwise vs rank-one", host(b).reshape(-1, 128), host(a).reshape(-1, 128),
+                 atol=1e-3, rtol=5e-3)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+def test_variant_fullsize_qwen14b_32k(mpfa, oracle_mod, variant):
+    """Each variant on the 32K benchmark inputs, in the launch configuration the
+    benchmark times, on synth.sample_rows."""
+    import torch
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("qwen14b_prefill_32k")
+    say(f"case: full-size prefill variant {variant} {cfg.name} (benchmark inputs)")
+    t0 = time.time()
+    x = synth.device_inputs(cfg, "cuda")
+    kq, vq = _caches(mpfa, variant, x["q"], x["k"], x["v"], True)
+    rows = synth.sample_rows(cfg)
+    idx = [torch.from_numpy(rows[:, i]).cuda() for i in range(3)]
+    out, lse = mpfa.prefill_variant(variant, x["q"], kq, vq, cfg.scale, causal=True,
+                                    out_dtype=torch.float32, with_lse=True)
+    got = host(out[idx[0], idx[1], idx[2]])
+    got_lse = host(lse[idx[0], idx[1], idx[2]])
+    del out, lse, kq, vq
+    torch.cuda.synchronize()
+    qh, kh, vh = (x[t].float().cpu().numpy() for t in ("q", "k", "v"))
+    del x
+    torch.cuda.empty_cache()
+    say(f"  gpu done ({time.time() - t0:.1f} s); oracle on {len(rows)} sampled rows")
+    ops = oracle_mod.Operands(qh, kh, vh, cfg.scale, smooth=True, identity=False,
+                              pv="bf16" if variant == "pv_bf16" else "fp8")
+    O, LSE, _, AMB = oracle_mod.prefill_rows(
+        qh, kh, vh, cfg.scale, causal=True, smooth=True, rows=rows, ops=ops, ambiguity=True,
+        amb_rel=POLY_AMB_REL if variant == "poly_exp2" else None)
+    say(f"  oracle done ({time.time() - t0:.1f} s)")
+    assert_close("out f32", got, O, slack=AMB)
+    assert_close("lse", got_lse, LSE, atol=LSE_ATOL, rtol=0.0)
