@@ -87,6 +87,10 @@ extern "C" {
 /* Largest GQA group (Hq / Hkv) the decode kernel packs into one tile. */
 #define MPFA_DECODE_MAX_GROUP 8
 
+/* Size of the fixed per-GPU scratch array of mpfa_decode_static (16 MiB):
+ * the largest mpfa_workspace_bytes(MPFA_OP_DECODE, ...) it serves. */
+#define MPFA_DECODE_STATIC_SCRATCH_BYTES 16777216
+
 /*
  * Bytes of device workspace the given operation needs for these sizes
  * (multiple of 256).  Arguments not used by an operation are ignored
@@ -404,6 +408,34 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
                 const float* v_scale, const uint16_t* delta_s, float softmax_scale,
                 int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
                 void* stream);
+
+/*
+ * mpfa_decode_static -- mpfa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace argument and allocates nothing:
+ * the decode's scratch (query amax slots, per-partition m, l and acc) lives in
+ * a fixed array of MPFA_DECODE_STATIC_SCRATCH_BYTES in each GPU's memory,
+ * part of the library's device code, held until the process ends.  The first
+ * call on a device looks up that device's copy (hipGetSymbolAddress; no
+ * allocation); make one call before a graph capture.  Results are those of
+ * mpfa_decode with the same arguments, bit for bit.
+ *
+ * Limit: mpfa_workspace_bytes(MPFA_OP_DECODE, B, Hq, Hkv, N_kv, 128,
+ * num_splits) <= MPFA_DECODE_STATIC_SCRATCH_BYTES (about B * Hq * num_splits
+ * <= 32000), else MPFA_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and give unspecified
+ * results; calls on one stream are ordered and safe.  The array keeps the
+ * last call's contents; every word a call reads is written earlier in the
+ * same call, so nothing needs clearing.  Returns MPFA_ERR_LAUNCH if the
+ * array cannot be located on the current device.  Other arguments and errors
+ * as mpfa_decode.
+ */
+int mpfa_decode_static(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                       const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                       const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                       const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                       int num_splits, void* out, int out_dtype, float* lse, void* stream);
 
 /*
  * mpfa_decode_paged -- mpfa_decode over a paged cache (layout above) with

@@ -24,6 +24,7 @@ MPFA_OP_QUANTIZE_V = 1
 MPFA_OP_PREFILL = 2
 MPFA_OP_DECODE = 3
 MPFA_DECODE_MAX_GROUP = 8
+MPFA_DECODE_STATIC_SCRATCH_BYTES = 16777216
 HEAD_DIM = 128
 V_TILE = 32  # tokens per head-dim-major V tile
 
@@ -31,7 +32,8 @@ EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4"
            "mpfa_quantize_k_nvfp4_with_q_amax", "mpfa_quantize_v_fp8", "mpfa_append_kv",
            "mpfa_append_kv_paged", "mpfa_prefill", "mpfa_prefill_with_q_amax", "mpfa_decode",
            "mpfa_decode_paged", "mpfa_prefill_tile_mean", "mpfa_prefill_elementwise",
-           "mpfa_prefill_poly_exp2", "mpfa_pack_v_bf16", "mpfa_prefill_pv_bf16")
+           "mpfa_prefill_poly_exp2", "mpfa_pack_v_bf16", "mpfa_prefill_pv_bf16",
+           "mpfa_decode_static")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -88,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_decode.restype = i32
     L.mpfa_decode.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32, i32,
                               P, i32, P, P, sz, P]
+    L.mpfa_decode_static.restype = i32
+    L.mpfa_decode_static.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32,
+                                     i32, P, i32, P, P]
     L.mpfa_append_kv_paged.restype = i32
     L.mpfa_append_kv_paged.argtypes = [P, P, i32, i32, i32, i32, P, P, i32, i32, i32, i32, P, P, P,
                                        P, P, P, P, P, P]
@@ -295,6 +300,21 @@ def mpfa_decode(q, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_sc
         float(softmax_scale), int(num_splits), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_decode", st)
+
+
+def mpfa_decode_static(q, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s,
+                       softmax_scale, num_splits, out, lse, stream=None):
+    """C-ABI call: mpfa_decode without a workspace (the library's fixed
+    per-GPU scratch array; nothing is allocated)."""
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, delta_s, out, lse)
+    B, Hq = q.shape[0], q.shape[1]
+    D = q.shape[-1]
+    st = load_library().mpfa_decode_static(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N_kv, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp8), _ptr(v_scale), _ptr(delta_s),
+        float(softmax_scale), int(num_splits), _ptr(out), _dtype_code(out), _ptr(lse),
+        _stream(stream))
+    _raise("mpfa_decode_static", st)
 
 
 def _int32(*ts):

@@ -1,6 +1,9 @@
 // C ABI of the library: argument validation, workspace layout and the
 // launch order of each entry point.  Everything runs on the caller's stream;
 // nothing is allocated, freed or synchronised here.
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mpfa.h"
 #include "mpfa_internal.hpp"
 
@@ -499,31 +502,45 @@ int mpfa_prefill_tile_mean(const void* q, int q_dtype, int B, int Hq, int Hkv, i
   return launch_status();
 }
 
-int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
-                const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
-                const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
-                const float* v_scale, const uint16_t* delta_s, float softmax_scale,
-                int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
-                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of mpfa_decode except the workspace.
+int decode_validate(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                    const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                    const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                    const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                    int num_splits, const void* out, int out_dtype, const float* lse) {
   int st = check_sizes(B, Hkv, N_kv, D);
   if (st) return st;
   if ((st = check_heads(Hq, Hkv, B))) return st;
   if (Hq / Hkv > MPFA_DECODE_MAX_GROUP) return MPFA_ERR_UNSUPPORTED;
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
   if (num_splits < 1) return MPFA_ERR_INVALID;
-  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out || !ws)
-    return MPFA_ERR_INVALID;
+  if (!q || !k_fp4 || !k_sf || !k_gscale || !v_fp8 || !v_scale || !out) return MPFA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_fp8) ||
-      !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
+      !aligned16(out) || (lse && !aligned16(lse)))
     return MPFA_ERR_INVALID;
   if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
                   !aligned16(delta_s)))
     return MPFA_ERR_INVALID;
   if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
   if ((int64_t)B * Hkv * num_splits > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
-  const DecodeWs L = decode_layout(B, Hq, num_splits);
-  if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
+  return MPFA_OK;
+}
 
+// The decode launches over a validated call and a workspace of at least
+// decode_layout(B, Hq, num_splits).total bytes.  Every workspace word the
+// kernels read is written by an earlier kernel of the same call (the query
+// amax slots, each partition's state, empty partitions included), so the
+// workspace needs no clearing.
+int decode_run(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, const float* q_mean,
+               const float* k_mean, const uint8_t* k_fp4, const uint8_t* k_sf,
+               const float* k_gscale, const uint8_t* v_fp8, const float* v_scale,
+               const uint16_t* delta_s, float softmax_scale, int num_splits, void* out,
+               int out_dtype, float* lse, void* ws, void* stream) {
+  const DecodeWs L = decode_layout(B, Hq, num_splits);
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)(w + L.amax);
@@ -562,6 +579,66 @@ int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, in
   p.order = nullptr;
   launch_decode(p, s);
   return launch_status();
+}
+
+// Scratch of mpfa_decode_static: a fixed array in every GPU's memory (each
+// device holds its own copy, at its own address, until the process ends).
+// Host code never uses the array's name as an address: the device address
+// comes from hipGetSymbolAddress, looked up once per device with that device
+// current and kept in scratch_ptr.
+constexpr size_t kStaticScratchBytes = (size_t)MPFA_DECODE_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 256;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// This device's scratch address, or nullptr if it cannot be found.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  ptr = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                int num_splits, void* out, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = decode_validate(q, q_dtype, B, Hq, Hkv, N_kv, D, q_mean, k_mean, k_fp4, k_sf, k_gscale,
+                           v_fp8, v_scale, delta_s, softmax_scale, num_splits, out, out_dtype, lse);
+  if (st) return st;
+  if (!ws || !aligned16(ws)) return MPFA_ERR_INVALID;
+  if (ws_bytes < decode_layout(B, Hq, num_splits).total) return MPFA_ERR_WORKSPACE;
+  return decode_run(q, q_dtype, B, Hq, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                    v_scale, delta_s, softmax_scale, num_splits, out, out_dtype, lse, ws, stream);
+}
+
+int mpfa_decode_static(const void* q, int q_dtype, int B, int Hq, int Hkv, int N_kv, int D,
+                       const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                       const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                       const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                       int num_splits, void* out, int out_dtype, float* lse, void* stream) {
+  int st = decode_validate(q, q_dtype, B, Hq, Hkv, N_kv, D, q_mean, k_mean, k_fp4, k_sf, k_gscale,
+                           v_fp8, v_scale, delta_s, softmax_scale, num_splits, out, out_dtype, lse);
+  if (st) return st;
+  if (decode_layout(B, Hq, num_splits).total > kStaticScratchBytes) return MPFA_ERR_WORKSPACE;
+  void* ws = static_scratch();
+  if (!ws) return MPFA_ERR_LAUNCH;
+  return decode_run(q, q_dtype, B, Hq, Hkv, N_kv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                    v_scale, delta_s, softmax_scale, num_splits, out, out_dtype, lse, ws, stream);
 }
 
 int mpfa_decode_paged(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,

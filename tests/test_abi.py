@@ -99,7 +99,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_constants_match_header():
     import mixed_precision_flashattention_amd as mpfa
     for name in ("MPFA_F32", "MPFA_BF16", "MPFA_OP_QUANTIZE_K", "MPFA_OP_QUANTIZE_V",
-                 "MPFA_OP_PREFILL", "MPFA_OP_DECODE", "MPFA_DECODE_MAX_GROUP"):
+                 "MPFA_OP_PREFILL", "MPFA_OP_DECODE", "MPFA_DECODE_MAX_GROUP",
+                 "MPFA_DECODE_STATIC_SCRATCH_BYTES"):
         assert getattr(mpfa, name) == header_define(name), name
 
 
@@ -326,3 +327,31 @@ def test_paged_decode_rejects_bad_arguments(lib):
     assert _decode_paged(lib, f, ws_bytes=256) == WS
     assert _decode_paged(lib, f, scale=0.0) == INVALID
     assert _decode_paged(lib, f, D=64) == UNSUP
+
+
+def _decode_static(lib, f, **kw):
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, splits=2,
+             out=f.p, out_dtype=1, lse=None, stream=None)
+    a.update(kw)
+    return lib.mpfa_decode_static(*a.values())
+
+
+def test_decode_static_rejects_bad_arguments_and_sizes_past_its_array(lib):
+    """Validation runs before the scratch array is looked up: these calls fail
+    on the host (nothing is enqueued, no GPU is touched)."""
+    f = _Fake()
+    INVALID, UNSUP, WS = -1, -2, -3
+    assert _decode_static(lib, f, Hq=18) == UNSUP
+    assert _decode_static(lib, f, splits=0) == INVALID
+    assert _decode_static(lib, f, out=None) == INVALID
+    assert _decode_static(lib, f, k_fp4=f.mis) == INVALID
+    cap = header_define("MPFA_DECODE_STATIC_SCRATCH_BYTES")
+    ws = lib.mpfa_workspace_bytes
+    # the largest batch whose workspace fits, and one past it
+    B = 1
+    while ws(3, B + 1, 32, 8, 1024, 128, 32) <= cap:
+        B += 1
+    assert ws(3, B, 32, 8, 1024, 128, 32) <= cap < ws(3, B + 1, 32, 8, 1024, 128, 32)
+    assert _decode_static(lib, f, B=B + 1, Hq=32, Hkv=8, splits=32) == WS
+    assert B >= 16  # the 128K decode workload (batch 16, 32 query heads, 32 splits) fits
