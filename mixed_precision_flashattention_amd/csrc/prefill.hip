@@ -594,11 +594,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // Steps alternate between the groups: in body j, group 0 runs its matrix
   // phase (P.V of block j-1, scores of block j) in the first step and the
   // softmax of block j in the second; group 1 runs the softmax of block j-1
-  // first and its matrix phase second.  Group 0 finishes its matrix phase
-  // first, so it issues the loads of K~(j+1), Delta_S(j+1) and V(j) before
-  // the middle barrier (their buffers were last read in body j-1); the
-  // barrier that opens body j+1 publishes them.  Both loops pass the same
-  // barriers.  In the per-tile mode K~ runs one block further ahead (K~(j+2)
+  // first and its matrix phase second.  The loads of K~(j+1), Delta_S(j+1)
+  // and V(j) (their buffers were last read in body j-1) are split between
+  // the groups so that neither softmax phase pays for issuing them: group 0
+  // issues its half after its matrix phase, group 1 its half at the start of
+  // its own; the barrier that opens body j+1 publishes them.  Both loops
+  // pass the same barriers.  In the per-tile mode K~ runs one block further ahead (K~(j+2)
   // is issued in body j, into the buffer of K~(j-1)), and each wave's matrix
   // phase also computes Delta_tile(j+1) of its own tile for key tile
   // (wave & 3) from the resident K~(j+1); the next opening barrier publishes
@@ -613,16 +614,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   do {                                                                                       \
     const int jk = (J) + (TILE ? 2 : 1); /* the K~ block loaded in this body */              \
     if (jk < n_max) {                                                                        \
-      issue_k_block<4>(kimg + (int64_t)jk * kKBlockBytes, lds_addr(smem_k[jk % NKB]), wave,   \
+      issue_k_block<8>(kimg + (int64_t)jk * kKBlockBytes, lds_addr(smem_k[jk % NKB]), wave,   \
                        lane);                                                                \
       if (SMOOTH && tid < kBlk) dd = dbase[min(((J) + 1) * kBlk + tid, N - 1)];              \
     }                                                                                        \
     if ((J) < n_max) {                                                                       \
       if (PV16)                                                                              \
-        issue_v_block_bf16<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, \
+        issue_v_block_bf16<8>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, \
                               lane);                                                         \
       else                                                                                   \
-        issue_v_block<4>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, lane); \
+        issue_v_block<8>(vbase, ntiles32, (J) * kBlk, ((J) & 1) ? lds_v1 : lds_v0, wave, lane); \
     }                                                                                        \
   } while (0)
 #define MPFA_MATRIX(J)                                                                       \
@@ -663,6 +664,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       MPFA_STEP_OPEN(j);
       MPFA_SOFTMAX(j - 1);
       __syncthreads();
+      MPFA_ISSUE(j);
       MPFA_MATRIX(j);
     }
   }
