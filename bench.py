@@ -216,6 +216,70 @@ def cpu_baseline(cfg, target_s=12.0):
     return done_flops / spent / 1e12, threads, sample
 
 
+def cpu_plan():
+    """The oracle on every configuration, on the host cores (no GPU): the
+    small prefill and the 128K decode in full; the 16K, 32K and 128K
+    prefills on synth.sample_rows with their full-run attention time
+    extrapolated by the count of visible (query, key) pairs (labelled as
+    such).  Quantizers run on the whole tensors and are timed apart.
+    Prints one JSON line."""
+    import oracle
+    from mixed_precision_flashattention_amd import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    entries = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    for name in ("prefill_1k_2x1", "llama8b_prefill_16k", "qwen14b_prefill_32k",
+                 "llama8b_prefill_128k_lse"):
+        cfg = synth.config(name)
+        (q, k, v), t_gen = timed(lambda: tuple(synth.full(cfg, t) for t in ("q", "k", "v")))
+        log(f"[cpu-plan] {name}: inputs drawn ({t_gen:.1f} s)")
+        ops, t_quant = timed(lambda: oracle.Operands(q, k, v, cfg.scale, smooth=True, identity=False))
+        log(f"[cpu-plan] {name}: stage one on the whole tensors {t_quant:.1f} s")
+        full_pairs = cfg.B * cfg.Hq * cfg.N * (cfg.N + 1) / 2
+        whole = name == "prefill_1k_2x1"
+        rows = None if whole else synth.sample_rows(cfg)
+        _, t_att = timed(lambda: oracle.prefill_rows(q, k, v, cfg.scale, causal=True, smooth=True,
+                                                     rows=rows, ops=ops))
+        pairs = full_pairs if whole else float((rows[:, 2] + 1).sum())
+        e = {"workload": name, "run": "full" if whole else "sampled rows",
+             "rows": int(cfg.B * cfg.Hq * cfg.N) if whole else int(len(rows)),
+             "pairs": pairs, "stage_one_s": round(t_quant, 2), "attention_s": round(t_att, 2),
+             "attention_TFLOPs": 4.0 * 128 * pairs / t_att / 1e12}
+        if not whole:
+            e["attention_full_s_extrapolated"] = round(t_att * full_pairs / pairs, 1)
+            e["label"] = "extrapolated from the sampled rows by the count of visible pairs"
+        log(f"[cpu-plan] {name}: attention {t_att:.1f} s over {pairs:.3g} pairs "
+            f"({e['attention_TFLOPs'] * 1e3:.3f} GFLOP/s)")
+        entries.append(e)
+        del q, k, v, ops
+
+    cfg = synth.config("llama8b_decode_128k")
+    (q, k, v), t_gen = timed(lambda: tuple(synth.full(cfg, t) for t in ("q", "k", "v")))
+    qm = synth.q_mean(cfg)
+    log(f"[cpu-plan] {cfg.name}: inputs drawn ({t_gen:.1f} s)")
+    ops, t_quant = timed(lambda: oracle.Operands(q, k, v, cfg.scale, smooth=True, identity=False,
+                                                 q_mean=qm))
+    log(f"[cpu-plan] {cfg.name}: stage one on the whole tensors {t_quant:.1f} s")
+    del k, v
+    _, t_att = timed(lambda: oracle.decode(q, None, None, qm, cfg.num_splits, cfg.scale,
+                                           smooth=True, ops=ops))
+    nbytes = decode_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.N)
+    log(f"[cpu-plan] {cfg.name}: decode {t_att:.1f} s")
+    entries.append({"workload": cfg.name, "run": "full", "rows": cfg.B * cfg.Hq,
+                    "pairs": float(cfg.B * cfg.Hq * cfg.N), "stage_one_s": round(t_quant, 2),
+                    "attention_s": round(t_att, 2), "attention_GBps": nbytes / t_att / 1e9,
+                    "note": "one query row per call: the oracle's loop over rows runs on one thread"})
+    env = host_env()
+    print(json.dumps({"cpu_oracle_plan": entries, "threads": threads,
+                      "cpu_model": env.get("cpu_model"), "cpu_count": env.get("cpu_count")}),
+          flush=True)
+
+
 def _error_stats(got, ref):
     d = got - ref
     return {"max_abs": float(np.abs(d).max()), "mean_abs": float(np.abs(d).mean()),
@@ -518,7 +582,13 @@ def main():
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="build profiles/traffic.json from the rocprofv3 counter CSVs in DIR "
                          "(pmc_{prefill,decode,copy}_{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv)")
+    ap.add_argument("--cpu-plan", action="store_true",
+                    help="run the CPU oracle on every configuration (full or sampled rows with "
+                         "extrapolation) on the host cores, print one JSON line and exit; no GPU")
     args = ap.parse_args()
+    if args.cpu_plan:
+        cpu_plan()
+        return
     if args.write_traffic:
         write_traffic(args.write_traffic, args)
         return
