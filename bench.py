@@ -473,15 +473,15 @@ def write_traffic(run_dir, args):
     # decode = the query amax, split, combine
     # prefill_tile = fill, tile means with the tile-centred Q amax, its fold, K
     # expansion, attention
-    calls = [("prefill", "prefill", "k_prefill<1>", (-1, 0),
+    calls = [("prefill", "prefill", "k_prefill<1, 0>", (-1, 0),
               f"mpfa_prefill {args.workload}"),
              ("decode", "decode", "k_decode_split<true, false>", (-1, 0, 1),
               f"mpfa_decode {args.decode_workload}")]
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_short_FETCH_SIZE")):
-        calls.append(("prefill_short", "prefill", "k_prefill<1>", (-1, 0),
+        calls.append(("prefill_short", "prefill", "k_prefill<1, 0>", (-1, 0),
                       f"mpfa_prefill {args.short_workload}"))
     if os.path.isdir(os.path.join(run_dir, "pmc_prefill_tile_FETCH_SIZE")):
-        calls.append(("prefill_tile", "prefill", "k_prefill<2>", (-4, -3, -2, -1, 0),
+        calls.append(("prefill_tile", "prefill", "k_prefill<2, 0>", (-4, -3, -2, -1, 0),
                       f"mpfa_prefill_tile_mean {args.workload}"))
     for op, kind, main_kernel, offsets, name in calls:
         fv, fn = load(op, "FETCH_SIZE")
@@ -752,7 +752,7 @@ def main():
                    "spikes": "0.1% of Q, K, V entries x20", "output_dtype": "bf16",
                    "step": "stage one (means, NVFP4 K, Delta_S, FP8 V) + prefill"},
         "roofline": {"bound": "mfma",
-                     "kernel": "mpfa_prefill_with_q_amax (k_expand_k + k_prefill<1>)",
+                     "kernel": "mpfa_prefill_with_q_amax (k_expand_k + k_prefill<1, 0>)",
                      "achieved": round(achieved, 2), "peak": round(PEAK_MIXED / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MIXED, 4),
                      "traffic": measured_traffic(f"mpfa_prefill {cfg.name}"),
