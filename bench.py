@@ -394,7 +394,7 @@ def measure_decode_paged(mpfa, dcfg, dkq, dvq, dq, dout, dws, iters):
     pool = {}
     for name, t, shape in (("k_fp4", dkq["k_fp4"], (B, Hkv, npg, P, 64)),
                            ("k_sf", dkq["k_sf"], (B, Hkv, npg, P, 8)),
-                           ("v_fp8", dvq["v_fp8"], (B, Hkv, npg, 4, D, 32)),
+                           ("v_fp8", dvq["v_fp8"], (B, Hkv, npg, 4, 2, D, 16)),
                            ("delta_s", dkq["delta_s"], (B, Hq, npg, P))):
         x = t.reshape(shape).transpose(1, 2).reshape((B * npg,) + (shape[1],) + shape[3:])
         pool[name] = torch.empty_like(x)
@@ -628,7 +628,7 @@ def main():
           "q_mean": torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
           "delta_s": torch.empty((B, Hq, N), dtype=torch.int16, device=dev),
           "q_amax": torch.empty(1, dtype=torch.float32, device=dev)}
-    vq = {"v_fp8": torch.empty((B, Hkv, (N + 31) // 32, D, 32), dtype=torch.uint8, device=dev),
+    vq = {"v_fp8": torch.empty((B, Hkv, (N + 31) // 32, 2, D, 16), dtype=torch.uint8, device=dev),
           "v_scale": torch.empty(1, dtype=torch.float32, device=dev)}
     out = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=dev)
     ws_k = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_QUANTIZE_K, B, Hq, Hkv, N),

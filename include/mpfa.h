@@ -36,11 +36,12 @@
  *                                     nibble of byte t (bit 3 = sign)
  *   k_sf     uint8 [B, Hkv, N, 8]    E4M3 scale code of each 16-element block
  *   k_gscale float [1]               per-tensor FP32 scale of the K codes
- *   v_fp8    uint8 [B, Hkv, ceil(N/32), 128, 32]  E4M3 codes of V, stored in
- *                                     tiles of 32 tokens, head-dim major
- *                                     inside a tile: element (t, d) sits at
- *                                     [t/32][d][t%32]; positions t >= N of
- *                                     the last tile hold code 0
+ *   v_fp8    uint8 [B, Hkv, ceil(N/32), 2, 128, 16]  E4M3 codes of V, stored
+ *                                     in tiles of 32 tokens, each two halves
+ *                                     of 16 tokens, head-dim major inside a
+ *                                     half: element (t, d) sits at
+ *                                     [t/32][(t%32)/16][d][t%16]; positions
+ *                                     t >= N of the last tile hold code 0
  *   v_scale  float [1]               per-tensor FP32 scale of the V codes
  *   delta_s  uint16 [B, Hq, N]       bf16 bits of Delta_S (smoothing only)
  *   q_mean   float [B, Hq, 128], k_mean float [B, Hkv, 128]
@@ -51,11 +52,13 @@
  * The V cache holds the same bytes as a row-major [B, Hkv, N, 128] FP8 cache
  * (one byte per element, paper section 6), permuted inside each 32-token
  * tile: the FP8 matrix instruction of P.V takes, per lane, 32 consecutive
- * tokens of one channel, which this layout serves with plain 16-byte loads
- * and no transpose.  Its size is 128 * 32 * ceil(N / 32) bytes per
- * (batch, KV head): N * 128 rounded up to whole tiles.  Converting to or from
- * the row layout is a pure byte permutation (byte (t, d) of the row layout is
- * byte [t / 32][d][t % 32] here).
+ * tokens of one channel, which this layout serves as two 16-byte pieces, the
+ * pieces of consecutive channels adjacent, so the operand loads of a wave
+ * read whole contiguous runs and need no transpose.  Its size is
+ * 128 * 32 * ceil(N / 32) bytes per (batch, KV head): N * 128 rounded up to
+ * whole tiles.  Converting to or from the row layout is a pure byte
+ * permutation (byte (t, d) of the row layout is byte
+ * [t / 32][(t % 32) / 16][d][t % 16] here).
  */
 #ifndef MPFA_H_
 #define MPFA_H_

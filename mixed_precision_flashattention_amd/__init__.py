@@ -26,7 +26,7 @@ MPFA_OP_DECODE = 3
 MPFA_DECODE_MAX_GROUP = 8
 MPFA_DECODE_STATIC_SCRATCH_BYTES = 16777216
 HEAD_DIM = 128
-V_TILE = 32  # tokens per head-dim-major V tile
+V_TILE = 32  # tokens per V tile (two head-dim-major halves of 16 tokens)
 
 EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4",
            "mpfa_quantize_k_nvfp4_with_q_amax", "mpfa_quantize_v_fp8", "mpfa_append_kv",
@@ -422,7 +422,8 @@ def quantize_v(v, stream=None):
     import torch
     B, Hkv, N, D = v.shape
     n_tiles = (N + V_TILE - 1) // V_TILE
-    out = {"v_fp8": torch.empty((B, Hkv, n_tiles, D, V_TILE), dtype=torch.uint8, device=v.device),
+    out = {"v_fp8": torch.empty((B, Hkv, n_tiles, 2, D, V_TILE // 2), dtype=torch.uint8,
+                                device=v.device),
            "v_scale": torch.empty(1, dtype=torch.float32, device=v.device)}
     ws = _workspace(MPFA_OP_QUANTIZE_V, B, 0, Hkv, N, 1, v.device)
     mpfa_quantize_v_fp8(v, out["v_fp8"], out["v_scale"], ws, stream=stream)
@@ -597,10 +598,12 @@ def append_kv_paged(k_new, v_new, pos, pool, block_table, stream=None):
 
 
 def v_tiles_to_rows(v_fp8_tiled, N: int):
-    """Host-side layout helper: tiled V codes [..., T, 128, 32] -> [..., N, 128]
-    (a pure permutation of bytes, used to compare caches element by element)."""
+    """Host-side layout helper: tiled V codes [..., T, 2, 128, 16] (token t,
+    channel d at [t / 32][(t % 32) / 16][d][t % 16]) -> [..., N, 128] (a pure
+    permutation of bytes, used to compare caches element by element)."""
     x = v_fp8_tiled
-    lead = x.shape[:-3]
-    T = x.shape[-3]
-    x = x.reshape(*lead, T, HEAD_DIM, V_TILE).swapaxes(-1, -2).reshape(*lead, T * V_TILE, HEAD_DIM)
+    lead = x.shape[:-4]
+    T = x.shape[-4]
+    x = x.reshape(*lead, T, 2, HEAD_DIM, V_TILE // 2).swapaxes(-1, -2)
+    x = x.reshape(*lead, T * V_TILE, HEAD_DIM)
     return x[..., :N, :]

@@ -151,10 +151,17 @@ __device__ __forceinline__ void decode_load(DecodeBlockRegs& r, const DecodeCtx&
       r.dl[i] = w;
     }
   }
+  // V^T operand of lane (n, kg): channel 16 dt + n, the 32 tokens of tile
+  // kg, as its two 16-token pieces (each load instruction reads 256
+  // contiguous bytes per tile)
   const int n = lane & 15, kg = lane >> 4;
   const uint8_t* vt = bp.v + (int64_t)min(kg, bp.vlast) * kVTileBytes;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) r.v[dt] = ld_stream<i32x8>(vt + (16 * dt + n) * 32);
+  for (int dt = 0; dt < 8; ++dt) {
+    const i32x4 lo = ld_stream<i32x4>(vt + (16 * dt + n) * 16);
+    const i32x4 hi = ld_stream<i32x4>(vt + kD * 16 + (16 * dt + n) * 16);
+    r.v[dt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
 }
 
 struct DecodeState {

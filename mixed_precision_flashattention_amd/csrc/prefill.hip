@@ -91,18 +91,21 @@ __device__ __forceinline__ void issue_k_block(const uint8_t* kimg, uint32_t dst,
   }
 }
 
-// Wave w's share of V block k0 when NW waves load it: pieces (tile, half,
-// 64 channels) 16/NW w .. 16/NW (w+1) - 1.
+// Wave w's share of V block k0 when NW waves load it: 1 KB pieces
+// 16/NW w .. 16/NW (w+1) - 1, each a contiguous copy (the cache's 32-token
+// tiles have the layout the P.V operands are read with: [half][channel][16
+// tokens]); tiles past the cache are clamped to its last tile (their keys
+// are masked).
 template <int NW>
 __device__ __forceinline__ void issue_v_block(const uint8_t* vbase, int ntiles32, int k0,
                                               uint32_t dst, int w, int lane) {
 #pragma unroll
   for (int i = 0; i < 16 / NW; ++i) {
     const int piece = (16 / NW) * w + i;
-    const int t = piece >> 2, half = (piece >> 1) & 1, ch0 = 64 * (piece & 1);
+    const int t = piece >> 2;
     const int tt = min(k0 / 32 + t, ntiles32 - 1);
-    lds_load16(vbase + (int64_t)tt * kVTileBytes + (ch0 + lane) * 32 + half * 16,
-               dst + t * kVTileBytes + half * (kD * 16) + ch0 * 16);
+    lds_load16_s(vbase + (int64_t)tt * kVTileBytes + (piece & 3) * 1024, 16 * lane,
+                 dst + piece * 1024);
   }
 }
 
@@ -364,9 +367,10 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], PR
         pr.w[t][u][wi + 1] = (int)cvt_bf16x2(e2, e3);
       } else {
         // The low half is written first and the high half second, so the
-        // register's old content does not matter; a value that dies here lets
-        // the compiler convert in place (a constant 0 costs a move per word).
-        uint32_t wd = cvt_fp8x2<false>(e0, e1, __float_as_uint(part));
+        // register's old content does not matter; e0, which dies here, lets
+        // the compiler convert in place (a constant 0, or a value still live
+        // such as part, costs a move per word).
+        uint32_t wd = cvt_fp8x2<false>(e0, e1, __float_as_uint(e0));
         wd = cvt_fp8x2<true>(e2, e3, wd);
         pr.w[c][k] = (int)wd;
       }

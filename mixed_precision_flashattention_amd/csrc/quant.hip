@@ -485,14 +485,18 @@ __global__ __launch_bounds__(512) void k_delta_s(const void* __restrict__ k, int
   delta[(hq0 + g) * N + t] = (uint16_t)bf16_rne((float)acc);
 }
 
-// FP8 E4M3 V in 32-token tiles, head-dim major inside a tile.  Block: 128
-// threads x one tile; positions past N are written as 0.  Thread (tr, cg)
-// reads channels 8 cg .. 8 cg + 7 of tokens 4 tr .. 4 tr + 3 of the tile
-// (16-byte loads of bf16), encodes them and keeps one word per channel (its
-// four tokens' codes); LDS turns the tile around so that thread d then
-// writes channel d's 32 codes in two 16-byte stores.  Channel c's 32-byte
-// LDS row sits in slot 8 (c / 8) + (c + c / 8) % 8, which spreads the word
-// writes of one instruction over the banks.
+// FP8 E4M3 V in 32-token tiles; inside a tile, two halves of 16 tokens,
+// each head-dim major: token t, channel d at [t / 32][(t % 32) / 16][d][t % 16],
+// so that 16 consecutive tokens of one channel are one 16-byte piece and the
+// pieces of consecutive channels are adjacent.  Block: 128 threads x one
+// tile; positions past N are written as 0.  Thread (tr, cg) reads channels
+// 8 cg .. 8 cg + 7 of tokens 4 tr .. 4 tr + 3 of the tile (16-byte loads of
+// bf16), encodes them and keeps one word per channel (its four tokens'
+// codes); LDS turns the tile around so that thread d then writes channel
+// d's two 16-token pieces (each store instruction of the block covers 2 KB
+// contiguously).  Channel c's 32-byte LDS row sits in slot
+// 8 (c / 8) + (c + c / 8) % 8, which spreads the word writes of one
+// instruction over the banks.
 __device__ __forceinline__ int v_tile_slot(int c) { return 8 * (c >> 3) + ((c + (c >> 3)) & 7); }
 __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, int is_bf16, int N,
                                                     int n_tiles, const uint32_t* __restrict__ amax,
@@ -530,9 +534,9 @@ __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, 
   __syncthreads();
   const int d = threadIdx.x;
   const uint4* src = reinterpret_cast<const uint4*>(rows + v_tile_slot(d) * 8);
-  uint4* dst = reinterpret_cast<uint4*>(out + ((bh * n_tiles + tile) * kD + d) * 32);
-  dst[0] = src[0];
-  dst[1] = src[1];
+  uint8_t* tbase = out + (bh * n_tiles + tile) * kD * 32;
+  *reinterpret_cast<uint4*>(tbase + d * 16) = src[0];           // tokens 0 .. 15
+  *reinterpret_cast<uint4*>(tbase + kD * 16 + d * 16) = src[1];  // tokens 16 .. 31
 }
 
 // Decode-time cache write (paper section 6 "Online quantization": the new
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, 
 // (FP64 over ascending channels).
 //
 // Where one appended token goes: its K code row (64 bytes), scale row (8
-// bytes), the V byte of channel 0 (channel d at + 32 d), and the Delta_S
+// bytes), the V byte of channel 0 (channel d at + 16 d), and the Delta_S
 // entry of the group's first query head (head g at + g * dstride).
 struct AppendDst {
   uint8_t* k;
@@ -563,7 +567,7 @@ __device__ __forceinline__ void append_token(const void* k_new, const void* v_ne
   float x = load_elem(k_new, src, is_bf16);
   if (k_mean_row) x = x - k_mean_row[d];
   kc[d] = x;
-  o.v[d * 32] = (uint8_t)e4m3_encode(load_elem(v_new, src, is_bf16) / vS);
+  o.v[d * 16] = (uint8_t)e4m3_encode(load_elem(v_new, src, is_bf16) / vS);
   __syncthreads();
   if (d < 8) {
     float xb[16];
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(128) void k_append_kv(
   AppendDst o;
   o.k = k_fp4 + row * 64;
   o.s = k_sf + row * 8;
-  o.v = v_fp8 + ((int64_t)bhk * ntiles + p / 32) * kD * 32 + (p & 31);
+  o.v = v_fp8 + ((int64_t)bhk * ntiles + p / 32) * kD * 32 + ((p & 31) >> 4) * kD * 16 + (p & 15);
   o.d = k_mean ? delta + (int64_t)bhk * G * N_cap + p : nullptr;  // head b*Hq + hk*G = bhk*G
   o.dstride = N_cap;
   append_token(k_new, v_new, is_bf16, (int64_t)bhk * T + t, k_mean ? k_mean + (int64_t)bhk * kD : nullptr,
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(128) void k_append_kv_paged(
   AppendDst o;
   o.k = k_fp4 + (slab * kBlk + slot) * 64;
   o.s = k_sf + (slab * kBlk + slot) * 8;
-  o.v = v_fp8 + (slab * 4 + slot / 32) * kD * 32 + (slot & 31);
+  o.v = v_fp8 + (slab * 4 + slot / 32) * kD * 32 + ((slot & 31) >> 4) * kD * 16 + (slot & 15);
   o.d = k_mean ? delta + ((int64_t)pg * Hkv * G + (int64_t)hk * G) * kBlk + slot : nullptr;
   o.dstride = kBlk;
   append_token(k_new, v_new, is_bf16, bhk, k_mean ? k_mean + (int64_t)bhk * kD : nullptr,

@@ -98,7 +98,7 @@ def test_decode_append_then_decode(mpfa, oracle_mod):
     ck["k_sf"][:, :, :N0] = kq["k_sf"]
     ck["delta_s"][:, :, :N0] = kq["delta_s"]
     nt0 = (N0 + 31) // 32
-    cv = {"v_fp8": torch.zeros((B, Hkv, (Ncap + 31) // 32, 128, 32), dtype=torch.uint8, device="cuda"),
+    cv = {"v_fp8": torch.zeros((B, Hkv, (Ncap + 31) // 32, 2, 128, 16), dtype=torch.uint8, device="cuda"),
           "v_scale": vq["v_scale"]}
     cv["v_fp8"][:, :, :nt0] = vq["v_fp8"]
     mpfa.append_kv(dev(kn, torch.bfloat16), dev(vn, torch.bfloat16),

@@ -32,7 +32,7 @@ def _buffers(mpfa, torch, B, Hq, Hkv, N, P, dev):
          "q_mean": torch.empty((B, Hq, D), dtype=f32, device=dev),
          "delta_s": torch.empty((B, Hq, N), dtype=torch.int16, device=dev),
          "q_amax": torch.empty(1, dtype=torch.float32, device=dev),
-         "v_fp8": torch.empty((B, Hkv, (N + 31) // 32, D, 32), dtype=u8, device=dev),
+         "v_fp8": torch.empty((B, Hkv, (N + 31) // 32, 2, D, 16), dtype=u8, device=dev),
          "v_scale": torch.empty(1, dtype=f32, device=dev),
          "out": torch.empty((B, Hq, N, D), dtype=f32, device=dev),
          "lse": torch.empty((B, Hq, N), dtype=f32, device=dev),

@@ -32,7 +32,7 @@ def _empty_pool(B, Hq, Hkv, num_pages, smooth, seed, fill="random"):
         return torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=g)
 
     pool = {"k_fp4": u8(num_pages, Hkv, PAGE, 64), "k_sf": u8(num_pages, Hkv, PAGE, 8),
-            "v_fp8": u8(num_pages, Hkv, 4, PAGE, 32)}
+            "v_fp8": u8(num_pages, Hkv, 4, 2, 128, 16)}
     if smooth:
         pool["delta_s"] = u8(num_pages, Hq, PAGE, 2).view(torch.int16).reshape(num_pages, Hq, PAGE)
     return pool
