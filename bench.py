@@ -410,8 +410,8 @@ def measure_decode_paged(mpfa, dcfg, dkq, dvq, dq, dout, dws, iters):
     def call(lens):
         mpfa.decode_paged(dq, pool, table, lens, dcfg.scale, dcfg.num_splits, out=dout, ws=dws)
 
-    ms_full = time_calls(lambda: call(full), iters, 3)
-    ms_rag = time_calls(lambda: call(ragged), iters, 3)
+    ms_full = float(np.median([time_calls(lambda: call(full), iters, 3) for _ in range(3)]))
+    ms_rag = float(np.median([time_calls(lambda: call(ragged), iters, 3) for _ in range(3)]))
     per_tok = Hkv * (64 + 8 + 128) + Hq * 2
     by_full = B * N * per_tok
     by_rag = int(ragged_host.sum()) * per_tok
@@ -823,9 +823,16 @@ def main():
                              dkq["delta_s"] if smooth else None, dcfg.scale, dcfg.num_splits,
                              dout, None, dws)
 
-        ms_dec = time_calls(decode_call, max(args.steps, 10), 3)
+        # smoothing and direct calls interleaved over three rounds of 20 calls
+        # each (the median round is reported), so that both see the same
+        # state of the device
+        dec_rounds = {"smooth": [], "direct": []}
+        for _ in range(3):
+            dec_rounds["smooth"].append(time_calls(decode_call, 20, 3))
+            dec_rounds["direct"].append(time_calls(lambda: decode_call(False), 20, 3))
+        ms_dec = float(np.median(dec_rounds["smooth"]))
+        ms_dec_direct = float(np.median(dec_rounds["direct"]))
         ms_dec_median = median_call_ms(decode_call)
-        ms_dec_direct = time_calls(lambda: decode_call(False), max(args.steps, 10), 3)
         nbytes = decode_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.N)
         gbs = nbytes / (ms_dec * 1e-3) / 1e9
         nbytes_d = decode_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.N, smooth=False)
@@ -839,6 +846,7 @@ def main():
                          "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4),
                          "traffic": measured_traffic("mpfa_decode llama8b_decode_128k")},
             "median_ms": round(ms_dec_median, 4),
+            "rounds_ms": {k: [round(x, 4) for x in v] for k, v in dec_rounds.items()},
             "direct_ms": round(ms_dec_direct, 4), "direct_GBps": round(gbs_d, 1),
             # attention FLOPs (4 * 128 per (query head, key)), for context only
             "flops_per_call": 4.0 * D * dcfg.N * dcfg.B * dcfg.Hq,
