@@ -185,7 +185,7 @@ int mpfa_quantize_v_fp8(const void* v, int v_dtype, int B, int Hkv, int N, int D
  * [B] (the caller's per-request lengths).  Caches of capacity N_cap tokens,
  * in the layouts mpfa_quantize_k_nvfp4 / mpfa_quantize_v_fp8 write:
  * k_fp4 [B, Hkv, N_cap, 64], k_sf [B, Hkv, N_cap, 8], v_fp8
- * [B, Hkv, ceil(N_cap/32), 128, 32], delta_s [B, Hq, N_cap] (bf16 bits).
+ * [B, Hkv, ceil(N_cap/32), 2, 128, 16], delta_s [B, Hq, N_cap] (bf16 bits).
  * The new rows are quantized exactly as the first stage would quantize
  * them with the same statistics: K_c = fp32(K - k_mean) (k_mean may be NULL:
  * direct mode), NVFP4 with the frozen global scale *k_gscale, FP8 with the
@@ -213,7 +213,7 @@ int mpfa_append_kv(const void* k_new, const void* v_new, int kv_dtype, int B, in
  * tokens (one softmax block; other sizes give MPFA_ERR_UNSUPPORTED):
  *   k_fp4   [num_pages, Hkv, 128, 64]      NVFP4 codes (element 2t low nibble)
  *   k_sf    [num_pages, Hkv, 128, 8]       E4M3 block scales
- *   v_fp8   [num_pages, Hkv, 4, 128, 32]   FP8 V, four head-dim-major 32-token tiles
+ *   v_fp8   [num_pages, Hkv, 4, 2, 128, 16] FP8 V, four 32-token tiles (layout above)
  *   delta_s [num_pages, Hq, 128]           bf16 compensation entries (smoothing)
  * block_table: device int32 [B, max_pages]; logical page i of request b
  * (its positions 128 i .. 128 i + 127) is physical page block_table[b, i].

@@ -564,7 +564,7 @@ def append_kv(k_new, v_new, pos, kq, vq, stream=None):
 def decode_paged(q, pool, block_table, seq_lens, softmax_scale, num_splits, out_dtype=None,
                  with_lse=False, ws=None, out=None, lse=None, stream=None):
     """Split-KV decode over a paged cache.  pool: k_fp4 [P, Hkv, 128, 64],
-    k_sf [P, Hkv, 128, 8], v_fp8 [P, Hkv, 4, 128, 32], per-request k_gscale
+    k_sf [P, Hkv, 128, 8], v_fp8 [P, Hkv, 4, 2, 128, 16], per-request k_gscale
     and v_scale [B] and, in smoothing mode, delta_s [P, Hq, 128], q_mean
     [B, Hq, 128], k_mean [B, Hkv, 128].  Returns (out [B, Hq, 128], lse or None)."""
     import torch
