@@ -200,7 +200,7 @@ def delta_s(qmean: np.ndarray, kc: np.ndarray) -> np.ndarray:
     return out
 
 
-P_FORMATS = {"none": 0, "e4m3": 1, "bf16": 2}
+P_FORMATS = {"none": 0, "e4m3": 1, "bf16": 2, "nvfp4": 3}
 AMB_REL = 2.0 ** -16  # how close to a rounding midpoint an FP32 exp2 cannot decide
 
 
@@ -211,8 +211,9 @@ def attn_state(q, row_pos, k, v, delta, kv_begin, kv_end, scale, quant_p=True, b
     q [R, D] f64; row_pos [R] int64 (-1: every key visible); k, v [Nk, D] f64;
     delta [Nk] f64 or None.  P is rounded as p_format says ("e4m3": the
     method's FP8 P with its fixed scale 448; "bf16": bf16 of 448 p, the BF16
-    P.V assignment; "none": not rounded); by default quant_p picks "e4m3" or
-    "none".  Returns (m [R], l [R], acc [R, D]) in FP64, and with
+    P.V assignment; "nvfp4": NVFP4 of p over 16-key groups with the fixed
+    global scale fp32(1/2688), the NVFP4 P.V assignment, acc in units of
+    448 p; "none": not rounded); by default quant_p picks "e4m3" or "none".  Returns (m [R], l [R], acc [R, D]) in FP64, and with
     ambiguity=True also amb [R, D]: how far acc may move if the keys whose
     448 p sits within amb_rel (relative) of a rounding midpoint round the
     other way (both roundings are correct for a p computed in FP32, or with
@@ -267,6 +268,8 @@ from .pipeline import (  # noqa: E402  (pipeline uses the bindings above)
     quantize_q_tiles,
     quantize_v,
     quantize_v_bf16,
+    quantize_v_nvfp4,
+    dequantize_v_nvfp4,
     tile_means,
     delta_tile,
     delta_tile_row,
@@ -277,7 +280,8 @@ __all__ = [
     "e2m1_decode", "e4m3_decode", "e2m1_table", "e4m3_table", "e2m1_encode", "e4m3_encode",
     "bf16_rne", "bf16_to_f64", "P_FORMATS", "AMB_REL", "channel_mean", "amax", "nvfp4_global_scale", "nvfp4_quantize",
     "nvfp4_dequantize", "fp8_scale", "fp8_quantize", "delta_s", "attn_state", "merge_states",
-    "quantize_k", "quantize_v", "quantize_v_bf16", "quantize_q", "prefill_rows", "decode", "decode_partitions",
+    "quantize_k", "quantize_v", "quantize_v_bf16", "quantize_v_nvfp4", "dequantize_v_nvfp4",
+    "quantize_q", "prefill_rows", "decode", "decode_partitions",
     "exact_attention", "Operands", "append_kv", "PAGE", "gather_pages", "decode_paged",
     "append_kv_paged", "Q_TILE", "tile_means", "quantize_q_tiles", "delta_tile", "delta_tile_row",
     "prefill_tile_mean_rows"

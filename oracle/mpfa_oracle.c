@@ -182,30 +182,34 @@ float oracle_nvfp4_global_scale(float amax) {
   return amax > 0.0f ? amax / 2688.0f : 1.0f;
 }
 
+/* One block of 16 values, the steps above: returns the scale code and
+ * writes the 16 element codes. */
+static int nvfp4_block_codes(const float* xb, float g, int* c) {
+  const float six_g = 6.0f * g;
+  float ab = 0.0f, s, sg;
+  int sc, j;
+  for (j = 0; j < 16; ++j) if (fabsf(xb[j]) > ab) ab = fabsf(xb[j]);
+  sc = oracle_e4m3_encode((double)(ab / six_g));
+  s = (float)oracle_e4m3_decode(sc);
+  sg = s * g;
+  for (j = 0; j < 16; ++j) {
+    if (s == 0.0f || sg == 0.0f) c[j] = signbit(xb[j]) ? 8 : 0;
+    else c[j] = oracle_e2m1_encode((double)(xb[j] / sg));
+  }
+  return sc;
+}
+
 void oracle_nvfp4_quantize(const float* x, int64_t rows, int D, float g,
                            uint8_t* codes, uint8_t* sf) {
-  const float six_g = 6.0f * g;
   int64_t r;
   init_tables();
 #pragma omp parallel for schedule(static)
   for (r = 0; r < rows; ++r) {
-    int b, j;
+    int b, j, c[16];
     for (b = 0; b < D / 16; ++b) {
-      const float* xb = x + r * D + b * 16;
-      float ab = 0.0f, s, sg;
-      int sc;
-      for (j = 0; j < 16; ++j) if (fabsf(xb[j]) > ab) ab = fabsf(xb[j]);
-      sc = oracle_e4m3_encode((double)(ab / six_g));
-      sf[r * (D / 16) + b] = (uint8_t)sc;
-      s = (float)oracle_e4m3_decode(sc);
-      sg = s * g;
-      for (j = 0; j < 16; ++j) {
-        int c;
-        if (s == 0.0f || sg == 0.0f) c = signbit(xb[j]) ? 8 : 0;
-        else c = oracle_e2m1_encode((double)(xb[j] / sg));
-        if (j & 1) codes[r * (D / 2) + b * 8 + j / 2] |= (uint8_t)(c << 4);
-        else codes[r * (D / 2) + b * 8 + j / 2] = (uint8_t)c;
-      }
+      sf[r * (D / 16) + b] = (uint8_t)nvfp4_block_codes(x + r * D + b * 16, g, c);
+      for (j = 0; j < 16; j += 2)
+        codes[r * (D / 2) + b * 8 + j / 2] = (uint8_t)(c[j] | (c[j + 1] << 4));
     }
   }
 }
@@ -276,17 +280,70 @@ void oracle_delta_s(const float* qmean, const float* kc, int64_t T, int D, uint1
  * `rel` (relative) of the midpoint between two neighbouring magnitudes --
  * closer than the kernel's own computation of p can place it -- else the
  * rounded value ph itself.                                                  */
-static double e4m3_alternative(double a, double ph, double rel) {
-  int lo = 0, hi = 126;
+static double table_alternative(double a, double ph, double rel, const double* mag, int n) {
+  int lo = 0, hi = n - 1;
   double mid;
-  if (a >= g_e4m3_mag[126] || a <= 0.0) return ph;
+  if (a >= mag[n - 1] || a <= 0.0) return ph;
   while (hi - lo > 1) {
     int m = (lo + hi) / 2;
-    if (g_e4m3_mag[m] <= a) lo = m; else hi = m;
+    if (mag[m] <= a) lo = m; else hi = m;
   }
-  mid = 0.5 * (g_e4m3_mag[lo] + g_e4m3_mag[hi]);
+  mid = 0.5 * (mag[lo] + mag[hi]);
   if (fabs(a - mid) > rel * a) return ph;
-  return ph == g_e4m3_mag[lo] ? g_e4m3_mag[hi] : g_e4m3_mag[lo];
+  return ph == mag[lo] ? mag[hi] : mag[lo];
+}
+static double e4m3_alternative(double a, double ph, double rel) {
+  return table_alternative(a, ph, rel, g_e4m3_mag, 127);
+}
+
+/* NVFP4 P (the NVFP4 + NVFP4 precision assignment of MpFA §3.1, Fig. 3(a):
+ * P quantized with a scale per 16 elements along the keys, computed on the
+ * softmax path).  Reading: the O3 block steps above applied to x = fp32(p)
+ * over 16 consecutive keys (groups aligned at the KV block start; masked or
+ * absent keys count as p = 0), with the global scale fixed at
+ * G_P = fp32(1/2688), the NVFP4 scale that maps the bound p <= 1 to the
+ * largest representable product 6 * 448 (as the fixed 448 does for FP8 P).
+ * ph[i] = 448 * dec(code) * s * G_P, in the 448 units of the other formats.
+ * alt[i]: the value farthest from ph[i] among the other roundings that are
+ * equally valid when the scale decision (amax / fp32(6 G_P)) or the element
+ * decision (x / fp32(s G_P)) lies within `rel` of a midpoint; ph[i] when
+ * there is none.                                                            */
+static const float G_P = 1.0f / 2688.0f;
+static void nvfp4_p_values(int sc, const int* c, double* ph) {
+  const double s = oracle_e4m3_decode(sc);
+  int i;
+  for (i = 0; i < 16; ++i) ph[i] = 448.0 * oracle_e2m1_decode(c[i]) * s * (double)G_P;
+}
+static void nvfp4_p_block(const float* x, double rel, double* ph, double* alt) {
+  const float six_g = 6.0f * G_P;
+  double cand[16];
+  float ab = 0.0f;
+  int c[16], i, k, sc, scs[2], nsc = 1;
+  for (i = 0; i < 16; ++i) if (x[i] > ab) ab = x[i];
+  sc = nvfp4_block_codes(x, G_P, c);
+  nvfp4_p_values(sc, c, ph);
+  for (i = 0; i < 16; ++i) alt[i] = ph[i];
+  scs[0] = sc;
+  {
+    const double qs = (double)(ab / six_g), s = oracle_e4m3_decode(sc);
+    const double s_alt = e4m3_alternative(qs, s, rel);
+    if (s_alt != s) scs[nsc++] = oracle_e4m3_encode(s_alt);
+  }
+  for (k = 0; k < nsc; ++k) {
+    const float s = (float)oracle_e4m3_decode(scs[k]), sg = s * G_P;
+    int ck[16];
+    for (i = 0; i < 16; ++i)
+      ck[i] = (s == 0.0f || sg == 0.0f) ? 0 : oracle_e2m1_encode((double)(x[i] / sg));
+    nvfp4_p_values(scs[k], ck, cand);
+    for (i = 0; i < 16; ++i) {
+      const double qe = (s == 0.0f || sg == 0.0f) ? 0.0 : (double)(x[i] / sg);
+      const double e = oracle_e2m1_decode(ck[i]);
+      const double e_alt = table_alternative(qe, e, rel, g_e2m1_mag, 8);
+      const double v_alt = 448.0 * e_alt * (double)s * (double)G_P;
+      if (fabs(cand[i] - ph[i]) > fabs(alt[i] - ph[i])) alt[i] = cand[i];
+      if (fabs(v_alt - ph[i]) > fabs(alt[i] - ph[i])) alt[i] = v_alt;
+    }
+  }
 }
 
 /* Nearest bf16 value (8 significant bits) to a >= 0, ties to the even
@@ -320,7 +377,8 @@ static double bf16_alternative(double a, double ph, double rel) {
  * (equally valid) rounding of those keys can move acc.  It does not change
  * m, l or acc.
  * p_format: 0 = P not rounded (p^ = 448 p), 1 = E4M3 of 448 p (the method's
- * FP8 P), 2 = bf16 of 448 p (the BF16 P.V precision assignment).
+ * FP8 P), 2 = bf16 of 448 p (the BF16 P.V precision assignment), 3 = 448 x
+ * the NVFP4 value of p (nvfp4_p_block; the NVFP4 P.V assignment).
  * amb_rel: the relative distance to a midpoint below which both roundings
  * count as valid (2^-16 for an FP32 exp2; wider for an approximate one).    */
 void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
@@ -362,6 +420,28 @@ void oracle_attn_state(int D, int R, const double* q, const int64_t* row_pos,
       for (d = 0; d < D; ++d) acc[d] *= alpha;
       if (amb)
         for (d = 0; d < D; ++d) amb[d] *= alpha;
+      if (p_format == 3) {
+        int64_t g0;
+        for (g0 = b0; g0 < last; g0 += 16) {
+          const int n = (int)(last - g0 < 16 ? last - g0 : 16);
+          float x[16];
+          double ph[16], alt[16];
+          int i;
+          for (i = 0; i < 16; ++i) {
+            const double p = i < n ? exp2(lam * (s[g0 + i - b0] - mn)) : 0.0;
+            x[i] = (float)p;
+            l += p;
+          }
+          nvfp4_p_block(x, amb_rel, ph, alt);
+          for (i = 0; i < n; ++i) {
+            for (d = 0; d < D; ++d) acc[d] += ph[i] * v[(g0 + i) * D + d];
+            if (amb && alt[i] != ph[i])
+              for (d = 0; d < D; ++d) amb[d] += fabs(alt[i] - ph[i]) * fabs(v[(g0 + i) * D + d]);
+          }
+        }
+        m = mn;
+        continue;
+      }
       for (j = b0; j < last; ++j) {
         double p = exp2(lam * (s[j - b0] - mn));
         double ph = 448.0 * p, alt = ph;

@@ -76,6 +76,39 @@ def quantize_v_bf16(v):
     return bf16_rne(np.asarray(v, dtype=F32))
 
 
+def quantize_v_nvfp4(v):
+    """NVFP4 V for the NVFP4 + NVFP4 precision assignment (MpFA §3.1,
+    Fig. 3(a)): the P.V contraction runs over the keys, so V's 16-element
+    blocks run along the keys, per channel.  Reading: the O3 steps of
+    ``quantize_k`` (global scale from the amax of the whole V tensor, E4M3
+    scale per block, E2M1 codes) applied to the rows of V transposed per
+    (batch, KV head), keys past N padded with zeros (they change no block
+    amax).  Returns v_fp4 [B, Hkv, ceil(N/16), D, 8] u8 (byte t of (block kb,
+    channel d) holds keys 16 kb + 2t in the low nibble and 16 kb + 2t + 1 in
+    the high one), v_sf [B, Hkv, ceil(N/16), D] u8 and v_gscale."""
+    v = np.asarray(v, dtype=F32)
+    B, Hkv, N, D = v.shape
+    nb = (N + 15) // 16
+    g = nvfp4_global_scale(amax(v))
+    vp = np.zeros((B, Hkv, nb * 16, D), dtype=F32)
+    vp[:, :, :N] = v
+    vt = np.ascontiguousarray(vp.transpose(0, 1, 3, 2))  # [B, Hkv, D, keys]
+    codes, sf = nvfp4_quantize(vt, g)  # [B, Hkv, D, nb * 8], [B, Hkv, D, nb]
+    v_fp4 = np.ascontiguousarray(codes.reshape(B, Hkv, D, nb, 8).transpose(0, 1, 3, 2, 4))
+    v_sf = np.ascontiguousarray(sf.transpose(0, 1, 3, 2))
+    return {"v_fp4": v_fp4, "v_sf": v_sf, "v_gscale": np.float32(g)}
+
+
+def dequantize_v_nvfp4(vq, b, hk, n):
+    """The dequantized NVFP4 V of (b, KV head hk), keys 0 .. n-1: [n, D] FP64."""
+    codes = vq["v_fp4"][b, hk]  # [nb, D, 8]
+    sf = vq["v_sf"][b, hk]      # [nb, D]
+    nb, D = sf.shape
+    rows_c = np.ascontiguousarray(codes.transpose(1, 0, 2).reshape(D, nb * 8))
+    rows_s = np.ascontiguousarray(sf.T)
+    return nvfp4_dequantize(rows_c, rows_s, vq["v_gscale"]).T[:n]
+
+
 def quantize_q(q, q_mean=None):
     """NVFP4 of Q_c = fp32(Q - Qbar) (direct mode: Q_c = Q), global scale from the
     amax of the whole Q_c tensor of the call.  Returns (codes, scales, g)."""
@@ -150,8 +183,10 @@ class Operands:
 
     def __init__(self, q, k, v, scale, smooth, identity, q_mean=None, pv="fp8"):
         """pv: the P.V precision: "fp8" (the method: E4M3 P with the fixed
-        scale 448, FP8 V with a per-tensor scale) or "bf16" (P rounded to
-        bf16, V in bf16: the NVFP4 + BF16 assignment of MpFA §3.1)."""
+        scale 448, FP8 V with a per-tensor scale), "bf16" (P rounded to
+        bf16, V in bf16: the NVFP4 + BF16 assignment of MpFA §3.1) or
+        "nvfp4" (P and V in NVFP4 over 16-key blocks: the NVFP4 + NVFP4
+        assignment of MpFA §3.1)."""
         q = np.asarray(q, dtype=F32)
         k = np.asarray(k, dtype=F32)
         v = np.asarray(v, dtype=F32)
@@ -165,7 +200,7 @@ class Operands:
         self.k_mean = None
         self._delta = None
         self.pv = pv
-        self.p_format = "none" if identity else ("bf16" if pv == "bf16" else "e4m3")
+        self.p_format = "none" if identity else {"bf16": "bf16", "nvfp4": "nvfp4"}.get(pv, "e4m3")
         if identity:
             if smooth:
                 self.k_mean = channel_mean(k)
@@ -184,6 +219,9 @@ class Operands:
             qcodes, qsf, gq = quantize_q(q, None)
         if pv == "bf16":
             vq = {"v_bf16": quantize_v_bf16(v)}
+            self.s_v = 1.0
+        elif pv == "nvfp4":
+            vq = quantize_v_nvfp4(v)
             self.s_v = 1.0
         else:
             vq = quantize_v(v)
@@ -241,6 +279,8 @@ class Operands:
             return self._v[b, hk].astype(F64)
         if self.pv == "bf16":
             return bf16_to_f64(self.vq["v_bf16"][b, hk])
+        if self.pv == "nvfp4":
+            return dequantize_v_nvfp4(self.vq, b, hk, self.n_kv)
         return self._table[self.vq["v_fp8"][b, hk]]
 
     def delta(self, b, h):
@@ -258,7 +298,8 @@ def prefill_rows(q, k, v, scale, causal=True, smooth=True, identity=False, rows=
     """Causal (or full) prefill, MpFA §5.1 second stage, for the selected rows.
 
     pv="bf16" gives the NVFP4 + BF16 precision assignment (P and V in bf16,
-    MpFA §3.1) instead of the method's FP8 P.V.  amb_rel: the width of the
+    MpFA §3.1) and pv="nvfp4" the NVFP4 + NVFP4 one (P and V in NVFP4 over
+    16-key blocks) instead of the method's FP8 P.V.  amb_rel: the width of the
     rounding-ambiguity window of AMB (default: an FP32 exp2's, 2^-16).
 
     rows: None (every row) or an int array [R, 3] of (b, q-head, position).

@@ -188,7 +188,7 @@ static void attention(void) {
   }
   for (i = 0; i < N; ++i) delta[i] = 0.1 * nrand();
   for (i = 0; i < R * D; ++i) q[i] = nrand();
-  for (fmt = 0; fmt <= 2; ++fmt) {
+  for (fmt = 0; fmt <= 3; ++fmt) {
     oracle_attn_state(D, R, q, pos, k, v, delta, 0, N, 128, 0.0883883476, fmt, 0x1p-16, m, l,
                       acc, amb);
     for (r = 0; r < R; ++r) CHECK(isfinite(m[r]) && l[r] >= 1.0, "state of row %d", r);
