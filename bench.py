@@ -289,12 +289,18 @@ def _error_stats(got, ref):
 
 def _mode_outputs(mpfa, q, k, v, scale):
     """fp32 outputs of the three prefill modes on one set of device inputs:
-    smoothing by the sequence means, direct (no smoothing), per-tile means."""
+    smoothing by the sequence means, direct (no smoothing), per-tile means;
+    and of the smoothing mode with the other two P.V precision assignments
+    (bf16 P and V; NVFP4 P and V)."""
     import torch
     vq = mpfa.quantize_v(v)
     res = {}
     kq = mpfa.quantize_k(k, q=q)
     res["smooth"], _ = mpfa.prefill(q, kq, vq, scale, causal=True, out_dtype=torch.float32)
+    res["smooth_pv_bf16"], _ = mpfa.prefill_variant("pv_bf16", q, kq, mpfa.pack_v_bf16(v), scale,
+                                                    causal=True, out_dtype=torch.float32)
+    res["smooth_pv_nvfp4"], _ = mpfa.prefill_variant("pv_nvfp4", q, kq, mpfa.quantize_v_nvfp4(v),
+                                                     scale, causal=True, out_dtype=torch.float32)
     del kq
     kq = mpfa.quantize_k(k, smooth=False)
     res["direct"], _ = mpfa.prefill(q, kq, vq, scale, causal=True, out_dtype=torch.float32)
@@ -701,16 +707,18 @@ def main():
     # precision / placement variants (MpFA page section 3.1 Fig. 3(a), 7.4,
     # 5.1) on the same caches, each taking its query amax in its own pass like
     # the smoothing call they are compared with
-    vq16 = mpfa.pack_v_bf16(v)
+    var_vq = {"pv_bf16": mpfa.pack_v_bf16(v), "pv_nvfp4": mpfa.quantize_v_nvfp4(v)}
+    ws_p4 = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL_PV_NVFP4, B, Hq, Hkv, N),
+                        dtype=torch.uint8, device=dev)
     ms_var = {}
-    for name in ("elementwise", "poly_exp2", "pv_bf16"):
+    for name in ("elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"):
         def var_call(name=name):
-            mpfa.prefill_variant(name, q, kq, vq16 if name == "pv_bf16" else vq, cfg.scale,
-                                 causal=True, out=out, ws=ws_p)
+            mpfa.prefill_variant(name, q, kq, var_vq.get(name, vq), cfg.scale, causal=True,
+                                 out=out, ws=ws_p4 if name == "pv_nvfp4" else ws_p)
         ms_var[name] = time_calls(var_call, max(3, args.steps // 2), 1)
         log(f"[bench] variant {name}: {ms_var[name]:.3f} ms ({ms_var[name] / ms_smooth_own - 1:+.2%} "
             f"against the rank-one smoothing call)")
-    del vq16
+    del var_vq, ws_p4
     torch.cuda.empty_cache()
 
     # the unsmoothed (direct) prefill on its own uncentred cache
@@ -773,7 +781,10 @@ def main():
                for name, t in ms_var.items()},
             "what": {"elementwise": "Delta_S added per score on the VALU (MpFA 7.4 placement)",
                      "poly_exp2": "one exp2 in four by a fitted cubic (MpFA 5.1 split)",
-                     "pv_bf16": "P and V in bf16, P.V on bf16 MFMA (MpFA 3.1 NVFP4+BF16)"}},
+                     "pv_bf16": "P and V in bf16, P.V on bf16 MFMA (MpFA 3.1 NVFP4+BF16)",
+                     "pv_nvfp4": "P quantized to NVFP4 per 16 keys on the softmax path, V from "
+                                 "an NVFP4 cache (16-key blocks) expanded per call, P.V on f16 "
+                                 "MFMA over the exact values (MpFA 3.1 NVFP4+NVFP4)"}},
         "prefill_direct_ms": round(ms_direct, 4),
         "prefill_tile_mean": {"ms": round(ms_tile, 4),
                               "roofline": {"bound": "mfma", "achieved": round(ach_tile, 2),

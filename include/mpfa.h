@@ -86,6 +86,7 @@ extern "C" {
 #define MPFA_OP_QUANTIZE_V 1
 #define MPFA_OP_PREFILL 2
 #define MPFA_OP_DECODE 3
+#define MPFA_OP_PREFILL_PV_NVFP4 4 /* mpfa_prefill_pv_nvfp4 */
 
 /* Largest GQA group (Hq / Hkv) the decode kernel packs into one tile. */
 #define MPFA_DECODE_MAX_GROUP 8
@@ -298,7 +299,8 @@ int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv,
 
 /*
  * Precision and placement variants of the smoothing-mode prefill (paper
- * section 3.1, Fig. 3(a): NVFP4 + FP8 against NVFP4 + BF16; section 7.4
+ * section 3.1, Fig. 3(a): NVFP4 + FP8 against NVFP4 + BF16 and NVFP4 +
+ * NVFP4; section 7.4
  * "Compensation placement": the rank-one MMA against an element-wise add;
  * section 5.1: part of the exponentials by a polynomial on the FMA units).
  * They exist to measure those choices on gfx950; each computes what its
@@ -355,6 +357,47 @@ int mpfa_prefill_pv_bf16(const void* q, int q_dtype, int B, int Hq, int Hkv, int
                          const uint16_t* delta_s, float softmax_scale, int causal, void* out,
                          int out_dtype, float* lse_or_null, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * mpfa_quantize_v_nvfp4 -- the NVFP4 V cache of mpfa_prefill_pv_nvfp4.  The
+ * P.V contraction runs over the keys, so V's 16-element blocks run along the
+ * keys of each channel (paper section 3.1: block-scaled NVFP4 P.V).  With A
+ * the amax of the whole V tensor, g = A > 0 ? fp32(A / 2688) : 1 -> *v_gscale;
+ * per (16-key block kb, channel d): s = E4M3(fp32(amax / fp32(6 g))),
+ * code_t = E2M1(fp32(v_t / fp32(s g))) (the steps of mpfa_quantize_k_nvfp4),
+ * keys past N counting as zero.
+ *   v      [B, Hkv, N, 128] in v_dtype.
+ *   v_fp4  [B, Hkv, ceil(N/16), 128, 8] uint8: byte t of (kb, d) holds key
+ *          16 kb + 2t in the low nibble and key 16 kb + 2t + 1 in the high.
+ *   v_sf   [B, Hkv, ceil(N/16), 128] uint8 E4M3 block scales.
+ *   ws: mpfa_workspace_bytes(MPFA_OP_QUANTIZE_V, ...).
+ */
+int mpfa_quantize_v_nvfp4(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp4,
+                          uint8_t* v_sf, float* v_gscale, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * mpfa_prefill_pv_nvfp4 -- the NVFP4 + NVFP4 precision assignment (paper
+ * section 3.1, Fig. 3(a)): Q.K^T as in mpfa_prefill; in each 128-key block
+ * the p of every 16 consecutive keys (groups aligned at the block start,
+ * masked keys zero) are quantized on the softmax path to NVFP4 with the
+ * fixed global scale G_P = fp32(1/2688) (so p <= 1 maps to at most 6 x 448):
+ * amax, E4M3 scale s = E4M3(fp32(amax / fp32(6 G_P))), codes
+ * E2M1(fp32(p / fp32(s G_P))); V from mpfa_quantize_v_nvfp4 (v_fp4, v_sf,
+ * v_gscale replace v_fp8 and v_scale).  P.V multiplies the exact values
+ * (code x block scale, in FP16) on f16 matrix instructions with FP32
+ * accumulation; l sums the unquantized p; out_i = acc G_P g_V / l; lse as
+ * mpfa_prefill.  Smoothing or direct as mpfa_prefill.
+ *   ws: mpfa_workspace_bytes(MPFA_OP_PREFILL_PV_NVFP4, B, Hq, Hkv, N, 128, 1)
+ *       (mpfa_prefill's, plus the FP16 image of V: 256 bytes per key and KV
+ *       head, written by this call).
+ */
+int mpfa_prefill_pv_nvfp4(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                          const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                          const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp4,
+                          const uint8_t* v_sf, const float* v_gscale, const uint16_t* delta_s,
+                          float softmax_scale, int causal, void* out, int out_dtype,
+                          float* lse_or_null, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mpfa_prefill_tile_mean -- mpfa_prefill with the queries smoothed per

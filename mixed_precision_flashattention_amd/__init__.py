@@ -23,6 +23,7 @@ MPFA_OP_QUANTIZE_K = 0
 MPFA_OP_QUANTIZE_V = 1
 MPFA_OP_PREFILL = 2
 MPFA_OP_DECODE = 3
+MPFA_OP_PREFILL_PV_NVFP4 = 4
 MPFA_DECODE_MAX_GROUP = 8
 MPFA_DECODE_STATIC_SCRATCH_BYTES = 16777216
 HEAD_DIM = 128
@@ -33,7 +34,7 @@ EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4"
            "mpfa_append_kv_paged", "mpfa_prefill", "mpfa_prefill_with_q_amax", "mpfa_decode",
            "mpfa_decode_paged", "mpfa_prefill_tile_mean", "mpfa_prefill_elementwise",
            "mpfa_prefill_poly_exp2", "mpfa_pack_v_bf16", "mpfa_prefill_pv_bf16",
-           "mpfa_decode_static")
+           "mpfa_quantize_v_nvfp4", "mpfa_prefill_pv_nvfp4", "mpfa_decode_static")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -84,6 +85,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        P, i32, P, P, sz, P]
     L.mpfa_pack_v_bf16.restype = i32
     L.mpfa_pack_v_bf16.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+    L.mpfa_quantize_v_nvfp4.restype = i32
+    L.mpfa_quantize_v_nvfp4.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
+    L.mpfa_prefill_pv_nvfp4.restype = i32
+    L.mpfa_prefill_pv_nvfp4.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                        f32, i32, P, i32, P, P, sz, P]
     L.mpfa_prefill_tile_mean.restype = i32
     L.mpfa_prefill_tile_mean.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f32, i32,
                                          P, i32, P, P, P, sz, P]
@@ -256,6 +262,27 @@ def mpfa_prefill_pv_bf16(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_bf16, 
         int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     _raise("mpfa_prefill_pv_bf16", st)
+
+
+def mpfa_quantize_v_nvfp4(v, v_fp4, v_sf, v_gscale, ws, stream=None):
+    _check(v, v_fp4, v_sf, v_gscale, ws)
+    B, Hkv, N, D = v.shape
+    st = load_library().mpfa_quantize_v_nvfp4(_ptr(v), _dtype_code(v), B, Hkv, N, D, _ptr(v_fp4),
+                                              _ptr(v_sf), _ptr(v_gscale), _ptr(ws),
+                                              ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_quantize_v_nvfp4", st)
+
+
+def mpfa_prefill_pv_nvfp4(q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp4, v_sf, v_gscale,
+                          delta_s, softmax_scale, causal, out, lse, ws, stream=None):
+    _check(q, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp4, v_sf, v_gscale, delta_s, out, lse, ws)
+    B, Hq, N, D = q.shape
+    st = load_library().mpfa_prefill_pv_nvfp4(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, N, D, _ptr(q_mean), _ptr(k_mean), _ptr(k_fp4),
+        _ptr(k_sf), _ptr(k_gscale), _ptr(v_fp4), _ptr(v_sf), _ptr(v_gscale), _ptr(delta_s),
+        float(softmax_scale), int(bool(causal)), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _raise("mpfa_prefill_pv_nvfp4", st)
 
 
 def mpfa_prefill_tile_mean(q, Hkv, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v_scale, softmax_scale,
@@ -474,13 +501,28 @@ def pack_v_bf16(v, stream=None):
     return {"v_bf16": out}
 
 
+def quantize_v_nvfp4(v, stream=None):
+    """Allocate and fill the NVFP4 V cache of the NVFP4 P.V variant (16-key
+    blocks per channel, see mpfa.h)."""
+    import torch
+    B, Hkv, N, D = v.shape
+    nb = (N + 15) // 16
+    out = {"v_fp4": torch.empty((B, Hkv, nb, D, 8), dtype=torch.uint8, device=v.device),
+           "v_sf": torch.empty((B, Hkv, nb, D), dtype=torch.uint8, device=v.device),
+           "v_gscale": torch.empty(1, dtype=torch.float32, device=v.device)}
+    ws = _workspace(MPFA_OP_QUANTIZE_V, B, 0, Hkv, N, 1, v.device)
+    mpfa_quantize_v_nvfp4(v, out["v_fp4"], out["v_sf"], out["v_gscale"], ws, stream=stream)
+    return out
+
+
 def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=None, with_lse=False,
                     ws=None, out=None, lse=None, stream=None):
     """One of the prefill's precision / placement variants on the caches of
     quantize_k (smoothing iff kq holds delta_s): "elementwise" (Delta_S added
     per score on the vector ALUs; smoothing only), "poly_exp2" (one exponential
-    in four by a cubic), "pv_bf16" (vq from pack_v_bf16: bf16 P and V).  The
-    query amax is taken in the call's own pass.  Returns (out, lse or None)."""
+    in four by a cubic), "pv_bf16" (vq from pack_v_bf16: bf16 P and V),
+    "pv_nvfp4" (vq from quantize_v_nvfp4: NVFP4 P and V).  The query amax is
+    taken in the call's own pass.  Returns (out, lse or None)."""
     import torch
     B, Hq, N, D = q.shape
     Hkv = kq["k_fp4"].shape[1]
@@ -490,7 +532,8 @@ def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=No
     if with_lse and lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = _workspace(MPFA_OP_PREFILL, B, Hq, Hkv, N, 1, q.device)
+        op = MPFA_OP_PREFILL_PV_NVFP4 if variant == "pv_nvfp4" else MPFA_OP_PREFILL
+        ws = _workspace(op, B, Hq, Hkv, N, 1, q.device)
     smooth = kq.get("delta_s") is not None
     common = (q, Hkv, kq.get("q_mean") if smooth else None, kq.get("k_mean") if smooth else None,
               kq["k_fp4"], kq["k_sf"], kq["k_gscale"])
@@ -498,6 +541,9 @@ def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=No
     if variant == "pv_bf16":
         mpfa_prefill_pv_bf16(*common, vq["v_bf16"], kq.get("delta_s") if smooth else None, *tail,
                              stream=stream)
+    elif variant == "pv_nvfp4":
+        mpfa_prefill_pv_nvfp4(*common, vq["v_fp4"], vq["v_sf"], vq["v_gscale"],
+                              kq.get("delta_s") if smooth else None, *tail, stream=stream)
     elif variant in ("elementwise", "poly_exp2"):
         _prefill_variant(f"mpfa_prefill_{variant}", *common, vq["v_fp8"], vq["v_scale"],
                          kq.get("delta_s") if smooth else None, *tail, stream=stream)

@@ -51,14 +51,18 @@ inline DecodeWs decode_layout(int B, int Hq, int P) {
 // Prefill: the Q amax slots, then K~ (the K cache expanded to FP16 block
 // images).
 struct PrefillWs {
-  size_t amax, k_f16, total;
+  size_t amax, k_f16, v_img, total;
 };
-inline PrefillWs prefill_layout(int B, int Hkv, int N) {
+// v_image: also the FP16 image of an NVFP4 V cache (NVFP4 P.V variant)
+inline PrefillWs prefill_layout(int B, int Hkv, int N, bool v_image = false) {
   PrefillWs w;
   w.amax = 0;
   w.k_f16 = kAmaxBytes;
   // K~ block images: 32 KB per (batch, KV head, 128-key block)
   w.total = align_up(w.k_f16 + (size_t)B * Hkv * ((N + kBlk - 1) / kBlk) * kBlk * kD * 2);
+  w.v_img = w.total;
+  // V image: 8 KB per (batch, KV head, 32-key tile)
+  if (v_image) w.total = align_up(w.v_img + (size_t)B * Hkv * ((N + 31) / 32) * 32 * kD * 2);
   return w;
 }
 
@@ -95,6 +99,8 @@ size_t mpfa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int nu
       return kAmaxBytes;
     case MPFA_OP_PREFILL:
       return prefill_layout(B, Hkv, N).total;
+    case MPFA_OP_PREFILL_PV_NVFP4:
+      return prefill_layout(B, Hkv, N, true).total;
     case MPFA_OP_DECODE:
       if (num_splits < 1 || Hq < 1) return 0;
       return decode_layout(B, Hq, num_splits).total;
@@ -297,30 +303,34 @@ namespace {
 
 // The prefill call; q_amax NULL: the Q_c amax comes from a pass over Q here.
 // variant: the attention kernel's precision / placement variant (0 = the
-// method); variant 3 reads V from v_bf16 instead of v_fp8 and v_scale.
+// method); variant 3 reads V from v_bf16 instead of v_fp8 and v_scale;
+// variant 4 reads the NVFP4 V cache v_fp4 / v_sf with its global scale in
+// v_scale and expands it into the workspace first.
 int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                  const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                  const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
                  const float* v_scale, const uint16_t* delta_s, const float* q_amax,
                  float softmax_scale, int causal, void* out, int out_dtype, float* lse, void* ws,
                  size_t ws_bytes, void* stream, int variant = 0,
-                 const uint16_t* v_bf16 = nullptr) {
+                 const uint16_t* v_bf16 = nullptr, const uint8_t* v_fp4 = nullptr,
+                 const uint8_t* v_sf = nullptr) {
   int st = check_sizes(B, Hkv, N, D);
   if (st) return st;
   if ((st = check_heads(Hq, Hkv, B))) return st;
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return MPFA_ERR_UNSUPPORTED;
-  const bool v16 = variant == kVarPvBf16;
+  const bool v16 = variant == kVarPvBf16, v4 = variant == kVarPvNvfp4;
   if (!q || !k_fp4 || !k_sf || !k_gscale || !out || !ws) return MPFA_ERR_INVALID;
-  if (v16 ? !v_bf16 : (!v_fp8 || !v_scale)) return MPFA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) ||
-      !aligned16(v16 ? (const void*)v_bf16 : (const void*)v_fp8) || !aligned16(out) ||
-      !aligned16(ws) || (lse && !aligned16(lse)))
+  if (v16 ? !v_bf16 : (v4 ? (!v_fp4 || !v_sf || !v_scale) : (!v_fp8 || !v_scale)))
+    return MPFA_ERR_INVALID;
+  const void* v_main = v16 ? (const void*)v_bf16 : (v4 ? (const void*)v_fp4 : (const void*)v_fp8);
+  if (!aligned16(q) || !aligned16(k_fp4) || !aligned16(k_sf) || !aligned16(v_main) ||
+      (v4 && !aligned16(v_sf)) || !aligned16(out) || !aligned16(ws) || (lse && !aligned16(lse)))
     return MPFA_ERR_INVALID;
   if (delta_s && (!q_mean || !k_mean || !aligned16(q_mean) || !aligned16(k_mean) ||
                   !aligned16(delta_s)))
     return MPFA_ERR_INVALID;
   if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return MPFA_ERR_INVALID;
-  const PrefillWs L = prefill_layout(B, Hkv, N);
+  const PrefillWs L = prefill_layout(B, Hkv, N, v4);
   if (ws_bytes < L.total) return MPFA_ERR_WORKSPACE;
   const int n_units = (N + 255) / 256;
   if ((int64_t)n_units * B * Hq > (int64_t)INT32_MAX) return MPFA_ERR_INVALID;
@@ -328,6 +338,8 @@ int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   hipStream_t s = (hipStream_t)stream;
   uint32_t* amax = (uint32_t*)((uint8_t*)ws + L.amax);
   uint8_t* k_f16 = (uint8_t*)ws + L.k_f16;
+  uint16_t* v_img = (uint16_t*)((uint8_t*)ws + L.v_img);
+  if (v4) launch_expand_v_nvfp4(v_fp4, v_sf, B * Hkv, N, v_img, s);
   // Q_c amax as per-workgroup maxima, folded by the K expansion that follows
   // (more heads than partial slots: cleared slots, atomics and a fold)
   // (given by the caller: no pass at all)
@@ -367,7 +379,7 @@ int prefill_impl(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int 
   p.q_amax = q_amax ? reinterpret_cast<const uint32_t*>(q_amax) : amax;
   p.n_units = n_units;
   p.variant = variant;
-  p.v_bf16 = v16 ? v_bf16 : nullptr;
+  p.v_bf16 = v16 ? v_bf16 : (v4 ? v_img : nullptr);
   launch_prefill(p, s);
   return launch_status();
 }
@@ -432,6 +444,41 @@ int mpfa_prefill_pv_bf16(const void* q, int q_dtype, int B, int Hq, int Hkv, int
   return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, nullptr,
                       nullptr, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
                       lse_or_null, ws, ws_bytes, stream, kVarPvBf16, v_bf16);
+}
+
+int mpfa_prefill_pv_nvfp4(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                          const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                          const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp4,
+                          const uint8_t* v_sf, const float* v_gscale, const uint16_t* delta_s,
+                          float softmax_scale, int causal, void* out, int out_dtype,
+                          float* lse_or_null, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, nullptr,
+                      v_gscale, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream, kVarPvNvfp4, nullptr, v_fp4, v_sf);
+}
+
+int mpfa_quantize_v_nvfp4(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint8_t* v_fp4,
+                          uint8_t* v_sf, float* v_gscale, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int st = check_sizes(B, Hkv, N, D);
+  if (st) return st;
+  if (!dtype_ok(v_dtype)) return MPFA_ERR_UNSUPPORTED;
+  if (!v || !v_fp4 || !v_sf || !v_gscale || !ws) return MPFA_ERR_INVALID;
+  if (!aligned16(v) || !aligned16(v_fp4) || !aligned16(v_sf) || !aligned16(ws))
+    return MPFA_ERR_INVALID;
+  if (ws_bytes < kAmaxBytes) return MPFA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = (uint32_t*)ws;
+  const int vb = v_dtype == MPFA_BF16;
+  const int n_part = launch_centered_amax_partials(v, vb, B * Hkv, N, nullptr, (float*)ws, s);
+  if (n_part > 0) {
+    launch_partials_fold((const float*)ws, n_part, amax, s);
+  } else {
+    launch_fill_u32(amax, kAmaxBytes / 4, 0u, s);
+    launch_centered_amax(v, vb, B * Hkv, N, nullptr, amax, s);
+  }
+  launch_quantize_v_nvfp4(v, vb, B * Hkv, N, amax, v_gscale, v_fp4, v_sf, s);
+  return launch_status();
 }
 
 int mpfa_pack_v_bf16(const void* v, int v_dtype, int B, int Hkv, int N, int D, uint16_t* v_bf16,

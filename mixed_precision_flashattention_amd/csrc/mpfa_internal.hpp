@@ -7,8 +7,12 @@ namespace mpfa {
 
 // Precision / placement variants of the prefill attention kernel
 // (PrefillParams::variant): the library's kernel, element-wise compensation,
-// polynomial exp2 for one exponential in four, bf16 P.V.
-constexpr int kVarNone = 0, kVarElementwise = 1, kVarPolyExp2 = 2, kVarPvBf16 = 3;
+// polynomial exp2 for one exponential in four, bf16 P.V, NVFP4 P.V.
+constexpr int kVarNone = 0, kVarElementwise = 1, kVarPolyExp2 = 2, kVarPvBf16 = 3,
+              kVarPvNvfp4 = 4;
+// The fixed NVFP4 global scale of P in the NVFP4 P.V variant: fp32(1/2688)
+// maps the bound p <= 1 to the largest E2M1 x E4M3 product, 6 x 448.
+constexpr float kNvfp4PScale = 1.0f / 2688.0f;
 
 struct PrefillParams {
   const void* q;
@@ -31,9 +35,10 @@ struct PrefillParams {
   int n_units;             // 256-row query units per (batch, head)
   // precision / placement variant of the attention kernel (0: the library's
   // kernel; 1: element-wise compensation; 2: polynomial exp2 for one
-  // exponential in four; 3: bf16 P.V over v_bf16)
+  // exponential in four; 3: bf16 P.V over v_bf16; 4: NVFP4 P.V over v_bf16
+  // holding the FP16 image of the NVFP4 V cache, v_scale its global scale)
   int variant;
-  const uint16_t* v_bf16;  // variant 3: the bf16 V cache (tiled), else NULL
+  const uint16_t* v_bf16;  // variants 3 and 4: tiled 16-bit V, else NULL
 };
 
 struct DecodeParams {
@@ -111,6 +116,11 @@ void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const fl
                              const uint32_t* q_ext, float* q_amax, hipStream_t st);
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
                     const float* q_mean, uint16_t* delta, hipStream_t st);
+// NVFP4 V along the keys: codes [BH, ceil(N/16), 128, 8 bytes] (key 2t of a
+// block in the low nibble of byte t), scales [BH, ceil(N/16), 128], global
+// scale from *amax written to gscale.
+void launch_quantize_v_nvfp4(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
+                             float* gscale, uint8_t* codes, uint8_t* sf, hipStream_t st);
 void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
                              float* vscale, uint8_t* out, hipStream_t st);
 
@@ -136,6 +146,11 @@ void launch_prefill(const PrefillParams& p, hipStream_t st);
 // bf16 V cache of the bf16 P.V variant: [BH, ceil(N/32), 4, 128, 8] bf16
 // (token t, channel d at [t/32][(t%32)/8][d][t%8]), zero past N.
 void launch_pack_v_bf16(const void* v, int is_bf16, int BH, int N, uint16_t* out, hipStream_t st);
+// FP16 image of an NVFP4 V cache (launch_quantize_v_nvfp4) in the layout of
+// the bf16 V cache: code value x block scale, exact in FP16 (the global scale
+// stays out); zero past N.
+void launch_expand_v_nvfp4(const uint8_t* codes, const uint8_t* sf, int BH, int N, uint16_t* out,
+                           hipStream_t st);
 
 // decode.hip
 void launch_decode(const DecodeParams& p, hipStream_t st);

@@ -202,7 +202,14 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
 //     path instead of the hardware exp2 (the split the paper's B200 kernel
 //     uses to relieve its transcendental unit);
 //   kVarPvBf16: P rounded to bf16 and V from a bf16 cache, P.V on bf16 MFMA
-//     (the NVFP4 + BF16 precision assignment).
+//     (the NVFP4 + BF16 precision assignment);
+//   kVarPvNvfp4: P quantized to NVFP4 per 16 keys on the softmax path (amax,
+//     E4M3 scale, correctly rounded quotients, E2M1 codes; global scale
+//     fp32(1/2688)) and V from an NVFP4 cache with 16-key blocks, both
+//     expanded to exact FP16 values (code x block scale) so that P.V runs
+//     on f16 MFMA (the NVFP4 + NVFP4 precision assignment: gfx950's
+//     block-scaled FP4 MFMA takes power-of-two scales per 32 elements, not
+//     E4M3 scales per 16).
 // P of one block as the B operands of the P.V products: E4M3, 32 keys per
 // 32x32x64 operand (64 bytes per lane), or bf16 for the bf16 variant, 8 keys
 // per 32x32x16 operand (128 bytes per lane): w[t][u] holds keys 8u .. 8u + 7
@@ -213,6 +220,10 @@ struct PRegs {
 };
 template <>
 struct PRegs<kVarPvBf16> {
+  i32x4 w[4][2];
+};
+template <>
+struct PRegs<kVarPvNvfp4> {  // the same layout, FP16 values
   i32x4 w[4][2];
 };
 
@@ -247,12 +258,14 @@ __device__ __forceinline__ i32x4 v_operand_bf16(const uint8_t* vblk, int i, int 
   return *reinterpret_cast<const i32x4*>(vblk + (2 * (t >> 1) + h) * kVBf16TileBytes +
                                          (2 * (t & 1) + u) * (kD * 16) + (32 * dt + col) * 16);
 }
-// O^T += V^T P^T for one block on bf16 MFMA (32 MFMAs: 8 key steps of 16 x 4
-// head-dim tiles); the V operand of MFMA i + 1 is read while MFMA i runs.  The
-// k slots of a step are keys 8u .. 8u + 7 of tile t in lane half 0 and the
-// same offsets 32 keys on in lane half 1, matching the P operand's keys.
-__device__ __forceinline__ void pv_block_bf16(f32x16 (&o)[4], const uint8_t* vblk,
-                                              const PRegs<kVarPvBf16>& pb, int h, int col) {
+// O^T += V^T P^T for one block on bf16 (or, F16, f16) MFMA (32 MFMAs: 8 key
+// steps of 16 x 4 head-dim tiles); the V operand of MFMA i + 1 is read while
+// MFMA i runs.  The k slots of a step are keys 8u .. 8u + 7 of tile t in lane
+// half 0 and the same offsets 32 keys on in lane half 1, matching the P
+// operand's keys.
+template <bool F16>
+__device__ __forceinline__ void pv_block_16(f32x16 (&o)[4], const uint8_t* vblk,
+                                            const i32x4 (&w)[4][2], int h, int col) {
   i32x4 va[2];
   va[0] = v_operand_bf16(vblk, 0, h, col);
 #pragma unroll
@@ -260,7 +273,8 @@ __device__ __forceinline__ void pv_block_bf16(f32x16 (&o)[4], const uint8_t* vbl
     if (i + 1 < 32) va[(i + 1) & 1] = v_operand_bf16(vblk, i + 1, h, col);
     __builtin_amdgcn_sched_barrier(0);
     const int ku = i >> 2;
-    o[i & 3] = mfma32_bf16(va[i & 1], pb.w[ku >> 1][ku & 1], o[i & 3]);
+    o[i & 3] = F16 ? mfma32_f16(va[i & 1], w[ku >> 1][ku & 1], o[i & 3])
+                   : mfma32_bf16(va[i & 1], w[ku >> 1][ku & 1], o[i & 3]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -277,8 +291,8 @@ __device__ __forceinline__ i32x8 v_operand(const uint8_t* vblk, int i, int h, in
 template <int VAR>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[4], const uint8_t* vblk, const PRegs<VAR>& pr,
                                          int h, int col) {
-  if constexpr (VAR == kVarPvBf16) {
-    pv_block_bf16(o, vblk, pr, h, col);
+  if constexpr (VAR == kVarPvBf16 || VAR == kVarPvNvfp4) {
+    pv_block_16<VAR == kVarPvNvfp4>(o, vblk, pr.w, h, col);
   } else {
     i32x8 va[2];
     va[0] = v_operand(vblk, 0, h, col);
@@ -345,8 +359,36 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], PR
   mx = max_halves(mx);
   const float m_new = fmaxf(m_run, mx);
   const float alpha = fast_exp2(lam * (m_run - m_new));
-  const float nb = kLog2_448 - lam * m_new;
   m_run = m_new;
+  if constexpr (VAR == kVarPvNvfp4) {
+    // p itself (no 448 in the exponent): each 16-key score tile row is one
+    // NVFP4 group of P, quantized as the query blocks are and expanded to
+    // FP16 code value x block scale for the f16 P.V MFMA
+    const float nb = -lam * m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float e[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(s[t][v], lam, nb));
+#pragma unroll
+      for (int v = 0; v < 16; v += 4) lsum += (e[v] + e[v + 1]) + (e[v + 2] + e[v + 3]);
+      uint32_t w[2], pk[8];
+      const uint32_t sc = nvfp4_block_packed(e, kNvfp4PScale, w);
+      const f16x2 s2 = e4m3_scale_f16x2(sc);
+      expand_fp4x8(w[0], s2, pk);
+      expand_fp4x8(w[1], s2, pk + 4);
+      pr.w[t][0] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+      pr.w[t][1] = i32x4{(int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+    }
+    l_run = fmaf(alpha, l_run, lsum);
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    return;
+  }
+  const float nb = kLog2_448 - lam * m_new;
 
   float lsum;
 #pragma unroll
@@ -434,7 +476,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // a rank-one compensation step (the element-wise variant adds Delta_S in
   // the softmax instead)
   constexpr bool RANK1 = (SMOOTH && VAR != kVarElementwise) || TILE;
-  constexpr bool PV16 = VAR == kVarPvBf16;
+  constexpr bool PV16 = VAR == kVarPvBf16 || VAR == kVarPvNvfp4;  // 16-bit V blocks
   constexpr int NKB = TILE ? 3 : 2;       // K~ block buffers
   __shared__ __align__(16) uint8_t smem_k[NKB][kBlk * kRowBytes];  // K~ blocks
   __shared__ __align__(16) uint8_t smem_v[2][PV16 ? kVBf16BlockBytes : kVBlockBytes];  // V blocks
@@ -459,7 +501,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float gQ = nvfp4_global_scale(__uint_as_float(*p.q_amax));
   const int n_qtiles = (N + kBlk - 1) / kBlk;  // query tiles of the per-tile means
   const float gK = *p.k_gscale;
-  const float sV = PV16 ? 1.0f : *p.v_scale;  // a bf16 V cache is unscaled
+  // a bf16 V cache is unscaled; NVFP4 P.V: the two global scales
+  const float sV = VAR == kVarPvNvfp4 ? kNvfp4PScale * *p.v_scale : (PV16 ? 1.0f : *p.v_scale);
   const float gg = gQ * gK;
   const float lam = p.scale * kLog2e * gg;  // exp2 constant per unit of the MFMA score
 
@@ -707,7 +750,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   if (p.lse && h == 0 && row_ok)
     p.lse[(int64_t)bh * N + my_row] =
-        kLn2 * (lam * m_run + log2f(l_tot)) - kLn2 * kLog2_448 + lse_off;
+        kLn2 * (lam * m_run + log2f(l_tot)) - (VAR == kVarPvNvfp4 ? 0.0f : kLn2 * kLog2_448) +
+        lse_off;
 }
 
 // K~ = E2M1 code value x E4M3 block scale in FP16, written as block images
@@ -825,6 +869,42 @@ void launch_pack_v_bf16(const void* v, int is_bf16, int BH, int N, uint16_t* out
                      is_bf16, N, ntiles, n_threads, reinterpret_cast<uint4*>(out));
 }
 
+// FP16 image of the NVFP4 V cache (NVFP4 P.V variant), the bf16 V cache's
+// layout: thread g writes the 16 bytes of (tile, group of 8 keys, channel d),
+// the group's 8 codes (one word of the channel's 16-key block) times the
+// block scale by the hardware FP4 -> FP16 conversion and one packed multiply;
+// zero past the last 16-key block.
+__global__ __launch_bounds__(256) void k_expand_v_nvfp4(const uint2* __restrict__ codes,
+                                                        const uint8_t* __restrict__ sf, int nb16,
+                                                        int ntiles, int64_t n_threads,
+                                                        uint4* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n_threads) return;
+  const int d = (int)(g & (kD - 1));
+  const int64_t r = g >> 7;  // (bh * ntiles + tile) * 4 + group
+  const int grp = (int)(r & 3);
+  const int64_t tb = r >> 2;
+  const int64_t bh = tb / ntiles;
+  const int t0 = (int)(tb - bh * ntiles) * 32 + grp * 8;
+  const int kb = t0 >> 4;
+  uint32_t w4[4] = {0u, 0u, 0u, 0u};
+  if (kb < nb16) {
+    const int64_t o = (bh * nb16 + kb) * kD + d;
+    const uint2 c = codes[o];
+    expand_fp4x8((t0 & 8) ? c.y : c.x, e4m3_scale_f16x2(sf[o]), w4);
+  }
+  out[g] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+}
+
+void launch_expand_v_nvfp4(const uint8_t* codes, const uint8_t* sf, int BH, int N, uint16_t* out,
+                           hipStream_t st) {
+  const int ntiles = (N + 31) / 32, nb16 = (N + 15) / 16;
+  const int64_t n_threads = (int64_t)BH * ntiles * 4 * kD;
+  hipLaunchKernelGGL(k_expand_v_nvfp4, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint2*>(codes), sf, nb16, ntiles, n_threads,
+                     reinterpret_cast<uint4*>(out));
+}
+
 void launch_prefill(const PrefillParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((int64_t)p.n_units * p.B * p.Hq);
   const dim3 g(grid), b(512);
@@ -835,12 +915,14 @@ void launch_prefill(const PrefillParams& p, hipStream_t st) {
       case kVarElementwise: hipLaunchKernelGGL((k_prefill<1, kVarElementwise>), g, b, 0, st, p); break;
       case kVarPolyExp2: hipLaunchKernelGGL((k_prefill<1, kVarPolyExp2>), g, b, 0, st, p); break;
       case kVarPvBf16: hipLaunchKernelGGL((k_prefill<1, kVarPvBf16>), g, b, 0, st, p); break;
+      case kVarPvNvfp4: hipLaunchKernelGGL((k_prefill<1, kVarPvNvfp4>), g, b, 0, st, p); break;
       default: hipLaunchKernelGGL((k_prefill<1, kVarNone>), g, b, 0, st, p); break;
     }
   } else {
     switch (p.variant) {
       case kVarPolyExp2: hipLaunchKernelGGL((k_prefill<0, kVarPolyExp2>), g, b, 0, st, p); break;
       case kVarPvBf16: hipLaunchKernelGGL((k_prefill<0, kVarPvBf16>), g, b, 0, st, p); break;
+      case kVarPvNvfp4: hipLaunchKernelGGL((k_prefill<0, kVarPvNvfp4>), g, b, 0, st, p); break;
       default: hipLaunchKernelGGL((k_prefill<0, kVarNone>), g, b, 0, st, p); break;
     }
   }

@@ -539,6 +539,36 @@ __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, 
   *reinterpret_cast<uint4*>(tbase + kD * 16 + d * 16) = src[1];  // tokens 16 .. 31
 }
 
+// NVFP4 V for the NVFP4 P.V variant (paper section 3.1, Fig. 3(a)): the P.V
+// contraction runs over the keys, so the 16-element blocks run along the keys
+// of one channel.  One 128-thread block per (16-key block, batch x KV head):
+// thread d gathers channel d's 16 keys (each key row is read coalesced
+// across the block; keys past N are zero), quantizes them with the global
+// scale of the tensor amax and stores 8 code bytes and the scale byte.
+__global__ __launch_bounds__(128) void k_quantize_v_nvfp4(const void* __restrict__ v, int is_bf16,
+                                                          int N, int nb16,
+                                                          const uint32_t* __restrict__ amax,
+                                                          float* __restrict__ gscale_out,
+                                                          uint2* __restrict__ codes,
+                                                          uint8_t* __restrict__ sf) {
+  const float g = nvfp4_global_scale(__uint_as_float(*amax));
+  const int kb = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int d = threadIdx.x;
+  if (kb == 0 && bh == 0 && d == 0) *gscale_out = g;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = 16 * kb + i;
+    x[i] = t < N ? load_elem(v, (bh * N + t) * kD + d, is_bf16) : 0.0f;
+  }
+  uint32_t w[2];
+  const uint32_t sc = nvfp4_block_packed(x, g, w);
+  const int64_t o = (bh * nb16 + kb) * kD + d;
+  codes[o] = make_uint2(w[0], w[1]);
+  sf[o] = (uint8_t)sc;
+}
+
 // Decode-time cache write (paper section 6 "Online quantization": the new
 // token is centred against the frozen per-request means and quantized with
 // the cache's frozen scales; its compensation entries are written in the
@@ -753,6 +783,13 @@ void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const ui
   const int n_tiles = (N + 31) / 32;
   hipLaunchKernelGGL(k_quantize_v, dim3(n_tiles, BH), dim3(128), 0, st, v, is_bf16, N, n_tiles,
                      amax, vscale, out);
+}
+
+void launch_quantize_v_nvfp4(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
+                             float* gscale, uint8_t* codes, uint8_t* sf, hipStream_t st) {
+  const int nb16 = (N + 15) / 16;
+  hipLaunchKernelGGL(k_quantize_v_nvfp4, dim3(nb16, BH), dim3(128), 0, st, v, is_bf16, N, nb16, amax,
+                     gscale, reinterpret_cast<uint2*>(codes), sf);
 }
 
 void launch_append_kv(const void* k_new, const void* v_new, int is_bf16, int B, int Hkv, int G,

@@ -99,7 +99,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_constants_match_header():
     import mixed_precision_flashattention_amd as mpfa
     for name in ("MPFA_F32", "MPFA_BF16", "MPFA_OP_QUANTIZE_K", "MPFA_OP_QUANTIZE_V",
-                 "MPFA_OP_PREFILL", "MPFA_OP_DECODE", "MPFA_DECODE_MAX_GROUP",
+                 "MPFA_OP_PREFILL", "MPFA_OP_DECODE", "MPFA_OP_PREFILL_PV_NVFP4",
+                 "MPFA_DECODE_MAX_GROUP",
                  "MPFA_DECODE_STATIC_SCRATCH_BYTES"):
         assert getattr(mpfa, name) == header_define(name), name
 
@@ -129,6 +130,10 @@ def test_workspace_sizes(lib):
     assert ws(2, 1, 32, 8, 1024, 128, 1) == AMAX + 8 * 8 * 32768
     assert ws(2, 2, 32, 8, 1001, 128, 1) == AMAX + 2 * 8 * 8 * 32768
     assert ws(2, 1, 4, 1, 1, 128, 1) == AMAX + 32768
+    # NVFP4 P.V: also the FP16 image of V, 8 KB per (batch, KV head, 32-key tile)
+    assert ws(4, 1, 32, 8, 1024, 128, 1) == ws(2, 1, 32, 8, 1024, 128, 1) + 8 * 32 * 8192
+    assert ws(4, 2, 32, 8, 1001, 128, 1) == ws(2, 2, 32, 8, 1001, 128, 1) + 2 * 8 * 32 * 8192
+    assert ws(4, 1, 4, 1, 1, 128, 1) == AMAX + 32768 + 8192
     assert ws(9, 1, 32, 8, 1024, 128, 1) == 0
     assert ws(3, 1, 32, 8, 1024, 128, 0) == 0
     assert ws(0, 0, 32, 8, 1024, 128, 1) == 0
@@ -251,6 +256,35 @@ def test_quantizers_reject_bad_arguments(lib):
     assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, 256, None) == -2
     assert qv(f.p, 1, 1, 2, 64, 128, None, f.p, f.p, 256, None) == -1
     assert qv(f.p, 1, 1, 2, 64, 128, f.p, f.p, f.p, 8, None) == -3
+
+
+def test_nvfp4_pv_entry_points_reject_bad_arguments(lib):
+    f = _Fake()
+    qv = lib.mpfa_quantize_v_nvfp4
+    # (v, v_dtype, B, Hkv, N, D, v_fp4, v_sf, v_gscale, ws, ws_bytes, stream)
+    assert qv(f.p, 1, 1, 2, 64, 64, f.p, f.p, f.p, f.p, 1 << 16, None) == -2
+    assert qv(f.p, 3, 1, 2, 64, 128, f.p, f.p, f.p, f.p, 1 << 16, None) == -2
+    assert qv(f.p, 1, 1, 2, 64, 128, f.p, None, f.p, f.p, 1 << 16, None) == -1
+    assert qv(f.p, 1, 1, 2, 64, 128, f.p, f.mis, f.p, f.p, 1 << 16, None) == -1
+    assert qv(f.p, 1, 1, 2, 0, 128, f.p, f.p, f.p, f.p, 1 << 16, None) == -1
+    assert qv(f.p, 1, 1, 2, 64, 128, f.p, f.p, f.p, f.p, 8, None) == -3
+    pv = lib.mpfa_prefill_pv_nvfp4
+
+    def call(**kw):
+        a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p,
+                 k_fp4=f.p, k_sf=f.p, k_gscale=f.p, v_fp4=f.p, v_sf=f.p, v_gscale=f.p, delta_s=f.p,
+                 scale=0.088, causal=1, out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256,
+                 stream=None)
+        a.update(kw)
+        return pv(*a.values())
+    assert call(v_sf=None) == -1
+    assert call(v_gscale=None) == -1
+    assert call(v_sf=f.mis) == -1
+    assert call(D=64) == -2
+    assert call(Hq=3) == -1
+    # the workspace must hold the V image too: the plain prefill's size is short
+    need = lib.mpfa_workspace_bytes(2, 1, 4, 2, 256, 128, 1)
+    assert call(ws_bytes=need) == -3
 
 
 def _append(lib, f, **kw):

@@ -10,7 +10,10 @@ polynomial for part of the exponentials) against the oracle:
   (2^-13 > 7.5e-5), since a P value that close to an E4M3 midpoint may round
   either way;
 * bf16 P.V: the oracle with P rounded to bf16 (of 448 p) and V in bf16; the
-  bf16 V cache byte for byte.
+  bf16 V cache byte for byte;
+* NVFP4 P.V: the oracle with P quantized to NVFP4 per 16 keys and V in NVFP4
+  along the keys; the NVFP4 V cache (codes, scales, global scale) byte for
+  byte.
 
 Output within |gpu - oracle| <= 2e-3 + 1e-2 |oracle| (+ the ambiguity slack),
 LSE within 2e-3, on every row of small cases and on sampled rows of the 32K
@@ -39,8 +42,16 @@ def mpfa():
 
 def _caches(mpfa, variant, qd, kd, vd, smooth):
     kq = mpfa.quantize_k(kd, q=qd) if smooth else mpfa.quantize_k(kd, smooth=False)
-    vq = mpfa.pack_v_bf16(vd) if variant == "pv_bf16" else mpfa.quantize_v(vd)
+    if variant == "pv_bf16":
+        vq = mpfa.pack_v_bf16(vd)
+    elif variant == "pv_nvfp4":
+        vq = mpfa.quantize_v_nvfp4(vd)
+    else:
+        vq = mpfa.quantize_v(vd)
     return kq, vq
+
+
+PV = {"pv_bf16": "bf16", "pv_nvfp4": "nvfp4"}
 
 
 def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
@@ -55,7 +66,7 @@ def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
     out, lse = mpfa.prefill_variant(variant, qd, kq, vq, cfg.scale, causal=causal,
                                     out_dtype=torch.float32, with_lse=True)
     torch.cuda.synchronize()
-    pv = "bf16" if variant == "pv_bf16" else "fp8"
+    pv = PV.get(variant, "fp8")
     amb_rel = POLY_AMB_REL if variant == "poly_exp2" else None
     if variant == "pv_bf16":
         ref = oracle_mod.quantize_v_bf16(v)
@@ -64,6 +75,12 @@ def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
         rows = tiles.transpose(0, 1, 2, 3, 5, 4).reshape(B, Hkv, T * 32, 128)
         assert_bytes_equal("v_bf16", rows[:, :, :cfg.N], ref)
         assert not rows[:, :, cfg.N:].any(), "the bf16 V cache is zero past N"
+    if variant == "pv_nvfp4":
+        ref = oracle_mod.quantize_v_nvfp4(v)
+        assert_bytes_equal("v_fp4", host(vq["v_fp4"]), ref["v_fp4"])
+        assert_bytes_equal("v_sf", host(vq["v_sf"]), ref["v_sf"])
+        assert_bytes_equal("v_gscale", host(vq["v_gscale"]).view(np.uint32),
+                           np.array([ref["v_gscale"]], np.float32).view(np.uint32))
     O, LSE, _, AMB = oracle_mod.prefill_rows(q, k, v, cfg.scale, causal=causal, smooth=smooth,
                                              ambiguity=True, pv=pv, amb_rel=amb_rel)
     assert_close("out", host(out).reshape(-1, 128), O, slack=AMB)
@@ -71,27 +88,27 @@ def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
     return host(out)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 def test_variant_small_config(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("prefill_1k_2x1"), variant)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 @pytest.mark.parametrize("N", [1, 129, 300])
 def test_variant_gqa5_spikes_ragged(mpfa, oracle_mod, variant, N):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("qwen14b_prefill_32k", B=2, Hq=10, Hkv=2, N=N), variant)
 
 
-@pytest.mark.parametrize("variant", ["poly_exp2", "pv_bf16"])
+@pytest.mark.parametrize("variant", ["poly_exp2", "pv_bf16", "pv_nvfp4"])
 def test_variant_direct_mode(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=4, Hkv=2, N=333), variant,
            smooth=False)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "pv_bf16"])
+@pytest.mark.parametrize("variant", ["elementwise", "pv_bf16", "pv_nvfp4"])
 def test_variant_non_causal(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=2, Hkv=1, N=260), variant,
@@ -115,7 +132,7 @@ def test_elementwise_matches_the_rank_one_kernel(mpfa):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16"])
+@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 def test_variant_fullsize_qwen14b_32k(mpfa, oracle_mod, variant):
     """Each variant on the 32K benchmark inputs, in the launch configuration the
     benchmark times, on synth.sample_rows."""
@@ -139,7 +156,7 @@ def test_variant_fullsize_qwen14b_32k(mpfa, oracle_mod, variant):
     torch.cuda.empty_cache()
     say(f"  gpu done ({time.time() - t0:.1f} s); oracle on {len(rows)} sampled rows")
     ops = oracle_mod.Operands(qh, kh, vh, cfg.scale, smooth=True, identity=False,
-                              pv="bf16" if variant == "pv_bf16" else "fp8")
+                              pv=PV.get(variant, "fp8"))
     O, LSE, _, AMB = oracle_mod.prefill_rows(
         qh, kh, vh, cfg.scale, causal=True, smooth=True, rows=rows, ops=ops, ambiguity=True,
         amb_rel=POLY_AMB_REL if variant == "poly_exp2" else None)
