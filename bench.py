@@ -164,6 +164,19 @@ def host_env():
     return env
 
 
+def valu_ceiling(peaks, achieved):
+    """The softmax's vector-ALU ceiling measured by mpfa_peaks (TFLOP/s of
+    algorithmic work one softmax wave per SIMD could serve if the matrix
+    products were free), as a fraction of the FP4/FP8 roofline, and the
+    fraction of it the prefill reaches; None without a peaks run."""
+    t = (peaks or {}).get("softmax_valu_tflops")
+    if not t:
+        return None
+    return {"tflops": t, "frac_of_roofline": round(t * 1e12 / PEAK_MIXED, 4),
+            "achieved_frac": round(achieved / t, 4),
+            "block_ns": peaks.get("softmax_block_ns")}
+
+
 def measured_peaks():
     """The device's measured ceilings from the standalone probe built beside
     the library (mixed_precision_flashattention_amd/mpfa_peaks): MFMA rates of
@@ -608,6 +621,7 @@ def main():
         peaks = measured_peaks()  # a child process, before this one touches the GPU
         if peaks:
             log(f"[bench] measured ceilings: MFMA {peaks.get('mfma_tflops')} TFLOP/s, "
+                f"softmax VALU {peaks.get('softmax_valu_tflops')} TFLOP/s, "
                 f"read {peaks.get('read_GBps')} GB/s")
 
     import torch
@@ -765,7 +779,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MIXED, 4),
                      "traffic": measured_traffic(f"mpfa_prefill {cfg.name}"),
                      "flops_per_launch": flops, "ms_per_launch": round(ms_prefill, 4),
-                     "frac_of_fp16_fp8_instruction_peak": round(achieved * 1e12 / PEAK_F16_FP8, 4)},
+                     "frac_of_fp16_fp8_instruction_peak": round(achieved * 1e12 / PEAK_F16_FP8, 4),
+                     # the secondary ceiling: one softmax wave per SIMD running
+                     # the kernel's per-block softmax mix with free matrix work
+                     # (measured by mpfa_peaks on this device)
+                     "valu_softmax_ceiling": valu_ceiling(peaks, achieved)},
         "prefill_ms": round(ms_prefill, 4), "prefill_median_ms": round(ms_prefill_median, 4),
         "stage_one_ms": round(ms_stage1, 4),
         "compensation": {

@@ -1,9 +1,10 @@
 // Measured ceilings of the MI355X that the roofline fractions are quoted
 // against: streaming-read bandwidth of HBM (plain and non-temporal 16-byte
-// loads over the 128K decode workload's 3.49 GB) and the issue rate of the
+// loads over the 128K decode workload's 3.49 GB), the issue rate of the
 // MFMA instructions the kernels use (32x32x16 f16 and bf16, 32x32x64 FP8
-// and FP4 with unit block scales).  A standalone program, not part of the
-// library: it prints one JSON object.
+// and FP4 with unit block scales), and the vector-ALU ceiling of the
+// prefill's softmax.  A standalone program, not part of the library: it
+// prints one JSON object.
 //
 // MFMA probe: every wave runs kIters rounds of 8 independent MFMAs (eight
 // accumulators, so no instruction waits on the previous one) on operands
@@ -67,6 +68,70 @@ __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ out) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s += acc[j][e];
   out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// Softmax VALU ceiling: one wave per SIMD (one 4-wave workgroup per CU,
+// held alone there by its LDS allocation) runs the prefill's per-block
+// softmax instruction mix on the 64 scores a lane owns in the S^T layout
+// (128 keys x 32 queries per wave): the row max (in-lane chain and one
+// lane-half exchange), the correction factor, exp2 of the scaled and
+// shifted scores, the row sum of the unrounded p and the E4M3 conversion of
+// P, kSmIters blocks in a row with the scores made opaque each time.  The
+// running max does not move after the first block, so the output rescale is
+// skipped as in most blocks of the kernel.  Each (block, wave) serves
+// 4 x 128 x 128 x 32 FLOP of the prefill's algorithmic work, which gives
+// the rate the softmax alone could sustain with free matrix products.
+constexpr int kSmIters = 4096;
+constexpr double kSmFlopPerBlockWave = 4.0 * 128 * 128 * 32;
+
+__global__ __launch_bounds__(256) void k_softmax(float* __restrict__ out, float lam) {
+  const int lane = threadIdx.x & 63;
+  float s[64], o[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    s[i] = 0.01f * (float)((lane * 7 + i * 13) & 63);
+    o[i] = 1.0f;
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  uint32_t pacc = 0u;
+  for (int it = 0; it < kSmIters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) asm volatile("" : "+v"(s[i]));
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) mx = fmaxf(mx, s[i]);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false,
+                                                    false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(lam * (m_run - m_new));
+    const float nb = 8.80735492f - lam * m_new;  // log2(448) - lam m
+    m_run = m_new;
+    float lsum = 0.0f;
+    uint32_t w[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[4 * k], lam, nb));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[4 * k + 1], lam, nb));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(s[4 * k + 2], lam, nb));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(s[4 * k + 3], lam, nb));
+      lsum += (e0 + e1) + (e2 + e3);
+      uint32_t wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __float_as_uint(e0), false);
+      w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+    }
+    l_run = fmaf(alpha, l_run, lsum);
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) o[i] *= alpha;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(w[k]));
+    pacc ^= w[0] ^ w[15];
+  }
+  float t = l_run + (float)(pacc & 1u);
+#pragma unroll
+  for (int i = 0; i < 64; ++i) t += o[i];
+  out[blockIdx.x * 256 + threadIdx.x] = t;
 }
 
 template <bool NT>
@@ -150,6 +215,21 @@ int main() {
     printf("%s\"%s\": %.1f", op ? ", " : "", names[op], flop / (ms * 1e-3) / 1e12);
   }
   printf("}");
+
+  // ---- softmax VALU ceiling: one workgroup per CU (its 96 KB of LDS keep a
+  // second one out), one wave per SIMD
+  {
+    const size_t lds = 96 * 1024;
+    CHECK(hipFuncSetAttribute((const void*)k_softmax, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds));
+    float ms = 0.0f;
+    if (time_ms([&] { hipLaunchKernelGGL(k_softmax, dim3(cus), dim3(256), lds, 0, out, 0.0127f); }, 5,
+                &ms))
+      return 1;
+    const double flop = (double)cus * 4 * kSmIters * kSmFlopPerBlockWave;
+    printf(", \"softmax_valu_tflops\": %.1f, \"softmax_block_ns\": %.1f", flop / (ms * 1e-3) / 1e12,
+           ms * 1e6 / kSmIters);
+  }
   CHECK(hipFree(out));
 
   // ---- streaming read over 3,489,660,928 bytes
