@@ -166,12 +166,15 @@ int quantize_k_impl(const void* k, int k_dtype, int B, int Hkv, int N, int D, co
   if (center) {
     // K and Q in the same launches; the K_c amax comes from K's channel
     // ranges and means, with no pass of its own
-    const ChannelMeanJob jobs[2] = {
-        {k, kb, B * Hkv, (uint32_t*)(w + L.kmax), (unsigned long long*)(w + L.ksum), k_mean,
-         amax},
-        {q, q_dtype == MPFA_BF16, B * Hq, (uint32_t*)(w + L.qmax),
-         (unsigned long long*)(w + L.qsum), q_mean, q_ext}};
-    launch_channel_means(jobs, (smooth && q) ? 2 : 1, N, s);
+    const ChannelMeanJob kjob = {k, kb, B * Hkv, (uint32_t*)(w + L.kmax),
+                                 (unsigned long long*)(w + L.ksum), k_mean, amax};
+    const ChannelMeanJob qjob = {q, q_dtype == MPFA_BF16, B * Hq, (uint32_t*)(w + L.qmax),
+                                 (unsigned long long*)(w + L.qsum), q_mean, q_ext};
+    // the query tensor (G times the keys) first: its long row blocks go out
+    // before the short key blocks, which then fill the pass's tail
+    const bool two = smooth && q;
+    const ChannelMeanJob jobs[2] = {two ? qjob : kjob, kjob};
+    launch_channel_means(jobs, two ? 2 : 1, N, s);
     kc_mean = k_mean;
   } else {
     launch_centered_amax(k, kb, B * Hkv, N, nullptr, amax, s);
