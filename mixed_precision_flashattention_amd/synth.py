@@ -9,7 +9,8 @@ so any slice can be regenerated on its own (the large configurations are
 checked on sampled heads and rows).
 
 Distributions: Q, K, V ~ N(0, 1) in fp32; K gets a per-channel offset
-~ N(0, 4) (sigma 2) on a few channels per KV head, constant across tokens and
+~ N(0, 4) (sigma 2; ``koff_sigma`` overrides it for the stronger ridges of the
+accuracy study) on a few channels per KV head, constant across tokens and
 shared by every batch entry (the persistent channel "ridges" of §4.2);
 optionally a fraction of entries of Q, K and V is multiplied by a spike
 factor.  bf16 configurations round the fp32 draws to bf16 (round to nearest
@@ -36,6 +37,7 @@ class Config:
     D: int = 128
     dtype: str = "bf16"  # input dtype: "bf16" or "f32"
     n_outlier: int = 5  # K outlier channels per KV head
+    koff_sigma: float = 2.0  # standard deviation of their offsets
     spike_frac: float = 0.0
     spike_mult: float = 20.0
     num_splits: int = 1
@@ -90,7 +92,7 @@ def k_outliers(cfg: Config, h: int) -> tuple[np.ndarray, np.ndarray]:
     """(channels, offsets) of KV head h."""
     r = _rng(cfg, "koff", h)
     ch = r.choice(cfg.D, size=cfg.n_outlier, replace=False)
-    off = r.normal(0.0, 2.0, size=cfg.n_outlier).astype(np.float32)
+    off = r.normal(0.0, cfg.koff_sigma, size=cfg.n_outlier).astype(np.float32)
     return ch, off
 
 
