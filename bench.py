@@ -139,7 +139,7 @@ def median_call_ms(fn, n=20):
 
 
 def host_env():
-    """Shader clock levels as the driver lists them (the active one marked),
+    """Shader clock levels as the amdgpu kernel driver lists them (the active one marked),
     the host CPU model and its logical core count."""
     import glob
     import platform
@@ -589,7 +589,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen14b_prefill_32k")
     ap.add_argument("--decode-workload", default="llama8b_decode_128k")
     ap.add_argument("--no-decode", action="store_true")
@@ -618,7 +618,7 @@ def main():
         write_traffic(args.write_traffic, args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
