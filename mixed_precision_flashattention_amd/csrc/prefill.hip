@@ -455,6 +455,34 @@ __device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* q
   if (lane < 32) dst[koff_t] = (uint16_t)bf16_rne(((d[0] + d[1]) + d[2]) * gK);
 }
 
+// The same for both row groups' query tiles in one product: rows 0-2 of the
+// A operand hold group 0's tile mean parts and rows 4-6 group 1's, so D rows
+// 0-2 land in registers 0-2 of lanes 0-31 and rows 4-6 in registers 0-2 of
+// lanes 32-63 (each lane half then holds its group's three partial products
+// for the key of its column, summed and rounded exactly as above).
+__device__ __forceinline__ void tile_delta_pair(const uint8_t* kblk, const uint8_t* qop,
+                                                int kbase_t, int koff_t, float gK, int lane,
+                                                uint16_t* dst0, uint16_t* dst1) {
+  const uint8_t* at = kblk + kbase_t;
+  const int r = lane & 31, g = r >> 2, part = r & 3;
+  const bool data = r < 7 && part < 3;
+  // lane (r, h) reads the 8 parts of row r for the head-dim slots of half h
+  const uint8_t* qa = qop + g * 768 + (lane >> 5) * 48 + part * 16;
+  f32x16 d = f32x16{};
+  i32x4 b[2], a[2];
+  b[0] = *reinterpret_cast<const i32x4*>(at);
+  a[0] = data ? *reinterpret_cast<const i32x4*>(qa) : i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    if (kc + 1 < 8) {
+      b[(kc + 1) & 1] = *reinterpret_cast<const i32x4*>(at + (kc + 1) * kKChunkBytes);
+      a[(kc + 1) & 1] = data ? *reinterpret_cast<const i32x4*>(qa + (kc + 1) * 96) : i32x4{0, 0, 0, 0};
+    }
+    d = mfma32_bf16(a[kc & 1], b[kc & 1], d);
+  }
+  (lane < 32 ? dst0 : dst1)[koff_t] = (uint16_t)bf16_rne(((d[0] + d[1]) + d[2]) * gK);
+}
+
 // Work unit: 256 query rows of one (batch, head) in two groups of 4 waves
 // (rows 0-127 and 128-255); each SIMD holds one wave of each group.  The
 // groups take turns: between two workgroup barriers one group runs its
@@ -647,10 +675,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   // issues its half after its matrix phase, group 1 its half at the start of
   // its own; the barrier that opens body j+1 publishes them.  Both loops
   // pass the same barriers.  In the per-tile mode K~ runs one block further ahead (K~(j+2)
-  // is issued in body j, into the buffer of K~(j-1)), and each wave's matrix
-  // phase also computes Delta_tile(j+1) of its own tile for key tile
-  // (wave & 3) from the resident K~(j+1); the next opening barrier publishes
-  // it, and its buffer was last read by the scores of block j-1.
+  // is issued in body j, into the buffer of K~(j-1)), and in body j the
+  // matrix phase of group j % 2 also computes Delta_tile(j+1) of both groups'
+  // tiles for key tile (wave & 3) from the resident K~(j+1) (one product for
+  // both, the groups taking turns); the next opening barrier publishes it,
+  // and its buffers were last read by the scores of block j-1.
 #define MPFA_STEP_OPEN(J)                                                                    \
   do {                                                                                       \
     wait_direct_loads(); /* this wave's loads of the previous body have landed */            \
@@ -679,13 +708,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     if ((J) < n_own) {                                                                       \
       score_block<RANK1, TILE>(s, smem_k[(J) % NKB], smem_delta[(J) & 1][TILE ? grp : 0], koff, \
                                kbase, qf, dB, h);                                            \
-      if (TILE && (J) + 1 < n_own)                                                           \
-        tile_delta(smem_k[((J) + 1) % NKB], qop_g, kbase[wave & 3], koff[wave & 3], gK, lane,  \
-                   smem_delta[((J) + 1) & 1][TILE ? grp : 0]);                               \
     } else {                                                                                 \
       /* defining s on this path too keeps the old scores from being live */                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \
     }                                                                                        \
+    /* the groups take turns computing Delta_tile(J+1) for both tiles */                    \
+    if (TILE && ((J) & 1) == grp && (J) + 1 < n_max)                                         \
+      tile_delta_pair(smem_k[((J) + 1) % NKB], smem_qop, kbase[wave & 3], koff[wave & 3], gK,  \
+                      lane, smem_delta[((J) + 1) & 1][0],                                    \
+                      smem_delta[((J) + 1) & 1][TILE ? 1 : 0]);                              \
   } while (0)
 #define MPFA_SOFTMAX(J)                                                                      \
   do {                                                                                       \
