@@ -54,13 +54,15 @@ def _caches(mpfa, variant, qd, kd, vd, smooth):
 PV = {"pv_bf16": "bf16", "pv_nvfp4": "nvfp4"}
 
 
-def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True):
+def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True, edit=None):
     import torch
     from mixed_precision_flashattention_amd import synth
     in_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     q, k, v = (synth.full(cfg, t) for t in ("q", "k", "v"))
+    if edit is not None:
+        q, k, v = edit(q, k, v)
     say(f"case: prefill variant {variant} B{cfg.B} Hq{cfg.Hq}/Hkv{cfg.Hkv} N{cfg.N} {cfg.dtype} "
-        f"smooth={smooth} causal={causal}")
+        f"smooth={smooth} causal={causal}{' ' + edit.__name__ if edit is not None else ''}")
     qd, kd, vd = dev(q, in_dtype), dev(k, in_dtype), dev(v, in_dtype)
     kq, vq = _caches(mpfa, variant, qd, kd, vd, smooth)
     out, lse = mpfa.prefill_variant(variant, qd, kq, vq, cfg.scale, causal=causal,
@@ -113,6 +115,35 @@ def test_variant_non_causal(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=2, Hkv=1, N=260), variant,
            causal=False)
+
+
+def _zero_k(q, k, v):
+    return q, np.zeros_like(k), v
+
+
+def _same_key(q, k, v):
+    return q, np.ascontiguousarray(np.broadcast_to(k[:, :, :1, :], k.shape)), v
+
+
+def _zero_v(q, k, v):
+    return q, k, np.zeros_like(v)
+
+
+def _zero_q(q, k, v):
+    return np.zeros_like(q), k, v
+
+
+@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q], ids=lambda f: f.__name__)
+@pytest.mark.parametrize("variant", ["pv_bf16", "pv_nvfp4"])
+def test_variant_degenerate_inputs(mpfa, oracle_mod, variant, edit):
+    """Zero keys or queries (every score equal: P of a whole group at its
+    maximum), keys identical along the sequence (centred K zero), zero V
+    (a zero V cache, a zero output) through the other P.V precisions."""
+    from mixed_precision_flashattention_amd import synth
+    out = _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=4, Hkv=2, N=200),
+                 variant, edit=edit)
+    if edit is _zero_v:
+        assert not np.any(out), "zero V must give a zero output"
 
 
 def test_elementwise_matches_the_rank_one_kernel(mpfa):
