@@ -179,10 +179,15 @@ int quantize_k_impl(const void* k, int k_dtype, int B, int Hkv, int N, int D, co
   } else {
     launch_centered_amax(k, kb, B * Hkv, N, nullptr, amax, s);
   }
-  // the K quantizer also copies the Q_c amax word out (it runs after the finalize)
-  launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf,
-                          q_ext, q_ext ? q_amax : nullptr, s);
-  if (smooth) launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s);
+  // the K quantizer also copies the Q_c amax word out (it runs after the
+  // finalize); in smoothing mode it rides in the Delta_S launch, which holds
+  // the centred rows anyway
+  if (smooth)
+    launch_delta_s(k, kb, B, Hkv, Hq / Hkv, N, k_mean, q_mean, delta_s, s, amax, k_gscale, k_fp4,
+                   k_sf, q_ext, q_ext ? q_amax : nullptr);
+  else
+    launch_quantize_k_codes(k, kb, B * Hkv, N, kc_mean, amax, k_gscale, k_fp4, k_sf, q_ext,
+                            q_ext ? q_amax : nullptr, s);
   return launch_status();
 }
 

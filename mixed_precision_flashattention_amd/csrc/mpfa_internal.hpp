@@ -114,8 +114,14 @@ void launch_tile_mean(const void* x, int is_bf16, int BH, int N, float* mean, ui
 void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const float* k_mean,
                              const uint32_t* amax, float* gscale, uint8_t* codes, uint8_t* sf,
                              const uint32_t* q_ext, float* q_amax, hipStream_t st);
+// codes non-NULL: the same launch also writes the NVFP4 K codes and scales
+// (and gscale, and q_amax from q_ext when q_amax is non-NULL), as
+// launch_quantize_k_codes would with k_mean
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
-                    const float* q_mean, uint16_t* delta, hipStream_t st);
+                    const float* q_mean, uint16_t* delta, hipStream_t st,
+                    const uint32_t* amax = nullptr, float* gscale = nullptr,
+                    uint8_t* codes = nullptr, uint8_t* sf = nullptr,
+                    const uint32_t* q_ext = nullptr, float* q_amax = nullptr);
 // NVFP4 V along the keys: codes [BH, ceil(N/16), 128, 8 bytes] (key 2t of a
 // block in the low nibble of byte t), scales [BH, ceil(N/16), 128], global
 // scale from *amax written to gscale.

@@ -450,12 +450,22 @@ __global__ void k_quantize_k(const void* __restrict__ k, int is_bf16, int64_t n_
 // head).  The block stages K_c = fp32(K - k_mean) of its tokens in LDS with
 // coalesced loads (rows padded to 129 words, so the per-token reads below
 // hit 64 different banks), then thread (token, head) runs its FP64 sum.
+// With codes non-NULL the first block of every (b, hk) column of the grid
+// (blockIdx.z == 0) also writes the NVFP4 codes and scales of its 64 centred
+// rows from the same LDS copy (the K quantizer's bytes: the same fp32 K_c
+// values and block steps), so K is read once for both.
 constexpr int kDsRows = 64;
 
 __global__ __launch_bounds__(512) void k_delta_s(const void* __restrict__ k, int is_bf16, int Hkv,
                                                  int G, int N, const float* __restrict__ k_mean,
                                                  const float* __restrict__ q_mean,
-                                                 uint16_t* __restrict__ delta) {
+                                                 uint16_t* __restrict__ delta,
+                                                 const uint32_t* __restrict__ amax,
+                                                 float* __restrict__ gscale_out,
+                                                 uint2* __restrict__ codes,
+                                                 uint8_t* __restrict__ sf,
+                                                 const uint32_t* __restrict__ q_ext,
+                                                 float* __restrict__ q_amax_out) {
   __shared__ float kc[kDsRows * (kD + 1)];
   __shared__ float qm[8 * kD];
   const int bhk = blockIdx.y;  // b * Hkv + hk
@@ -474,6 +484,25 @@ __global__ __launch_bounds__(512) void k_delta_s(const void* __restrict__ k, int
   }
   for (int e = threadIdx.x; e < ng * kD; e += blockDim.x) qm[e] = q_mean[hq0 * kD + e];
   __syncthreads();
+  if (codes && blockIdx.z == 0) {  // uniform across the block
+    const float gk = nvfp4_global_scale(__uint_as_float(*amax));
+    if (blockIdx.x == 0 && bhk == 0 && threadIdx.x == 0) {
+      *gscale_out = gk;
+      if (q_amax_out) *q_amax_out = __uint_as_float(*q_ext);  // the Q_c amax, passed on
+    }
+    for (int gi = threadIdx.x; gi < kDsRows * 8; gi += blockDim.x) {
+      const int rr = gi >> 3, c = gi & 7;
+      if (t0 + rr >= N) continue;
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = kc[rr * (kD + 1) + 16 * c + j];
+      uint32_t w[2];
+      const uint32_t sc = nvfp4_block_packed(x, gk, w);
+      const int64_t o = ((int64_t)bhk * N + t0 + rr) * 8 + c;
+      codes[o] = make_uint2(w[0], w[1]);
+      sf[o] = (uint8_t)sc;
+    }
+  }
   const int r = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int t = t0 + r;
   if (t >= N || g >= ng) return;
@@ -772,10 +801,13 @@ void launch_quantize_k_codes(const void* k, int is_bf16, int BH, int N, const fl
 }
 
 void launch_delta_s(const void* k, int is_bf16, int B, int Hkv, int G, int N, const float* k_mean,
-                    const float* q_mean, uint16_t* delta, hipStream_t st) {
+                    const float* q_mean, uint16_t* delta, hipStream_t st, const uint32_t* amax,
+                    float* gscale, uint8_t* codes, uint8_t* sf, const uint32_t* q_ext,
+                    float* q_amax) {
   dim3 grid((N + kDsRows - 1) / kDsRows, B * Hkv, (G + 7) / 8);
   hipLaunchKernelGGL(k_delta_s, grid, dim3(kDsRows * min(G, 8)), 0, st, k, is_bf16, Hkv, G, N,
-                     k_mean, q_mean, delta);
+                     k_mean, q_mean, delta, amax, gscale, reinterpret_cast<uint2*>(codes), sf,
+                     q_ext, q_amax);
 }
 
 void launch_quantize_v_codes(const void* v, int is_bf16, int BH, int N, const uint32_t* amax,
