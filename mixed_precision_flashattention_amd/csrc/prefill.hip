@@ -467,7 +467,8 @@ __device__ __forceinline__ void tile_delta_pair(const uint8_t* kblk, const uint8
   const int r = lane & 31, g = r >> 2, part = r & 3;
   const bool data = r < 7 && part < 3;
   // lane (r, h) reads the 8 parts of row r for the head-dim slots of half h
-  const uint8_t* qa = qop + g * 768 + (lane >> 5) * 48 + part * 16;
+  // (lanes of the zero rows keep a base inside the array)
+  const uint8_t* qa = qop + (data ? g * 768 + part * 16 : 0) + (lane >> 5) * 48;
   f32x16 d = f32x16{};
   i32x4 b[2], a[2];
   b[0] = *reinterpret_cast<const i32x4*>(at);
