@@ -224,3 +224,24 @@ def test_lossless_pv_nvfp4_equals_exact(oracle_mod, causal):
     O8, _, _ = oracle_mod.prefill_rows(q, k, v, LOSSLESS_SCALE, causal=causal, smooth=False,
                                        out_f64=True)
     assert np.abs(O8 - Oe).max() > 1e-3 * np.abs(Oe).max()
+
+
+def test_p_nvfp4_scale_midpoint_is_ambiguous(oracle_mod):
+    """A 16-key group whose largest p puts amax / fp32(6 G_P) next to the
+    E4M3 midpoint 432 (between the scales 416 and 448): the group's scale
+    decision is ambiguous, and the key that sets it moves with the other
+    scale (its code stays 6, its value follows the scale).  The group that
+    holds the row maximum (quotient 6, scale 448) is not ambiguous, and with
+    a zero window neither is."""
+    s = np.full(32, -100.0)  # p ~ 2^-100: zero codes, far from every midpoint
+    s[0] = 0.0  # the row max: group 0's p = 1
+    s[16] = math.log2(432.0 / 448.0) + 1e-6  # group 1 amax p ~ 432/448, 1e-6 off the midpoint
+    scale = math.log(2.0)  # lam = 1
+    _, _, acc, amb = _probe(oracle_mod, s, scale)
+    assert amb[0, 16] > 0.0
+    assert amb[0, 0] == 0.0 and not amb[0, 17:32].any()
+    g = float(G_P)
+    assert acc[0, 16] in (448.0 * 6 * 416 * g, 448.0 * 6 * 448 * g)
+    assert abs(amb[0, 16] - 448.0 * 6 * 32 * g) < 1e-9
+    _, _, acc0, amb0 = _probe(oracle_mod, s, scale, amb_rel=0.0)
+    assert np.array_equal(acc, acc0) and not amb0.any()
