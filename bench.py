@@ -11,8 +11,9 @@ step.
 
 Also reported, each timed on its own with HIP events on the launch stream:
 the prefill call alone (the dominant kernel, against the mixed FP4/FP8 MFMA
-roofline), the same call with and without the rank-one compensation step on
-one centred K cache (the compensation overhead), the prefill with
+roofline), the same call with and without the compensation term on one
+centred K cache (the compensation overhead), its placement variants, the
+prefill with
 per-128-row query-tile means (mpfa_prefill_tile_mean), the Llama-3.1-8B-shaped
 16K prefill and the 128K two-sequence prefill with LSE, and the split-KV
 decode of the Llama-3.1-8B-shaped 128K cache (batch 16, 32 splits) as KV bytes
@@ -703,7 +704,7 @@ def main():
         f"({achieved * 1e12 / PEAK_MIXED:.4f} of the FP4/FP8 roofline); stage one {ms_stage1:.3f} ms")
 
     # ---- compensation overhead: one centred K cache, the same call with and
-    # without the rank-one step.  Without Delta_S the centred cache gives
+    # without the compensation term.  Without Delta_S the centred cache gives
     # Q . K_c = Q_c . K_c + Qbar . K_c, the same scores up to the query
     # quantization, so the softmax does the same work; both calls take their
     # query amax in their own pass.
@@ -712,18 +713,19 @@ def main():
                           kq["k_gscale"], vq["v_fp8"], vq["v_scale"], kq["delta_s"], cfg.scale,
                           True, out, None, ws_p)
 
-    def prefill_no_rank_one():
+    def prefill_no_compensation():
         mpfa.mpfa_prefill(q, Hkv, None, None, kq["k_fp4"], kq["k_sf"], kq["k_gscale"],
                           vq["v_fp8"], vq["v_scale"], None, cfg.scale, True, out, None, ws_p)
 
-    ms_pair = {"smooth": [], "no_rank_one": []}
+    ms_pair = {"smooth": [], "no_compensation": []}
     for _ in range(3):  # interleaved, so clock drift hits both alike
         ms_pair["smooth"].append(time_calls(prefill_smooth_own_amax, max(3, args.steps // 2), 1))
-        ms_pair["no_rank_one"].append(time_calls(prefill_no_rank_one, max(3, args.steps // 2), 1))
+        ms_pair["no_compensation"].append(time_calls(prefill_no_compensation,
+                                                     max(3, args.steps // 2), 1))
     ms_smooth_own = float(np.median(ms_pair["smooth"]))
-    ms_no_rank_one = float(np.median(ms_pair["no_rank_one"]))
-    log(f"[bench] same centred cache: with the rank-one step {ms_smooth_own:.3f} ms, without "
-        f"{ms_no_rank_one:.3f} ms ({ms_smooth_own / ms_no_rank_one - 1:+.2%})")
+    ms_no_comp = float(np.median(ms_pair["no_compensation"]))
+    log(f"[bench] same centred cache: with the compensation {ms_smooth_own:.3f} ms, without "
+        f"{ms_no_comp:.3f} ms ({ms_smooth_own / ms_no_comp - 1:+.2%})")
     # precision / placement variants (MpFA page section 3.1 Fig. 3(a), 7.4,
     # 5.1) on the same caches, each taking its query amax in its own pass like
     # the smoothing call they are compared with
@@ -731,13 +733,13 @@ def main():
     ws_p4 = torch.empty(mpfa.mpfa_workspace_bytes(mpfa.MPFA_OP_PREFILL_PV_NVFP4, B, Hq, Hkv, N),
                         dtype=torch.uint8, device=dev)
     ms_var = {}
-    for name in ("elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"):
+    for name in ("rank_one", "elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"):
         def var_call(name=name):
             mpfa.prefill_variant(name, q, kq, var_vq.get(name, vq), cfg.scale, causal=True,
                                  out=out, ws=ws_p4 if name == "pv_nvfp4" else ws_p)
         ms_var[name] = time_calls(var_call, max(3, args.steps // 2), 1)
         log(f"[bench] variant {name}: {ms_var[name]:.3f} ms ({ms_var[name] / ms_smooth_own - 1:+.2%} "
-            f"against the rank-one smoothing call)")
+            f"against the smoothing call)")
     del var_vq, ws_p4
     torch.cuda.empty_cache()
 
@@ -793,17 +795,20 @@ def main():
         "prefill_ms": round(ms_prefill, 4), "prefill_median_ms": round(ms_prefill_median, 4),
         "stage_one_ms": round(ms_stage1, 4),
         "compensation": {
-            "cache": "one centred K cache; the call with Delta_S (rank-one step) and without it; "
+            "cache": "one centred K cache; the call with Delta_S (the score accumulator's "
+                     "input) and without it; "
                      "both take the query amax in their own pass",
-            "with_rank_one_ms": round(ms_smooth_own, 4), "without_ms": round(ms_no_rank_one, 4),
-            "overhead": round(ms_smooth_own / ms_no_rank_one - 1.0, 4),
+            "with_ms": round(ms_smooth_own, 4), "without_ms": round(ms_no_comp, 4),
+            "overhead": round(ms_smooth_own / ms_no_comp - 1.0, 4),
             "samples_ms": {k_: [round(t, 4) for t in v_] for k_, v_ in ms_pair.items()}},
         "variants": {
             "reference": "the smoothing call with its own query-amax pass "
-                         "(compensation.with_rank_one_ms); same caches",
-            **{name: {"ms": round(t, 4), "vs_rank_one_smoothing": round(t / ms_smooth_own - 1.0, 4)}
+                         "(compensation.with_ms); same caches",
+            **{name: {"ms": round(t, 4), "vs_smoothing": round(t / ms_smooth_own - 1.0, 4)}
                for name, t in ms_var.items()},
-            "what": {"elementwise": "Delta_S added per score on the VALU (MpFA 7.4 placement)",
+            "what": {"rank_one": "Delta_S written into the score accumulator by its own "
+                                 "rank-one bf16 MFMA step per tile (MpFA 5.2 MMA placement)",
+                     "elementwise": "Delta_S added per score on the VALU (MpFA 7.4 placement)",
                      "poly_exp2": "one exp2 in four by a fitted cubic (MpFA 5.1 split)",
                      "pv_bf16": "P and V in bf16, P.V on bf16 MFMA (MpFA 3.1 NVFP4+BF16)",
                      "pv_nvfp4": "P quantized to NVFP4 per 16 keys on the softmax path, V from "

@@ -7,9 +7,10 @@
  * operands (E2M1 elements, one E4M3 scale per 16 head-dim elements, one FP32
  * scale per tensor), P.V from FP8 E4M3 operands, with an FP32 online softmax
  * (paper section 4.1).  With smoothing, Q and K are centred on their
- * per-head sequence means and the score correction Delta_S = Qbar . K_c is
- * added to the score accumulator as a rank-one matrix product before the
- * mask and the running-max update (sections 3.2, 5.1, 5.2).
+ * per-head sequence means and the score correction Delta_S = Qbar . K_c
+ * enters the score accumulator of the matrix product (its input, before the
+ * Q.K^T terms), before the mask and the running-max update (sections 3.2,
+ * 5.1, 5.2).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -301,7 +302,9 @@ int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv,
  * Precision and placement variants of the smoothing-mode prefill (paper
  * section 3.1, Fig. 3(a): NVFP4 + FP8 against NVFP4 + BF16 and NVFP4 +
  * NVFP4; section 7.4
- * "Compensation placement": the rank-one MMA against an element-wise add;
+ * "Compensation placement": the compensation inside the matrix product
+ * against an element-wise add, here in two forms of the former -- the score
+ * accumulator's input (mpfa_prefill) and a rank-one MMA step;
  * section 5.1: part of the exponentials by a polynomial on the FMA units).
  * They exist to measure those choices on gfx950; each computes what its
  * description says and is checked against the oracle like mpfa_prefill.
@@ -309,8 +312,9 @@ int mpfa_prefill_with_q_amax(const void* q, int q_dtype, int B, int Hq, int Hkv,
  *
  * mpfa_prefill_elementwise -- Delta_S * 1/(gQ gK) added to every score on the
  * vector ALUs at the start of the softmax of each block (before the mask and
- * the running max), instead of the rank-one matrix step; the scores are the
- * same up to FP32 rounding.  delta_s == NULL returns MPFA_ERR_INVALID.
+ * the running max), instead of entering the score accumulator before the
+ * products; the scores are the same up to FP32 rounding.  delta_s == NULL
+ * returns MPFA_ERR_INVALID.
  */
 int mpfa_prefill_elementwise(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                              const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
@@ -318,6 +322,22 @@ int mpfa_prefill_elementwise(const void* q, int q_dtype, int B, int Hq, int Hkv,
                              const float* v_scale, const uint16_t* delta_s, float softmax_scale,
                              int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * mpfa_prefill_rank_one -- the compensation as its own rank-one matrix step
+ * (paper section 5.2's MMA placement): per 32-key score tile one bf16
+ * 32x32x16 matrix instruction with A = the bf16 Delta_S of each key and B =
+ * 1/(gQ gK) as three bf16 parts writes the term into the score accumulator
+ * before the Q.K^T products, where mpfa_prefill instead loads Delta_S *
+ * 1/(gQ gK) (fp32) as that accumulator's input; the scores are the same up to
+ * FP32 rounding.  delta_s == NULL returns MPFA_ERR_INVALID.
+ */
+int mpfa_prefill_rank_one(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                          const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                          const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                          const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                          int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * mpfa_prefill_poly_exp2 -- mpfa_prefill with one exponential in four
@@ -416,8 +436,8 @@ int mpfa_prefill_pv_nvfp4(const void* q, int q_dtype, int B, int Hq, int Hkv, in
  *     in BF16 like Delta_S (section 5.2) and computed in the attention kernel
  *     one 128-key block ahead by a matrix product of the mean's three exact
  *     bf16 parts with the K operands (FP32 accumulation);
- *   S_ij = Q~_c,i . K~_c,j + Delta_tile[tile of i, j], the offset written into
- *     the score accumulator by the rank-one step of mpfa_prefill;
+ *   S_ij = Q~_c,i . K~_c,j + Delta_tile[tile of i, j], the offset entering
+ *     the score accumulator as Delta_S does in mpfa_prefill;
  * then the online softmax, P.V and epilogue of mpfa_prefill; lse adds back
  * scale * (Q_i . k_mean).
  *

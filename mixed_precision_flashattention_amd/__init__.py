@@ -34,7 +34,8 @@ EXPORTS = ("mpfa_workspace_bytes", "mpfa_status_string", "mpfa_quantize_k_nvfp4"
            "mpfa_append_kv_paged", "mpfa_prefill", "mpfa_prefill_with_q_amax", "mpfa_decode",
            "mpfa_decode_paged", "mpfa_prefill_tile_mean", "mpfa_prefill_elementwise",
            "mpfa_prefill_poly_exp2", "mpfa_pack_v_bf16", "mpfa_prefill_pv_bf16",
-           "mpfa_quantize_v_nvfp4", "mpfa_prefill_pv_nvfp4", "mpfa_decode_static")
+           "mpfa_quantize_v_nvfp4", "mpfa_prefill_pv_nvfp4", "mpfa_decode_static",
+           "mpfa_prefill_rank_one")
 PAGE_SIZE = 128  # tokens per page of a paged cache
 
 _lib = None
@@ -76,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mpfa_prefill_with_q_amax.restype = i32
     L.mpfa_prefill_with_q_amax.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                            P, f32, i32, P, i32, P, P, sz, P]
-    for name in ("mpfa_prefill_elementwise", "mpfa_prefill_poly_exp2"):
+    for name in ("mpfa_prefill_elementwise", "mpfa_prefill_poly_exp2", "mpfa_prefill_rank_one"):
         getattr(L, name).restype = i32
         getattr(L, name).argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f32,
                                      i32, P, i32, P, P, sz, P]
@@ -237,6 +238,11 @@ def _prefill_variant(fn, q, Hkv, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8, v
 def mpfa_prefill_elementwise(*args, **kw):
     """C-ABI call, the arguments of mpfa_prefill (smoothing mode)."""
     _prefill_variant("mpfa_prefill_elementwise", *args, **kw)
+
+
+def mpfa_prefill_rank_one(*args, **kw):
+    """C-ABI call, the arguments of mpfa_prefill (smoothing mode)."""
+    _prefill_variant("mpfa_prefill_rank_one", *args, **kw)
 
 
 def mpfa_prefill_poly_exp2(*args, **kw):
@@ -519,7 +525,8 @@ def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=No
                     ws=None, out=None, lse=None, stream=None):
     """One of the prefill's precision / placement variants on the caches of
     quantize_k (smoothing iff kq holds delta_s): "elementwise" (Delta_S added
-    per score on the vector ALUs; smoothing only), "poly_exp2" (one exponential
+    per score on the vector ALUs; smoothing only), "rank_one" (Delta_S by a
+    rank-one bf16 matrix step; smoothing only), "poly_exp2" (one exponential
     in four by a cubic), "pv_bf16" (vq from pack_v_bf16: bf16 P and V),
     "pv_nvfp4" (vq from quantize_v_nvfp4: NVFP4 P and V).  The query amax is
     taken in the call's own pass.  Returns (out, lse or None)."""
@@ -544,7 +551,7 @@ def prefill_variant(variant, q, kq, vq, softmax_scale, causal=True, out_dtype=No
     elif variant == "pv_nvfp4":
         mpfa_prefill_pv_nvfp4(*common, vq["v_fp4"], vq["v_sf"], vq["v_gscale"],
                               kq.get("delta_s") if smooth else None, *tail, stream=stream)
-    elif variant in ("elementwise", "poly_exp2"):
+    elif variant in ("elementwise", "poly_exp2", "rank_one"):
         _prefill_variant(f"mpfa_prefill_{variant}", *common, vq["v_fp8"], vq["v_scale"],
                          kq.get("delta_s") if smooth else None, *tail, stream=stream)
     else:

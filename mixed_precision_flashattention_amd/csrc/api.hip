@@ -432,6 +432,18 @@ int mpfa_prefill_elementwise(const void* q, int q_dtype, int B, int Hq, int Hkv,
                       lse_or_null, ws, ws_bytes, stream, kVarElementwise);
 }
 
+int mpfa_prefill_rank_one(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
+                          const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
+                          const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,
+                          const float* v_scale, const uint16_t* delta_s, float softmax_scale,
+                          int causal, void* out, int out_dtype, float* lse_or_null, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!delta_s) return MPFA_ERR_INVALID;  // a placement of the compensation needs one
+  return prefill_impl(q, q_dtype, B, Hq, Hkv, N, D, q_mean, k_mean, k_fp4, k_sf, k_gscale, v_fp8,
+                      v_scale, delta_s, nullptr, softmax_scale, causal, out, out_dtype,
+                      lse_or_null, ws, ws_bytes, stream, kVarRankOne);
+}
+
 int mpfa_prefill_poly_exp2(const void* q, int q_dtype, int B, int Hq, int Hkv, int N, int D,
                            const float* q_mean, const float* k_mean, const uint8_t* k_fp4,
                            const uint8_t* k_sf, const float* k_gscale, const uint8_t* v_fp8,

@@ -7,9 +7,10 @@ namespace mpfa {
 
 // Precision / placement variants of the prefill attention kernel
 // (PrefillParams::variant): the library's kernel, element-wise compensation,
-// polynomial exp2 for one exponential in four, bf16 P.V, NVFP4 P.V.
+// polynomial exp2 for one exponential in four, bf16 P.V, NVFP4 P.V, the
+// compensation as a separate rank-one bf16 MMA step.
 constexpr int kVarNone = 0, kVarElementwise = 1, kVarPolyExp2 = 2, kVarPvBf16 = 3,
-              kVarPvNvfp4 = 4;
+              kVarPvNvfp4 = 4, kVarRankOne = 5;
 // The fixed NVFP4 global scale of P in the NVFP4 P.V variant: fp32(1/2688)
 // maps the bound p <= 1 to the largest E2M1 x E4M3 product, 6 x 448.
 constexpr float kNvfp4PScale = 1.0f / 2688.0f;

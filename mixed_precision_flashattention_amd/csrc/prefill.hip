@@ -12,16 +12,18 @@
 // group.  The groups alternate between workgroup barriers: one runs its
 // matrix products while the other runs its softmax, so the matrix cores and
 // the vector ALUs of a SIMD work at the same time.  Per 128-key block:
-//   * K~ block images, the FP8 V tiles and Delta_S reach LDS by direct
-//     global->LDS loads (no registers, no VALU address work), double-buffered
-//     and issued one block ahead by the first row group after its matrix
-//     products;
+//   * K~ block images and the FP8 V tiles reach LDS by direct global->LDS
+//     loads (no registers, no VALU address work), double-buffered and issued
+//     one block ahead; Delta_S goes through the registers of the first 128
+//     threads, which store it to LDS as Delta_S * (1 / (gQ gK)) in fp32;
 //   * each wave computes S^T (keys x its 32 queries) on MFMA: with
-//     smoothing, a first bf16 step writes Delta_S * (1 / (gQ gK)) into the
-//     accumulator (the rank-one term of section 5.2 -- no element-wise add on
-//     the softmax path), then 8 f16 steps accumulate Q~ K~^T over the head
-//     dimension, the four 32-key tiles interleaved so no step waits on the
-//     previous one; Q~ stays in registers for the whole loop;
+//     smoothing, the score accumulators start at Delta_S * (1 / (gQ gK)),
+//     read from LDS as the first MFMA's accumulator input (section 5.2's
+//     compensation inside the matrix product -- no element-wise add on the
+//     softmax path and no matrix step of its own), then 8 f16 steps
+//     accumulate Q~ K~^T over the head dimension, the four 32-key tiles
+//     interleaved so no step waits on the previous one; Q~ stays in
+//     registers for the whole loop;
 //   * softmax in the S^T layout: each lane owns one query and 64 of the 128
 //     keys, so the row max is in-lane plus one exchange with lane ^ 32; the
 //     global scales and the softmax scale are one constant in the exp2
@@ -154,10 +156,18 @@ __device__ __forceinline__ void prefill_unit(const PrefillParams& p, int wid, in
 // Scores S^T of one 128-key block: 4 tiles of 32 keys x the wave's 32 queries.
 // The K~ operands of head-dim step kc + 1 are read from LDS while the four
 // MFMAs of step kc run (the scheduling barriers keep the reads that early),
-// so the matrix core does not wait on LDS latency.
-template <bool SMOOTH, bool BF16>
+// so the matrix core does not wait on LDS latency.  COMP selects how the
+// compensation column term enters the accumulator before the products:
+//   0: not at all (direct mode);
+//   1: a rank-one bf16 MFMA step, A = the bf16 term of each key (comp: bf16
+//      per key), B = 1/(gQ gK) in three bf16 parts (dB);
+//   2: as the first product's accumulator input (comp: term x 1/(gQ gK) in
+//      fp32 per key): lane half h's output register v of tile t is key
+//      64(t/2) + 32h + 16(t%2) + v, so a tile's inputs are four 16-byte
+//      reads of consecutive keys, the same for every lane of the half.
+template <int COMP, bool BF16>
 __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
-                                            const uint16_t* dblk, const int (&koff)[4],
+                                            const void* comp, const int (&koff)[4],
                                             const int (&kbase)[4], const i32x4 (&qf)[8],
                                             const i32x4& dB, int h) {
   const uint8_t* at[4];
@@ -166,7 +176,8 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
   i32x4 a[2][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) a[0][t] = *reinterpret_cast<const i32x4*>(at[t]);
-  if (SMOOTH) {
+  if constexpr (COMP == 1) {
+    const uint16_t* dblk = static_cast<const uint16_t*>(comp);
     uint32_t dv[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dv[t] = dblk[koff[t]];
@@ -174,6 +185,15 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
     for (int t = 0; t < 4; ++t) {
       const i32x4 dA = {h == 0 ? (int)(dv[t] | (dv[t] << 16)) : 0, h == 0 ? (int)dv[t] : 0, 0, 0};
       s[t] = mfma32_bf16(dA, dB, f32x16{});
+    }
+  } else if constexpr (COMP == 2) {
+    const float* dsc = static_cast<const float*>(comp) + 32 * h;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(dsc + 64 * (t >> 1) + 16 * (t & 1));
+      const f32x4 c0 = src[0], c1 = src[1], c2 = src[2], c3 = src[3];
+      s[t] = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                    c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
     }
   }
 #pragma unroll
@@ -186,7 +206,7 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const f32x16 c = (SMOOTH || kc > 0) ? s[t] : f32x16{};
+      const f32x16 c = (COMP != 0 || kc > 0) ? s[t] : f32x16{};
       s[t] = BF16 ? mfma32_bf16(a[kc & 1][t], qf[kc], c) : mfma32_f16(a[kc & 1][t], qf[kc], c);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -197,7 +217,10 @@ __device__ __forceinline__ void score_block(f32x16 (&s)[4], const uint8_t* kblk,
 // section 3.1 and 7.4 comparisons, built as separate kernels; the library's
 // calls use kVarNone):
 //   kVarElementwise: Delta_S * 1/(gQ gK) added to each score on the VALU at
-//     the start of the softmax, instead of the rank-one matrix step;
+//     the start of the softmax, instead of entering the score accumulator;
+//   kVarRankOne: the term written into the score accumulator by a rank-one
+//     bf16 MFMA step per tile (A = Delta_S per key, B = 1/(gQ gK) in three
+//     bf16 parts) instead of read from LDS as its input;
 //   kVarPolyExp2: one exponential in four evaluated by a cubic on the FMA
 //     path instead of the hardware exp2 (the split the paper's B200 kernel
 //     uses to relieve its transcendental unit);
@@ -426,7 +449,8 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], PR
 }
 
 // Per-tile mode: Delta_tile of the 32 keys of score tile t of a K~ block for
-// this wave's query tile, as one bf16 value per key in dst[key].  A = the
+// this wave's query tile, rounded to bf16, as the score accumulator's input
+// fp32(Delta_tile * cinv) per key in dst[key].  A = the
 // tile mean split exactly into three bf16 parts (rows 0, 1, 2 of the A
 // operand; the other rows zero), B = the K~ operands of tile t, the same
 // registers the score product uses as its A operand (an A operand read as B
@@ -434,8 +458,11 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[4], f32x16 (&o)[4], PR
 // rows 0-2 land in registers 0-2 of lanes 0-31.  The three partial products
 // are exact in FP32 (8 x 6 significant bits); they are summed in FP32, scaled
 // by the K global scale and rounded once to bf16.
+__device__ __forceinline__ float tile_delta_input(float d, float gK, float cinv) {
+  return __uint_as_float(bf16_rne(d * gK) << 16) * cinv;
+}
 __device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* qop, int kbase_t,
-                                           int koff_t, float gK, int lane, uint16_t* dst) {
+                                           int koff_t, float gK, float cinv, int lane, float* dst) {
   const uint8_t* at = kblk + kbase_t;
   const bool data = (lane & 31) < 3;
   // lane (r, h) reads the 8 parts of row r for the head-dim slots of half h
@@ -452,7 +479,7 @@ __device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* q
     }
     d = mfma32_bf16(a[kc & 1], b[kc & 1], d);
   }
-  if (lane < 32) dst[koff_t] = (uint16_t)bf16_rne(((d[0] + d[1]) + d[2]) * gK);
+  if (lane < 32) dst[koff_t] = tile_delta_input((d[0] + d[1]) + d[2], gK, cinv);
 }
 
 // The same for both row groups' query tiles in one product: rows 0-2 of the
@@ -461,8 +488,8 @@ __device__ __forceinline__ void tile_delta(const uint8_t* kblk, const uint8_t* q
 // lanes 32-63 (each lane half then holds its group's three partial products
 // for the key of its column, summed and rounded exactly as above).
 __device__ __forceinline__ void tile_delta_pair(const uint8_t* kblk, const uint8_t* qop,
-                                                int kbase_t, int koff_t, float gK, int lane,
-                                                uint16_t* dst0, uint16_t* dst1) {
+                                                int kbase_t, int koff_t, float gK, float cinv,
+                                                int lane, float* dst0, float* dst1) {
   const uint8_t* at = kblk + kbase_t;
   const int r = lane & 31, g = r >> 2, part = r & 3;
   const bool data = r < 7 && part < 3;
@@ -481,7 +508,7 @@ __device__ __forceinline__ void tile_delta_pair(const uint8_t* kblk, const uint8
     }
     d = mfma32_bf16(a[kc & 1], b[kc & 1], d);
   }
-  (lane < 32 ? dst0 : dst1)[koff_t] = (uint16_t)bf16_rne(((d[0] + d[1]) + d[2]) * gK);
+  (lane < 32 ? dst0 : dst1)[koff_t] = tile_delta_input((d[0] + d[1]) + d[2], gK, cinv);
 }
 
 // Work unit: 256 query rows of one (batch, head) in two groups of 4 waves
@@ -492,26 +519,34 @@ __device__ __forceinline__ void tile_delta_pair(const uint8_t* kblk, const uint8
 // vector ALUs of every SIMD are busy at the same time.  Both groups read
 // the same K~ / V / Delta_S blocks from LDS (double-buffered, loaded two
 // steps ahead by all 8 waves).
-// MODE 0: direct; 1: smoothing by the sequence means with the rank-one
-// Delta_S step; 2: per-tile means: the column term Delta_tile[j] =
-// Qbar_tile . K~_c[j] is computed here, one block ahead, and enters through
-// the same rank-one step (BF16 K~ images and query operands, K~ blocks
-// triple-buffered so the next block is resident while the current one is
-// scored).
+// MODE 0: direct; 1: smoothing by the sequence means, Delta_S entering the
+// score accumulator; 2: per-tile means: the column term Delta_tile[j] =
+// Qbar_tile . K~_c[j] is computed here, one block ahead, and enters the
+// score accumulator the same way (BF16 K~ images and query operands, K~
+// blocks triple-buffered so the next block is resident while the current
+// one is scored).
 template <int MODE, int VAR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(
     PrefillParams p) {
   constexpr bool SMOOTH = MODE == 1, TILE = MODE == 2;
-  // a rank-one compensation step (the element-wise variant adds Delta_S in
-  // the softmax instead)
-  constexpr bool RANK1 = (SMOOTH && VAR != kVarElementwise) || TILE;
+  // The compensation term (Delta_S, or Delta_tile in the per-tile mode) times
+  // 1/(gQ gK) is the score accumulator's input (section 5.2's compensation
+  // inside the matrix product, without an MMA step of its own); kVarRankOne
+  // writes it by a rank-one bf16 MMA step, kVarElementwise adds it in the
+  // softmax.
+  constexpr bool RANK1 = SMOOTH && VAR == kVarRankOne;
+  constexpr bool CINIT = (SMOOTH && VAR != kVarElementwise && !RANK1) || TILE;
+  constexpr bool DELTA16 = SMOOTH && !CINIT;  // bf16 Delta_S in LDS
+  constexpr int COMP = CINIT ? 2 : (RANK1 ? 1 : 0);
   constexpr bool PV16 = VAR == kVarPvBf16 || VAR == kVarPvNvfp4;  // 16-bit V blocks
   constexpr int NKB = TILE ? 3 : 2;       // K~ block buffers
   __shared__ __align__(16) uint8_t smem_k[NKB][kBlk * kRowBytes];  // K~ blocks
   __shared__ __align__(16) uint8_t smem_v[2][PV16 ? kVBf16BlockBytes : kVBlockBytes];  // V blocks
-  // Delta_S (smoothing: [buffer][0][key]) or Delta_tile (per-tile mode:
-  // [buffer][row group][key])
-  __shared__ __align__(16) uint16_t smem_delta[2][TILE ? 2 : 1][kBlk];
+  // bf16 Delta_S of the rank-one and element-wise variants, [buffer][key]
+  __shared__ __align__(16) uint16_t smem_delta[2][DELTA16 ? kBlk : 1];
+  // the accumulator input term x 1/(gQ gK) in fp32: smoothing [buffer][0][key],
+  // per-tile mode [buffer][row group][key]
+  __shared__ __align__(16) float smem_comp[CINIT ? 2 : 1][TILE ? 2 : 1][CINIT ? kBlk : 4];
   // per-tile mode: the tile means' bf16 parts as score-operand rows,
   // [row group][kc][lane half][part][8 bf16]
   __shared__ __align__(16) uint8_t smem_qop[TILE ? 2 * 8 * 2 * 3 * 16 : 16];
@@ -664,7 +699,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     wait_direct_loads();
     __syncthreads();
     if (n_own > 0)
-      tile_delta(smem_k[0], qop_g, kbase[wave & 3], koff[wave & 3], gK, lane, smem_delta[0][grp]);
+      tile_delta(smem_k[0], qop_g, kbase[wave & 3], koff[wave & 3], gK, cinv, lane,
+                 smem_comp[0][grp]);
   }
 
   // Steps alternate between the groups: in body j, group 0 runs its matrix
@@ -684,7 +720,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #define MPFA_STEP_OPEN(J)                                                                    \
   do {                                                                                       \
     wait_direct_loads(); /* this wave's loads of the previous body have landed */            \
-    if (SMOOTH && tid < kBlk) smem_delta[(J) & 1][0][tid] = (uint16_t)dd;                    \
+    if (SMOOTH && CINIT && tid < kBlk)                                                       \
+      smem_comp[(J) & 1][0][tid] = __uint_as_float(dd << 16) * cinv;                         \
+    if (DELTA16 && tid < kBlk) smem_delta[(J) & 1][tid] = (uint16_t)dd;                      \
     __syncthreads();                                                                         \
   } while (0)
 #define MPFA_ISSUE(J)                                                                        \
@@ -707,8 +745,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   do {                                                                                       \
     if ((J) >= 1 && (J) <= n_own) pv_block<VAR>(o, smem_v[((J) - 1) & 1], pb, h, col);      \
     if ((J) < n_own) {                                                                       \
-      score_block<RANK1, TILE>(s, smem_k[(J) % NKB], smem_delta[(J) & 1][TILE ? grp : 0], koff, \
-                               kbase, qf, dB, h);                                            \
+      score_block<COMP, TILE>(s, smem_k[(J) % NKB],                                          \
+                              CINIT ? (const void*)smem_comp[(J) & 1][TILE ? grp : 0]        \
+                                    : (const void*)smem_delta[(J) & 1],                      \
+                              koff, kbase, qf, dB, h);                                       \
     } else {                                                                                 \
       /* defining s on this path too keeps the old scores from being live */                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) s[t] = f32x16{};                         \
@@ -716,8 +756,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     /* the groups take turns computing Delta_tile(J+1) for both tiles */                    \
     if (TILE && ((J) & 1) == grp && (J) + 1 < n_max)                                         \
       tile_delta_pair(smem_k[((J) + 1) % NKB], smem_qop, kbase[wave & 3], koff[wave & 3], gK,  \
-                      lane, smem_delta[((J) + 1) & 1][0],                                    \
-                      smem_delta[((J) + 1) & 1][TILE ? 1 : 0]);                              \
+                      cinv, lane, smem_comp[((J) + 1) & 1][0],                               \
+                      smem_comp[((J) + 1) & 1][TILE ? 1 : 0]);                               \
   } while (0)
 #define MPFA_SOFTMAX(J)                                                                      \
   do {                                                                                       \
@@ -725,7 +765,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int k0 = (J) * kBlk;                                                             \
       const bool mask = (p.causal && k0 + kBlk > grow0) || (k0 + kBlk > N);                 \
       softmax_block<VAR>(s, o, pb, m_run, l_run, lam, mask, k0, lim, h,                      \
-                         &smem_delta[(J) & 1][0][0], cinv);                                  \
+                         &smem_delta[(J) & 1][0], cinv);                                     \
     } else {                                                                                 \
       pb = PRegs<VAR>{}; /* as for s: keeps old P from being live */                         \
     }                                                                                        \
@@ -948,6 +988,7 @@ void launch_prefill(const PrefillParams& p, hipStream_t st) {
       case kVarPolyExp2: hipLaunchKernelGGL((k_prefill<1, kVarPolyExp2>), g, b, 0, st, p); break;
       case kVarPvBf16: hipLaunchKernelGGL((k_prefill<1, kVarPvBf16>), g, b, 0, st, p); break;
       case kVarPvNvfp4: hipLaunchKernelGGL((k_prefill<1, kVarPvNvfp4>), g, b, 0, st, p); break;
+      case kVarRankOne: hipLaunchKernelGGL((k_prefill<1, kVarRankOne>), g, b, 0, st, p); break;
       default: hipLaunchKernelGGL((k_prefill<1, kVarNone>), g, b, 0, st, p); break;
     }
   } else {

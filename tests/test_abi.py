@@ -201,6 +201,21 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, f, ws_bytes=16) == WS
 
 
+@pytest.mark.parametrize("name", ["mpfa_prefill_elementwise", "mpfa_prefill_rank_one"])
+def test_compensation_placements_reject_bad_arguments(lib, name):
+    """The placement variants need a Delta_S; otherwise validated as
+    mpfa_prefill (their argument list is its own)."""
+    f = _Fake()
+    INVALID, WS = -1, -3
+    a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, q_mean=f.p, k_mean=f.p, k_fp4=f.p,
+             k_sf=f.p, k_gscale=f.p, v_fp8=f.p, v_scale=f.p, delta_s=f.p, scale=0.088, causal=1,
+             out=f.p, out_dtype=1, lse=None, ws=f.p, ws_bytes=256, stream=None)
+    fn = getattr(lib, name)
+    assert fn(*dict(a, delta_s=None, q_mean=None, k_mean=None).values()) == INVALID
+    assert fn(*dict(a, Hq=3).values()) == INVALID
+    assert fn(*dict(a, ws_bytes=16).values()) == WS
+
+
 def _prefill_tile(lib, f, **kw):
     a = dict(q=f.p, q_dtype=1, B=1, Hq=4, Hkv=2, N=256, D=128, k_mean=f.p, k_fp4=f.p, k_sf=f.p,
              k_gscale=f.p, v_fp8=f.p, v_scale=f.p, scale=0.088, causal=1, out=f.p, out_dtype=1,

@@ -3,8 +3,8 @@ section 3.1, Fig. 3(a): NVFP4 + BF16 P.V; section 7.4 "Compensation
 placement": an element-wise add instead of the rank-one MMA; section 5.1: a
 polynomial for part of the exponentials) against the oracle:
 
-* element-wise compensation: the same scores as the smoothing oracle
-  (S = Q~ K~^T + Delta_S before the mask and the max);
+* element-wise compensation and the rank-one MMA step: the same scores as
+  the smoothing oracle (S = Q~ K~^T + Delta_S before the mask and the max);
 * polynomial exp2: the smoothing and direct oracles, with the oracle's
   rounding-ambiguity window widened to the polynomial's relative error
   (2^-13 > 7.5e-5), since a P value that close to an E4M3 midpoint may round
@@ -90,13 +90,13 @@ def _check(mpfa, oracle_mod, cfg, variant, smooth=True, causal=True, edit=None):
     return host(out)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
+@pytest.mark.parametrize("variant", ["rank_one", "elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 def test_variant_small_config(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("prefill_1k_2x1"), variant)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
+@pytest.mark.parametrize("variant", ["rank_one", "elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 @pytest.mark.parametrize("N", [1, 129, 300])
 def test_variant_gqa5_spikes_ragged(mpfa, oracle_mod, variant, N):
     from mixed_precision_flashattention_amd import synth
@@ -110,7 +110,7 @@ def test_variant_direct_mode(mpfa, oracle_mod, variant):
            smooth=False)
 
 
-@pytest.mark.parametrize("variant", ["elementwise", "pv_bf16", "pv_nvfp4"])
+@pytest.mark.parametrize("variant", ["rank_one", "elementwise", "pv_bf16", "pv_nvfp4"])
 def test_variant_non_causal(mpfa, oracle_mod, variant):
     from mixed_precision_flashattention_amd import synth
     _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=2, Hkv=1, N=260), variant,
@@ -146,24 +146,26 @@ def test_variant_degenerate_inputs(mpfa, oracle_mod, variant, edit):
         assert not np.any(out), "zero V must give a zero output"
 
 
-def test_elementwise_matches_the_rank_one_kernel(mpfa):
-    """The two placements compute the same scores; their outputs agree far
-    inside the oracle tolerance."""
+@pytest.mark.parametrize("variant", ["elementwise", "rank_one"])
+def test_placements_match_the_library_kernel(mpfa, variant):
+    """The three placements of the compensation (the score accumulator's
+    input, an element-wise add, a rank-one MMA step) compute the same scores;
+    their outputs agree far inside the oracle tolerance."""
     import torch
     from mixed_precision_flashattention_amd import synth
     cfg = synth.config("llama8b_prefill_16k", B=1, Hq=8, Hkv=2, N=1000)
     q, k, v = (dev(synth.full(cfg, t), torch.bfloat16) for t in ("q", "k", "v"))
-    say("case: element-wise against rank-one compensation, N1000")
+    say(f"case: {variant} against the library's compensation placement, N1000")
     kq, vq = mpfa.quantize_k(k, q=q), mpfa.quantize_v(v)
     a, _ = mpfa.prefill(q, kq, vq, cfg.scale, out_dtype=torch.float32)
-    b, _ = mpfa.prefill_variant("elementwise", q, kq, vq, cfg.scale, out_dtype=torch.float32)
+    b, _ = mpfa.prefill_variant(variant, q, kq, vq, cfg.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_close("elementwise vs rank-one", host(b).reshape(-1, 128), host(a).reshape(-1, 128),
+    assert_close(f"{variant} vs library", host(b).reshape(-1, 128), host(a).reshape(-1, 128),
                  atol=1e-3, rtol=5e-3)
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("variant", ["elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
+@pytest.mark.parametrize("variant", ["rank_one", "elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"])
 def test_variant_fullsize_qwen14b_32k(mpfa, oracle_mod, variant):
     """Each variant on the 32K benchmark inputs, in the launch configuration the
     benchmark times, on synth.sample_rows."""
