@@ -178,6 +178,27 @@ def valu_ceiling(peaks, achieved):
             "block_ns": peaks.get("softmax_block_ns")}
 
 
+def schedule_ceiling(peaks, achieved):
+    """The ceilings of the prefill's two-group schedule measured by
+    mpfa_peaks with its per-block MFMA and softmax instruction mix and random
+    operands: "free_operands" with the operands in registers (the floor set
+    by the instruction mix and the barriers) and "lds_feed" with the kernel's
+    operand traffic (K~, V and the accumulator inputs read from LDS, the next
+    blocks brought in by direct loads); TFLOP/s of algorithmic work, cycles
+    per body (one 128-key block for all 8 waves), the clock the probe ran
+    at, and the fraction of each the prefill reaches; None without a peaks
+    run."""
+    out = {}
+    for key, name in (("pingpong", "free_operands"), ("pingpong_lds", "lds_feed")):
+        d = (peaks or {}).get(key)
+        if not d:
+            return None
+        out[name] = {"tflops": d["tflops"], "frac_of_roofline": round(d["tflops"] * 1e12 / PEAK_MIXED, 4),
+                     "achieved_frac": round(achieved / d["tflops"], 4),
+                     "body_cycles": d.get("body_cycles"), "clock_GHz": d.get("clock_GHz")}
+    return out
+
+
 def measured_peaks():
     """The device's measured ceilings from the standalone probe built beside
     the library (mixed_precision_flashattention_amd/mpfa_peaks): MFMA rates of
@@ -629,6 +650,8 @@ def main():
         if peaks:
             log(f"[bench] measured ceilings: MFMA {peaks.get('mfma_tflops')} TFLOP/s, "
                 f"softmax VALU {peaks.get('softmax_valu_tflops')} TFLOP/s, "
+                f"ping-pong schedule {(peaks.get('pingpong') or {}).get('tflops')} / "
+                f"{(peaks.get('pingpong_lds') or {}).get('tflops')} TFLOP/s (free operands / LDS feed), "
                 f"read {peaks.get('read_GBps')} GB/s")
 
     import torch
@@ -791,7 +814,11 @@ def main():
                      # the secondary ceiling: one softmax wave per SIMD running
                      # the kernel's per-block softmax mix with free matrix work
                      # (measured by mpfa_peaks on this device)
-                     "valu_softmax_ceiling": valu_ceiling(peaks, achieved)},
+                     "valu_softmax_ceiling": valu_ceiling(peaks, achieved),
+                     # the ceilings of the kernel's schedule and instruction
+                     # mix with free operands and with its LDS operand
+                     # traffic (mpfa_peaks)
+                     "schedule_ceiling": schedule_ceiling(peaks, achieved)},
         "prefill_ms": round(ms_prefill, 4), "prefill_median_ms": round(ms_prefill_median, 4),
         "stage_one_ms": round(ms_stage1, 4),
         "compensation": {
