@@ -19,6 +19,30 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
 // rows rl, rl + 16, ... of its chunk (four 16-byte loads in flight), the
 // block reduces its 16 row lanes in LDS and then updates the 128 channel
 // totals with one atomic each.
+// The same with non-temporal loads, for the statistics passes that stream a
+// whole tensor once each (nothing they read is reused from the cache).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load8_stream(const void* p, int64_t i, int is_bf16, float* x) {
+  if (is_bf16) {
+    const u32x4_nt a = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_nt*>(reinterpret_cast<const uint16_t*>(p) + i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(a[j] << 16);
+      x[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4_nt* s = reinterpret_cast<const f32x4_nt*>(reinterpret_cast<const float*>(p) + i);
+    const f32x4_nt a = __builtin_nontemporal_load(s), b = __builtin_nontemporal_load(s + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+}
+
 __device__ __forceinline__ void load8(const void* p, int64_t i, int is_bf16, float* x) {
   if (is_bf16) {
     const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
@@ -37,6 +61,13 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, int is_bf16, flo
 }
 
 constexpr int kStatBlocks = 2048;  // target number of blocks per statistics pass
+// The two statistics passes read the same tensors one after the other.  When
+// they fit in the device's last-level cache (256 MiB on MI355X) the second
+// pass finds them there, and each thread keeps 8 rows of loads in flight
+// over blocks of whole 128-row steps; when they do not, nothing is reused,
+// and the loads are non-temporal with 4 rows in flight (each choice the
+// faster one in measurements at 16K and 32K tokens).
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
 
 // The sequence-mean passes take one or two [BH, N, 128] tensors of the same
 // N (K and Q) in one launch: blocks [0, nblk0) cover tensor 0 and the rest
@@ -81,6 +112,7 @@ __device__ __forceinline__ float range_absmax(const uint32_t* range, int64_t nch
 }
 
 // Per (b, h, d): max over tokens of x and of -x (the channel's range).
+template <bool STREAM, int ROWS>
 __global__ __launch_bounds__(256) void k_channel_absmax(StatJobs J) {
   __shared__ float red[2][16][kD];
   const StatBlock sb = stat_block(J);
@@ -95,13 +127,15 @@ __global__ __launch_bounds__(256) void k_channel_absmax(StatJobs J) {
   float hi[8], lo[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) hi[j] = lo[j] = -INFINITY;
-  for (int r = r_begin + rl; r < r_end; r += 64) {
-    float v[4][8];
+  for (int r = r_begin + rl; r < r_end; r += 16 * ROWS) {
+    float v[ROWS][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      load8(x, (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg, is_bf16, v[k]);
+    for (int k = 0; k < ROWS; ++k) {
+      const int64_t i = (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg;
+      if (STREAM) load8_stream(x, i, is_bf16, v[k]); else load8(x, i, is_bf16, v[k]);
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < ROWS; ++k)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {  // repeats are harmless
         hi[j] = fmaxf(hi[j], v[k][j]);
@@ -135,6 +169,7 @@ __device__ __forceinline__ long long fixed_point_term(float x, int shift) {
 // has magnitude below 2^30, so the FP32 ldexp is exact wherever the result
 // can round to a nonzero integer, the FP32 round-to-nearest-even gives the
 // same integer as in FP64, and it fits an int32.
+template <bool STREAM, int ROWS>
 __global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
   __shared__ long long red[16][kD];
   const StatBlock sb = stat_block(J);
@@ -156,13 +191,15 @@ __global__ __launch_bounds__(256) void k_channel_fixsum(StatJobs J) {
   const int r_begin = sb.r_begin;
   const int r_end = min(N, r_begin + rows_per_block);
   long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = r_begin + rl; r < r_end; r += 64) {
-    float v[4][8];
+  for (int r = r_begin + rl; r < r_end; r += 16 * ROWS) {
+    float v[ROWS][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      load8(x, (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg, is_bf16, v[k]);
+    for (int k = 0; k < ROWS; ++k) {
+      const int64_t i = (bh * N + min(r + 16 * k, r_end - 1)) * kD + 8 * cg;
+      if (STREAM) load8_stream(x, i, is_bf16, v[k]); else load8(x, i, is_bf16, v[k]);
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < ROWS; ++k) {
       if (r + 16 * k < r_end) {  // every row counted exactly once
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] += fixed_point_term(v[k][j], shift[j]);
@@ -534,6 +571,14 @@ __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, 
   __shared__ __align__(16) uint32_t rows[kD * 8];  // [slot of channel][token / 4]
   const float A = __uint_as_float(*amax);
   const float s = A > 0.0f ? A / kE4M3Max : 1.0f;
+  // every element is divided by s: one rounded reciprocal and two residual
+  // corrections (block_quotient) give the correctly rounded quotient
+  // wherever the E4M3 code depends on it.  That is for quotients of
+  // magnitude >= 2^-10, half the smallest subnormal; with the divisor scaled
+  // into [2^-64, 2^64], their residuals are multiples of at least 2^-120 and
+  // stay exact.  Smaller quotients give a zero code, with the sign of x,
+  // either way.
+  const BlockDivisor dv = block_divisor(s, false);
   const int tile = blockIdx.x;
   const int64_t bh = blockIdx.y;
   if (tile == 0 && bh == 0 && threadIdx.x == 0) *vscale_out = s;
@@ -555,7 +600,7 @@ __global__ __launch_bounds__(128) void k_quantize_v(const void* __restrict__ v, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tile * 32 + 4 * tr + i;
-      const uint32_t c = t < N ? e4m3_encode(x[i][j] / s) : 0u;
+      const uint32_t c = t < N ? e4m3_encode(block_quotient(dv, x[i][j])) : 0u;
       word |= c << (8 * i);
     }
     rows[v_tile_slot(8 * cg + j) * 8 + tr] = word;
@@ -731,13 +776,16 @@ static inline int stat_rows_per_block(int BH, int N, int align) {
 void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStream_t st) {
   StatJobs J{};
   J.N = N;
-  int64_t nblk = 0;
+  int64_t nblk = 0, bytes = 0;
+  for (int t = 0; t < n_jobs; ++t)
+    bytes += (int64_t)jobs[t].BH * N * kD * (jobs[t].is_bf16 ? 2 : 4);
+  const bool stream = bytes > kLastLevelCacheBytes;
   for (int t = 0; t < 2; ++t) {
     const ChannelMeanJob& c = jobs[t < n_jobs ? t : 0];
     J.x[t] = c.x;
     J.is_bf16[t] = c.is_bf16;
     J.BH[t] = c.BH;
-    J.rows[t] = stat_rows_per_block(c.BH, N, 64);
+    J.rows[t] = stat_rows_per_block(c.BH, N, stream ? 64 : 128);
     J.gx[t] = (N + J.rows[t] - 1) / J.rows[t];
     J.range[t] = c.range;
     J.sums[t] = c.sums;
@@ -746,8 +794,13 @@ void launch_channel_means(const ChannelMeanJob* jobs, int n_jobs, int N, hipStre
     if (t < n_jobs) nblk += (int64_t)J.gx[t] * c.BH;
   }
   J.nblk0 = J.gx[0] * J.BH[0];
-  hipLaunchKernelGGL(k_channel_absmax, dim3((unsigned)nblk), dim3(256), 0, st, J);
-  hipLaunchKernelGGL(k_channel_fixsum, dim3((unsigned)nblk), dim3(256), 0, st, J);
+  if (stream) {
+    hipLaunchKernelGGL((k_channel_absmax<true, 4>), dim3((unsigned)nblk), dim3(256), 0, st, J);
+    hipLaunchKernelGGL((k_channel_fixsum<true, 4>), dim3((unsigned)nblk), dim3(256), 0, st, J);
+  } else {
+    hipLaunchKernelGGL((k_channel_absmax<false, 8>), dim3((unsigned)nblk), dim3(256), 0, st, J);
+    hipLaunchKernelGGL((k_channel_fixsum<false, 8>), dim3((unsigned)nblk), dim3(256), 0, st, J);
+  }
   const int n0 = J.BH[0] * kD;
   const int n = n0 + (n_jobs > 1 ? J.BH[1] * kD : 0);
   hipLaunchKernelGGL(k_mean_finalize, dim3((n + 255) / 256), dim3(256), 0, st, J, n0, n);
