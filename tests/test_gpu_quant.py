@@ -48,6 +48,16 @@ def test_quantize_k_smooth_small_fp32(mpfa, oracle_mod):
     _compare_k(mpfa, oracle_mod, synth.full(cfg, "k"), q=synth.full(cfg, "q"))
 
 
+def test_quantize_k_smooth_fp32_past_the_last_level_cache(mpfa, oracle_mod):
+    """fp32 Q and K of 335 MB together, more than the 256 MiB last-level cache:
+    the statistics passes take their streaming form (non-temporal loads,
+    four rows in flight) on the fp32 path; every byte as the oracle's."""
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("prefill_1k_2x1", B=1, Hq=16, Hkv=4, N=32768)
+    say(f"case: quantize_k smooth fp32 {cfg.B}x{cfg.Hq}/{cfg.Hkv}x{cfg.N} (Q + K 335 MB)")
+    _compare_k(mpfa, oracle_mod, synth.full(cfg, "k"), q=synth.full(cfg, "q"))
+
+
 @pytest.mark.parametrize("N", [1, 77, 1000])
 def test_quantize_k_smooth_bf16_gqa_ragged(mpfa, oracle_mod, N):
     import torch
