@@ -192,7 +192,18 @@ def _zero_q(q, k, v):
     return np.zeros_like(q), k, v
 
 
-@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q], ids=lambda f: f.__name__)
+def _offset_query(q, k, v):
+    """Queries offset by up to +-6 per channel (bf16-exact): the sequence mean
+    carries most of Q, so the compensation term Qbar . K_c dominates the
+    scores."""
+    x = (q + np.linspace(-6.0, 6.0, q.shape[-1], dtype=np.float32)).astype(np.float32)
+    u = x.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32), k, v
+
+
+@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q, _offset_query],
+                         ids=lambda f: f.__name__)
 @pytest.mark.parametrize("smooth", [True, False])
 def test_prefill_degenerate_inputs(mpfa, oracle_mod, edit, smooth):
     from mixed_precision_flashattention_amd import synth

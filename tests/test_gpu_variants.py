@@ -133,12 +133,25 @@ def _zero_q(q, k, v):
     return np.zeros_like(q), k, v
 
 
-@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q], ids=lambda f: f.__name__)
-@pytest.mark.parametrize("variant", ["pv_bf16", "pv_nvfp4"])
+def _offset_query(q, k, v):
+    """Queries offset by up to +-6 per channel (bf16-exact): the sequence mean
+    carries most of Q, so the compensation term Qbar . K_c dominates the
+    scores."""
+    x = (q + np.linspace(-6.0, 6.0, q.shape[-1], dtype=np.float32)).astype(np.float32)
+    u = x.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32), k, v
+
+
+@pytest.mark.parametrize("edit", [_zero_k, _same_key, _zero_v, _zero_q, _offset_query],
+                         ids=lambda f: f.__name__)
+@pytest.mark.parametrize("variant", ["rank_one", "elementwise", "pv_bf16", "pv_nvfp4"])
 def test_variant_degenerate_inputs(mpfa, oracle_mod, variant, edit):
     """Zero keys or queries (every score equal: P of a whole group at its
     maximum), keys identical along the sequence (centred K zero), zero V
-    (a zero V cache, a zero output) through the other P.V precisions."""
+    (a zero V cache, a zero output), and queries carried mostly by their
+    sequence mean (the compensation term dominates the scores), through the
+    other compensation placements and P.V precisions."""
     from mixed_precision_flashattention_amd import synth
     out = _check(mpfa, oracle_mod, synth.config("llama8b_prefill_16k", B=1, Hq=4, Hkv=2, N=200),
                  variant, edit=edit)
