@@ -254,3 +254,42 @@ def test_prefill_takes_the_first_stage_query_amax(mpfa, oracle_mod):
     q.mul_(2.0)
     with pytest.raises(ValueError):
         mpfa.prefill(q, kq, vq, scale, causal=True)
+
+
+# ---- seeded random shapes: combinations the cases above do not pin down ----
+def _sweep_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 3, 5, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        cases.append(dict(B=int(rng.integers(1, 4)), Hkv=hkv, Hq=hkv * g,
+                          N=int(rng.integers(1, 700)), bf16=bool(rng.integers(0, 2)),
+                          causal=bool(rng.integers(0, 2)), smooth=bool(rng.integers(0, 2)),
+                          out_bf16=bool(rng.integers(0, 2)), splits=int(rng.choice([1, 2, 3, 7, 16]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(20261203, 12), ids=lambda c: (
+    f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
+    f"{'causal' if c['causal'] else 'full'}-{'smooth' if c['smooth'] else 'direct'}"))
+def test_prefill_random_shapes(mpfa, oracle_mod, case):
+    """Batch, KV heads (odd counts take the plain heaviest-first order), GQA
+    factor, length (ragged), input dtype, causality, smoothing and output
+    dtype drawn from a fixed seed; every row against the oracle."""
+    from mixed_precision_flashattention_amd import synth
+    base = "llama8b_prefill_16k" if case["bf16"] else "prefill_1k_2x1"
+    cfg = synth.config(base, B=case["B"], Hq=case["Hq"], Hkv=case["Hkv"], N=case["N"])
+    _check_prefill(mpfa, oracle_mod, cfg, causal=case["causal"], smooth=case["smooth"],
+                   out_bf16=case["out_bf16"])
+
+
+@pytest.mark.parametrize("case", _sweep_cases(20261204, 8), ids=lambda c: (
+    f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-splits{c['splits']}-"
+    f"{'smooth' if c['smooth'] else 'direct'}"))
+def test_decode_random_shapes(mpfa, oracle_mod, case):
+    """The same draw for decode: batch, heads, cached length, partitions."""
+    from mixed_precision_flashattention_amd import synth
+    cfg = synth.config("llama8b_decode_128k", B=case["B"], Hq=case["Hq"], Hkv=case["Hkv"],
+                       N=case["N"], num_splits=case["splits"])
+    _check_decode(mpfa, oracle_mod, cfg, smooth=case["smooth"])
