@@ -228,3 +228,41 @@ def test_paged_decode_empty_and_over_long_requests(mpfa, oracle_mod):
     O, L = _oracle_paged(mpfa, oracle_mod, pool, table, q, lens, splits, 0.1)
     assert_close("out", o[1:].reshape(-1, 128), O[1:].reshape(-1, 128))
     assert_close("lse", l[1:].ravel(), L[1:].ravel(), atol=LSE_ATOL, rtol=0.0)
+
+
+# ---- seeded random pools: request count, heads, GQA factor, ragged and empty
+# lengths, partitions and spare table slots drawn from a fixed seed ----
+def _paged_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 7))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        lens = [int(x) for x in rng.integers(0, 1500, B)]
+        if rng.integers(0, 3) == 0:
+            lens[int(rng.integers(0, B))] = 0
+        cases.append(dict(B=B, Hkv=hkv, Hq=hkv * g, lens=lens, splits=int(rng.choice([1, 2, 3, 8, 32])),
+                          smooth=bool(rng.integers(0, 2)), extra=int(rng.integers(0, 3)), seed=500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _paged_cases(20261205, 8), ids=lambda c: (
+    f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-splits{c['splits']}-{'smooth' if c['smooth'] else 'direct'}"))
+def test_paged_decode_random_pools(mpfa, oracle_mod, case):
+    import torch
+    B, Hq, Hkv, lens, splits = case["B"], case["Hq"], case["Hkv"], case["lens"], case["splits"]
+    max_pages = max(-(-max(lens) // PAGE), 1) + case["extra"]
+    say(f"case: paged decode B{B} Hq{Hq}/Hkv{Hkv} lengths {lens} splits {splits} "
+        f"smooth={case['smooth']} table width {max_pages}")
+    pool, table, q = _ragged_setup(mpfa, case["smooth"], lens, B, Hq, Hkv, max_pages, seed=case["seed"])
+    out, lse = mpfa.decode_paged(dev(q, torch.bfloat16), pool, dev(table), dev(np.array(lens, np.int32)),
+                                 0.0883883, splits, out_dtype=torch.float32, with_lse=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_paged(mpfa, oracle_mod, pool, table, q, lens, splits, 0.0883883)
+    assert_close("out", host(out).reshape(-1, 128), O.reshape(-1, 128))
+    got, ref = host(lse).ravel(), L.ravel()
+    finite = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), finite), "empty requests give LSE = -inf, the others a finite one"
+    if finite.any():
+        assert_close("lse", got[finite], ref[finite], atol=LSE_ATOL, rtol=0.0)

@@ -124,3 +124,27 @@ def test_tile_mean_with_a_smoothing_cache_is_identical(mpfa, oracle_mod):
                                        out_dtype=torch.float32, with_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- seeded random shapes: batch, KV heads, GQA factor, ragged length, input
+# dtype, causality and output dtype drawn from a fixed seed ----
+def _tile_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 3, 5, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        cases.append(dict(B=int(rng.integers(1, 4)), Hkv=hkv, Hq=hkv * g, N=int(rng.integers(1, 700)),
+                          bf16=bool(rng.integers(0, 2)), causal=bool(rng.integers(0, 2)),
+                          out_bf16=bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _tile_cases(20261206, 6), ids=lambda c: (
+    f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
+    f"{'causal' if c['causal'] else 'full'}"))
+def test_tile_mean_random_shapes(mpfa, oracle_mod, case):
+    from mixed_precision_flashattention_amd import synth
+    base = "llama8b_prefill_16k" if case["bf16"] else "prefill_1k_2x1"
+    cfg = synth.config(base, B=case["B"], Hq=case["Hq"], Hkv=case["Hkv"], N=case["N"])
+    _check_tile(mpfa, oracle_mod, cfg, causal=case["causal"], out_bf16=case["out_bf16"])

@@ -209,3 +209,30 @@ def test_variant_fullsize_qwen14b_32k(mpfa, oracle_mod, variant):
     say(f"  oracle done ({time.time() - t0:.1f} s)")
     assert_close("out f32", got, O, slack=AMB)
     assert_close("lse", got_lse, LSE, atol=LSE_ATOL, rtol=0.0)
+
+
+# ---- seeded random shapes: variant, batch, KV heads, GQA factor, ragged
+# length, input dtype, causality and (for the P.V and exp2 variants)
+# smoothing drawn from a fixed seed ----
+def _variant_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 3, 5, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        variant = str(rng.choice(["rank_one", "elementwise", "poly_exp2", "pv_bf16", "pv_nvfp4"]))
+        smooth = variant in ("rank_one", "elementwise") or bool(rng.integers(0, 2))
+        cases.append(dict(variant=variant, B=int(rng.integers(1, 4)), Hkv=hkv, Hq=hkv * g,
+                          N=int(rng.integers(1, 700)), bf16=bool(rng.integers(0, 2)),
+                          causal=bool(rng.integers(0, 2)), smooth=smooth))
+    return cases
+
+
+@pytest.mark.parametrize("case", _variant_cases(20261207, 8), ids=lambda c: (
+    f"{c['variant']}-B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
+    f"{'causal' if c['causal'] else 'full'}-{'smooth' if c['smooth'] else 'direct'}"))
+def test_variant_random_shapes(mpfa, oracle_mod, case):
+    from mixed_precision_flashattention_amd import synth
+    base = "llama8b_prefill_16k" if case["bf16"] else "prefill_1k_2x1"
+    cfg = synth.config(base, B=case["B"], Hq=case["Hq"], Hkv=case["Hkv"], N=case["N"])
+    _check(mpfa, oracle_mod, cfg, case["variant"], smooth=case["smooth"], causal=case["causal"])
