@@ -625,8 +625,8 @@ B200_CONTEXT = {
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen14b_prefill_32k")
     ap.add_argument("--decode-workload", default="llama8b_decode_128k")
     ap.add_argument("--no-decode", action="store_true")
