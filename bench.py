@@ -105,12 +105,36 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, iters, warmup):
-    """Average ms per call over `iters` calls, HIP events on the current stream."""
+WARM_MS = 60.0  # back-to-back work before any timed region
+
+
+def warm_up(fn, calls, min_ms=WARM_MS, max_calls=200):
+    """`calls` untimed calls, then, issued back to back, as many more as fill
+    `min_ms` at the rate the first ones ran: after an idle or memory-bound
+    stretch the shader clock takes some tens of milliseconds of matrix work
+    to settle, and a region timed before that reads slow."""
     import torch
-    for _ in range(warmup):
+    calls = max(calls, 1)
+    t0 = time.perf_counter()
+    for _ in range(calls):
         fn()
     torch.cuda.synchronize()
+    spent = (time.perf_counter() - t0) * 1e3
+    if spent < min_ms:
+        per_call = max(spent / calls, 1e-3)
+        extra = min(max_calls, int(np.ceil((min_ms - spent) / per_call)))
+        for _ in range(extra):
+            fn()
+        torch.cuda.synchronize()
+        calls += extra
+    return calls
+
+
+def time_calls(fn, iters, warmup):
+    """Average ms per call over `iters` calls, HIP events on the current
+    stream, after `warm_up`."""
+    import torch
+    time_calls.warm_calls = warm_up(fn, warmup)
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -124,9 +148,9 @@ def time_calls(fn, iters, warmup):
 
 def median_call_ms(fn, n=20):
     """Median of n single calls, each bracketed by its own HIP events on the
-    current stream (after one untimed call)."""
+    current stream (after `warm_up`)."""
     import torch
-    fn()
+    warm_up(fn, 1)
     st = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
@@ -735,11 +759,13 @@ def main():
     # ---- the dominant kernel, alone --------------------------------------
     stage1()
     ms_prefill = time_calls(prefill_call, args.steps, 2)
+    warm_prefill = time_calls.warm_calls
     ms_prefill_median = median_call_ms(prefill_call)
     ms_stage1 = time_calls(stage1, args.steps, 1)
     achieved = flops / (ms_prefill * 1e-3) / 1e12
     log(f"[bench] prefill call {ms_prefill:.3f} ms -> {achieved:.1f} TFLOP/s "
-        f"({achieved * 1e12 / PEAK_MIXED:.4f} of the FP4/FP8 roofline); stage one {ms_stage1:.3f} ms")
+        f"({achieved * 1e12 / PEAK_MIXED:.4f} of the FP4/FP8 roofline; {args.steps} calls after "
+        f"{warm_prefill} untimed); stage one {ms_stage1:.3f} ms")
 
     # ---- compensation overhead: one centred K cache, the same call with and
     # without the compensation term.  Without Delta_S the centred cache gives
