@@ -1,9 +1,18 @@
 """Helpers shared by the GPU parity tests (marshalling and comparison only)."""
+import os
+
 import numpy as np
 
 ATOL = 2e-3  # attention output tolerance (max-abs) against the oracle
 RTOL = 1e-2  # and relative part: |gpu - oracle| <= ATOL + RTOL * |oracle|
 LSE_ATOL = 2e-3
+
+
+def sweep_count(n):
+    """Case count of a seeded random-shape test: n, times the integer in the
+    environment variable MPFA_SWEEP_SCALE when it is set (the first n cases
+    stay the same, more are drawn after them)."""
+    return n * max(1, int(os.environ.get("MPFA_SWEEP_SCALE", "1")))
 
 
 def say(msg):

@@ -4,7 +4,7 @@ within 2e-3.  Sizes span several tiles and ragged tails."""
 import numpy as np
 import pytest
 
-from gpu_util import LSE_ATOL, assert_close, dev, host, say
+from gpu_util import LSE_ATOL, assert_close, dev, host, say, sweep_count
 
 pytestmark = pytest.mark.gpu
 
@@ -270,7 +270,7 @@ def _sweep_cases(seed, n):
     return cases
 
 
-@pytest.mark.parametrize("case", _sweep_cases(20261203, 12), ids=lambda c: (
+@pytest.mark.parametrize("case", _sweep_cases(20261203, sweep_count(12)), ids=lambda c: (
     f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
     f"{'causal' if c['causal'] else 'full'}-{'smooth' if c['smooth'] else 'direct'}"))
 def test_prefill_random_shapes(mpfa, oracle_mod, case):
@@ -284,7 +284,7 @@ def test_prefill_random_shapes(mpfa, oracle_mod, case):
                    out_bf16=case["out_bf16"])
 
 
-@pytest.mark.parametrize("case", _sweep_cases(20261204, 8), ids=lambda c: (
+@pytest.mark.parametrize("case", _sweep_cases(20261204, sweep_count(8)), ids=lambda c: (
     f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-splits{c['splits']}-"
     f"{'smooth' if c['smooth'] else 'direct'}"))
 def test_decode_random_shapes(mpfa, oracle_mod, case):

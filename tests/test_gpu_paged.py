@@ -6,7 +6,7 @@ kernels must never let into a result."""
 import numpy as np
 import pytest
 
-from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say
+from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say, sweep_count
 
 pytestmark = pytest.mark.gpu
 PAGE = 128
@@ -247,7 +247,7 @@ def _paged_cases(seed, n):
     return cases
 
 
-@pytest.mark.parametrize("case", _paged_cases(20261205, 8), ids=lambda c: (
+@pytest.mark.parametrize("case", _paged_cases(20261205, sweep_count(8)), ids=lambda c: (
     f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-splits{c['splits']}-{'smooth' if c['smooth'] else 'direct'}"))
 def test_paged_decode_random_pools(mpfa, oracle_mod, case):
     import torch

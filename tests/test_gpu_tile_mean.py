@@ -6,7 +6,7 @@ groups and degenerate queries."""
 import numpy as np
 import pytest
 
-from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say
+from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say, sweep_count
 
 pytestmark = pytest.mark.gpu
 
@@ -140,7 +140,7 @@ def _tile_cases(seed, n):
     return cases
 
 
-@pytest.mark.parametrize("case", _tile_cases(20261206, 6), ids=lambda c: (
+@pytest.mark.parametrize("case", _tile_cases(20261206, sweep_count(6)), ids=lambda c: (
     f"B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
     f"{'causal' if c['causal'] else 'full'}"))
 def test_tile_mean_random_shapes(mpfa, oracle_mod, case):

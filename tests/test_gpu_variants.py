@@ -23,7 +23,7 @@ import time
 import numpy as np
 import pytest
 
-from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say
+from gpu_util import LSE_ATOL, assert_bytes_equal, assert_close, dev, host, say, sweep_count
 
 pytestmark = pytest.mark.gpu
 
@@ -228,7 +228,7 @@ def _variant_cases(seed, n):
     return cases
 
 
-@pytest.mark.parametrize("case", _variant_cases(20261207, 8), ids=lambda c: (
+@pytest.mark.parametrize("case", _variant_cases(20261207, sweep_count(8)), ids=lambda c: (
     f"{c['variant']}-B{c['B']}-H{c['Hq']}x{c['Hkv']}-N{c['N']}-{'bf16' if c['bf16'] else 'f32'}-"
     f"{'causal' if c['causal'] else 'full'}-{'smooth' if c['smooth'] else 'direct'}"))
 def test_variant_random_shapes(mpfa, oracle_mod, case):
